@@ -1,0 +1,19 @@
+"""fp64 CPU oracle for the attention forward pass (test infrastructure only).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It shares no code with the HIP library.
+"""
+
+from .attention import (  # noqa: F401
+    LN2,
+    LOG2E,
+    attention_blocked,
+    attention_naive,
+    attention_online_tiled,
+    attention_probs_naive,
+    attention_rows,
+    classify_tiles,
+    kv_head_of,
+    key_visibility,
+    tile_plan,
+)

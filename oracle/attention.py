@@ -1,0 +1,386 @@
+"""Plain fp64 CPU oracle for the FlashAttention-style attention forward pass.
+
+TEST INFRASTRUCTURE ONLY.  This module exists to check the HIP path.  Only the
+test suite, the smoke check in ``__graft_entry__`` and the CPU-baseline leg of
+``bench.py`` may import it; nothing on the product path calls it, and it shares
+no code, tables or helpers with the HIP library.
+
+Sources, cited by page title and section:
+
+* [cuTile]  "Tuning Flash Attention for peak performance in NVIDIA CUDA Tile"
+            (NVIDIA technical blog post on cuTile, Japanese-titled mirror).
+* [Journey] "How I Beat PyTorch's Flash Attention: A CUDA Optimization Journey".
+* [Tiled]   "TiledAttention: a CUDA Tile SDPA Kernel for PyTorch" (abstract and
+            Figure 1).
+
+What is computed (every input is converted exactly to float64 first):
+
+    kvh    = hq // (Hq // Hkv)                                  [cuTile] "Grouped-query attention"
+    V(i)   = { j < Skv : not causal  or  j <= input_pos + i }   [cuTile] "Causal attention",
+                                                                 Part 1 "Applying the causal mask"
+    s_j    = scale * <q[b,hq,i,:], k[b,kvh,j,:]>     for j in V(i)
+    O      = sum_j exp(s_j - m) v[b,kvh,j,:] / sum_j exp(s_j - m),  m = max_j s_j
+    LSE    = m + ln(sum_j exp(s_j - m))
+
+The attention formula itself was lost when the [cuTile] page was extracted
+("What is attention?"); the textbook reading softmax(scale * Q K^T + M) V is
+the one its kernel code (Part 1, "Online softmax update" and "Final
+normalization and store") implements, with the default scale 1/sqrt(D) from
+its host code ("Launching the kernel: Host-side code").  The log-sum-exp output
+is on no page; it is read as the natural-log log-sum-exp of the scaled, masked
+scores of each row.
+
+Three forms are provided, written independently of one another:
+
+* ``attention_naive``          pure-Python loops over the definition (tiny shapes);
+* ``attention_blocked``        the definition with NumPy matmuls, row block by row
+                               block (the oracle used for parity and the CPU baseline);
+* ``attention_online_tiled``   the tile-by-tile online-softmax algorithm of the
+                               [cuTile] kernel, with its loop bound, K-loop split,
+                               exp2 domain and rescaling, in float64.
+
+Parity status: every function here is pinned by the CPU test suite against
+brute force, an independent library routine (PyTorch's CPU float64
+scaled_dot_product_attention), closed forms and invariants.  Nothing is
+"parity unpinned".
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+LN2 = math.log(2.0)
+LOG2E = 1.0 / LN2  # the [cuTile] kernel's INV_LOG_2, Part 1 "Defining the kernel interface"
+
+
+# ----------------------------------------------------------------------------
+# Shape checks shared by the NumPy forms (argument checking only, no arithmetic)
+# ----------------------------------------------------------------------------
+
+def _shapes(q, k, v):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be [B, H, S, D]")
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Skv, Dk = k.shape
+    if k.shape != v.shape or Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    if Hkv < 1 or Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if Skv < 1:
+        raise ValueError("Skv must be >= 1")
+    return B, Hq, Hkv, Sq, Skv, D
+
+
+# ----------------------------------------------------------------------------
+# Form (i): pure-Python loops over the definition
+# ----------------------------------------------------------------------------
+
+def attention_naive(q, k, v, scale, causal=False, input_pos=0):
+    """Brute-force definition with pure-Python loops; float64; tiny shapes only.
+
+    Follows [cuTile] "What is attention?" (textbook softmax(scale Q K^T + M) V),
+    "Causal attention" (key n visible to query m iff offs_m >= offs_n, where the
+    query position offs_m carries input_pos, Part 1 "Initializing
+    accumulators") and "Grouped-query attention" (query heads in contiguous
+    groups of Hq/Hkv share one K/V head).
+
+    Returns (O [B,Hq,Sq,D], LSE [B,Hq,Sq]) as float64 arrays.
+    """
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    group = Hq // Hkv
+    ql, kl, vl = np.asarray(q, np.float64).tolist(), np.asarray(k, np.float64).tolist(), \
+        np.asarray(v, np.float64).tolist()
+    O = np.zeros((B, Hq, Sq, D))
+    L = np.zeros((B, Hq, Sq))
+    for b in range(B):
+        for hq in range(Hq):
+            g = hq // group
+            for i in range(Sq):
+                last = Skv - 1
+                if causal:
+                    last = min(last, input_pos + i)
+                qi = ql[b][hq][i]
+                s = []
+                for j in range(last + 1):
+                    kj = kl[b][g][j]
+                    acc = 0.0
+                    for d in range(D):
+                        acc += qi[d] * kj[d]
+                    s.append(scale * acc)
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                den = sum(e)
+                for d in range(D):
+                    num = 0.0
+                    for j in range(last + 1):
+                        num += e[j] * vl[b][g][j][d]
+                    O[b, hq, i, d] = num / den
+                L[b, hq, i] = m + math.log(den)
+    return O, L
+
+
+def attention_probs_naive(q, k, scale, causal=False, input_pos=0):
+    """The attention-weight matrix P = softmax(scale Q K^T + M), pure Python, float64.
+
+    [cuTile] "What is attention?" and "Causal attention": masked entries are
+    exactly zero.  Returns P [B, Hq, Sq, Skv].
+    """
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    group = Hq // Hkv
+    ql, kl = np.asarray(q, np.float64).tolist(), np.asarray(k, np.float64).tolist()
+    P = np.zeros((B, Hq, Sq, Skv))
+    for b in range(B):
+        for hq in range(Hq):
+            g = hq // group
+            for i in range(Sq):
+                last = Skv - 1 if not causal else min(Skv - 1, input_pos + i)
+                s = [scale * sum(ql[b][hq][i][d] * kl[b][g][j][d] for d in range(D))
+                     for j in range(last + 1)]
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                den = sum(e)
+                for j in range(last + 1):
+                    P[b, hq, i, j] = e[j] / den
+    return P
+
+
+# ----------------------------------------------------------------------------
+# Form (ii): the definition, NumPy matmuls, one block of query rows at a time
+# ----------------------------------------------------------------------------
+
+def kv_head_of(hq, Hq, Hkv):
+    """Index of the K/V head that query head ``hq`` reads.
+
+    [cuTile] "Grouped-query attention" and Part 1 "Block ID mapping":
+    kv_head = head // query_group_size with query_group_size = Hq // Hkv, so
+    query heads 0..G-1 share K/V head 0, G..2G-1 share head 1, and so on.
+    """
+    return hq // (Hq // Hkv)
+
+
+def key_visibility(rows, Skv, causal, input_pos):
+    """Boolean [len(rows), Skv]: may query row i attend to key j?
+
+    [cuTile] "Causal attention" and Part 1 "Applying the causal mask": with
+    causal masking key j is visible iff j <= input_pos + i (the query position
+    carries input_pos, Part 1 "Initializing accumulators"); without it every
+    key 0..Skv-1 is visible and input_pos plays no part.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.arange(Skv, dtype=np.int64)
+    if not causal:
+        return np.ones((rows.size, Skv), dtype=bool)
+    return cols[None, :] <= (rows[:, None] + input_pos)
+
+
+def scaled_scores(q_rows, k_head, scale):
+    """scale * Q K^T for a block of query rows against one K head (float64).
+
+    [cuTile] "What is attention?"; the scale multiplies the raw dot products
+    (Part 1 "Online softmax update", default 1/sqrt(D) from the host code).
+    """
+    return scale * (q_rows @ k_head.T)
+
+
+def masked_softmax_stats(s, visible):
+    """Row maximum m, un-normalised weights e = exp(s - m) and row sum l.
+
+    Masked entries contribute nothing ([cuTile] "Causal attention": adding -inf
+    makes them zero after the softmax).  This is the numerically safe softmax
+    of "Understanding online softmax", computed over the whole row at once.
+    """
+    s = np.where(visible, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    return m, e, l
+
+
+def normalise(e, l, v_head):
+    """O = (e V) / l: [cuTile] Part 1 "Final normalization and store"."""
+    return (e @ v_head) / l
+
+
+def log_sum_exp(m, l):
+    """Natural-log log-sum-exp of the scaled, masked scores: m + ln(l)."""
+    return m[:, 0] + np.log(l[:, 0])
+
+
+def attention_blocked(q, k, v, scale, causal=False, input_pos=0, rows_per_block=512):
+    """The definition in float64 with NumPy matmuls, ``rows_per_block`` query rows at a time.
+
+    Row blocking only bounds memory: every row is computed from its full set of
+    visible scores in one pass, exactly as defined (module docstring).
+    Returns (O [B,Hq,Sq,D], LSE [B,Hq,Sq]) as float64 arrays.
+    """
+    B, Hq, Hkv, Sq, Skv, D = _shapes(q, k, v)
+    if not (math.isfinite(scale) and scale > 0):
+        raise ValueError("scale must be finite and > 0")
+    O = np.empty((B, Hq, Sq, D))
+    L = np.empty((B, Hq, Sq))
+    for b in range(B):
+        for hq in range(Hq):
+            g = kv_head_of(hq, Hq, Hkv)
+            kh = np.asarray(k[b, g], np.float64)
+            vh = np.asarray(v[b, g], np.float64)
+            for i0 in range(0, Sq, rows_per_block):
+                i1 = min(Sq, i0 + rows_per_block)
+                rows = np.arange(i0, i1)
+                s = scaled_scores(np.asarray(q[b, hq, i0:i1], np.float64), kh, scale)
+                m, e, l = masked_softmax_stats(s, key_visibility(rows, Skv, causal, input_pos))
+                O[b, hq, i0:i1] = normalise(e, l, vh)
+                L[b, hq, i0:i1] = log_sum_exp(m, l)
+    return O, L
+
+
+def attention_rows(q, k, v, scale, causal, input_pos, samples):
+    """The blocked definition evaluated only at sampled rows.
+
+    ``samples`` is an iterable of (b, hq, i).  Used to check full-size runs
+    whose complete oracle would take too long.  Returns (O [n,D], LSE [n]).
+    """
+    B, Hq, Hkv, Sq, Skv, D = _shapes(q, k, v)
+    samples = list(samples)
+    O = np.empty((len(samples), D))
+    L = np.empty(len(samples))
+    for n, (b, hq, i) in enumerate(samples):
+        g = kv_head_of(hq, Hq, Hkv)
+        vis = key_visibility([i], Skv, causal, input_pos)
+        last = int(np.nonzero(vis[0])[0].max()) + 1  # only rows up to the last visible key are read
+        kh = np.asarray(k[b, g, :last], np.float64)
+        vh = np.asarray(v[b, g, :last], np.float64)
+        s = scaled_scores(np.asarray(q[b, hq, i:i + 1], np.float64), kh, scale)
+        m, e, l = masked_softmax_stats(s, vis[:, :last])
+        O[n] = normalise(e, l, vh)[0]
+        L[n] = log_sum_exp(m, l)[0]
+    return O, L
+
+
+# ----------------------------------------------------------------------------
+# Form (iii): the tile-by-tile online-softmax algorithm of the cuTile kernel
+# ----------------------------------------------------------------------------
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def tile_plan(q_tile, tile_m, tile_n, Skv, causal, input_pos):
+    """Loop bound and mask start for one query tile, as the [cuTile] kernel sets them.
+
+    Part 1 "The main loop over K/V tiles": with causal masking the loop stops
+    at cdiv(min(input_pos + (q_tile + 1) * TILE_M, Skv), TILE_N); tiles past it
+    are fully masked and never visited.  Otherwise it covers cdiv(Skv, TILE_N).
+    Part 2 "K-loop split": tiles before mask_start =
+    min((input_pos + q_tile * TILE_M) // TILE_N, Skv // TILE_N) need no mask.
+
+    Returns (Tc, mask_start).
+    """
+    if causal:
+        m_end = input_pos + (q_tile + 1) * tile_m
+        tc = _cdiv(min(m_end, Skv), tile_n)
+    else:
+        tc = _cdiv(Skv, tile_n)
+    mask_start = min((input_pos + q_tile * tile_m) // tile_n, Skv // tile_n)
+    return tc, mask_start
+
+
+def classify_tiles(Sq, Skv, tile_m, tile_n, causal, input_pos=0):
+    """Count (unmasked, masked, skipped) K/V tiles over all query tiles.
+
+    [cuTile] Part 2 "K-loop split": tiles below mask_start run without mask
+    code, tiles from mask_start to the loop bound build the mask, and the rest
+    are skipped.  A tile counts as masked only where the mask is needed, i.e.
+    under causal masking or a ragged key tail.
+    """
+    n_q = _cdiv(Sq, tile_m)
+    n_k = _cdiv(Skv, tile_n)
+    even_k = Skv % tile_n == 0
+    unmasked = masked = 0
+    for t in range(n_q):
+        tc, ms = tile_plan(t, tile_m, tile_n, Skv, causal, input_pos)
+        if causal or not even_k:
+            unmasked += min(ms, tc)
+            masked += max(0, tc - ms)
+        else:
+            unmasked += tc
+    return unmasked, masked, n_q * n_k - unmasked - masked
+
+
+def attention_online_tiled(q, k, v, scale, causal=False, input_pos=0, tile_m=64, tile_n=64,
+                           split_loop=True):
+    """The [cuTile] kernel's tile loop, in float64, one (batch, head, query tile) at a time.
+
+    Steps, in the page's order and notation (Part 1):
+      * "Block ID mapping": kv head = head // QUERY_GROUP_SIZE.
+      * "Initializing accumulators": qk_scale = scale / ln 2; offs_m = tile
+        rows + input_pos; m_i = -inf, l_i = 0, acc = 0.
+      * "Loading the query tile": rows past Sq are padded with zeros and
+        dropped at the store.
+      * "The main loop over K/V tiles": Tc from ``tile_plan``; qk = q k^T.
+      * "Applying the causal mask" / Part 2 "K-loop split": on tiles j >=
+        mask_start (every tile when ``split_loop`` is False), keys past Skv
+        and, under causal masking, keys with offs_n > offs_m get -inf.
+      * "Online softmax update": m_ij = max(m_i, rowmax(qk) * qk_scale);
+        p = exp2(qk * qk_scale - m_ij); alpha = exp2(m_i - m_ij);
+        l_i = l_i * alpha + rowsum(p); acc = acc * alpha.
+      * "Accumulating the output": acc += p V; m_i = m_ij.
+      * "Final normalization and store": O = acc / l_i.
+    The log-sum-exp (on no page) is ln 2 * (m_i + log2 l_i) from the same state.
+    p is not rounded to the input type here: the oracle stays in float64.
+    Returns (O [B,Hq,Sq,D], LSE [B,Hq,Sq]).
+    """
+    B, Hq, Hkv, Sq, Skv, D = _shapes(q, k, v)
+    if not (math.isfinite(scale) and scale > 0):
+        raise ValueError("scale must be finite and > 0")
+    group = Hq // Hkv
+    qk_scale = scale * LOG2E
+    even_k = Skv % tile_n == 0
+    O = np.empty((B, Hq, Sq, D))
+    L = np.empty((B, Hq, Sq))
+    for b in range(B):
+        for head in range(Hq):
+            off_kv_h = head // group
+            kh = np.asarray(k[b, off_kv_h], np.float64)
+            vh = np.asarray(v[b, off_kv_h], np.float64)
+            for bid_x in range(_cdiv(Sq, tile_m)):
+                rows = bid_x * tile_m + np.arange(tile_m)
+                valid = rows < Sq
+                qt = np.zeros((tile_m, D))
+                qt[valid] = np.asarray(q[b, head, rows[valid]], np.float64)
+                offs_m = (rows + input_pos)[:, None]
+                m_i = np.full(tile_m, -np.inf)
+                l_i = np.zeros(tile_m)
+                acc = np.zeros((tile_m, D))
+                tc, mask_start = tile_plan(bid_x, tile_m, tile_n, Skv, causal, input_pos)
+                for j in range(tc):
+                    cols = j * tile_n + np.arange(tile_n)
+                    in_k = cols < Skv
+                    kt = np.zeros((tile_n, D))
+                    vt = np.zeros((tile_n, D))
+                    kt[in_k] = kh[cols[in_k]]
+                    vt[in_k] = vh[cols[in_k]]
+                    qk = qt @ kt.T
+                    if (causal or not even_k) and (j >= mask_start or not split_loop):
+                        mask = np.ones((tile_m, tile_n), dtype=bool)
+                        if not even_k:
+                            mask &= in_k[None, :]
+                        if causal:
+                            mask &= offs_m >= cols[None, :]
+                        qk = qk + np.where(mask, 0.0, -np.inf)
+                    qk_max = qk.max(axis=1)
+                    m_ij = np.maximum(m_i, qk_max * qk_scale)
+                    p = np.exp2(qk * qk_scale - m_ij[:, None])
+                    l_ij = p.sum(axis=1)
+                    alpha = np.exp2(m_i - m_ij)
+                    l_i = l_i * alpha + l_ij
+                    acc = acc * alpha[:, None] + p @ vt
+                    m_i = m_ij
+                out = acc / l_i[:, None]
+                lse = (m_i + np.log2(l_i)) * LN2
+                O[b, head, rows[valid]] = out[valid]
+                L[b, head, rows[valid]] = lse[valid]
+    return O, L
