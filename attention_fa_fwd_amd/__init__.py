@@ -1,0 +1,162 @@
+"""MI355X (gfx950) FlashAttention-style attention forward pass.
+
+A thin ctypes binding over the C ABI in ``include/fa_fwd.h`` (``libfa_fwd.so``,
+built in-tree by ``attention_fa_fwd_amd.build``).  This module only marshals
+torch tensors into pointers and sizes and passes the current HIP stream; every
+step of the computation runs in the HIP kernels.  There is no fallback: if the
+library is missing or the tensors are not on a GPU, the call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+__all__ = ["fa_fwd", "fa_fwd_into", "select_config", "config_names", "num_configs", "FaError",
+           "load_library", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_fwd.so")
+
+FA_DTYPE_FP16 = 0
+FA_DTYPE_BF16 = 1
+
+_lib = None
+_lock = threading.Lock()
+
+_c_int, _c_float, _vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+_FWD_ARGS = [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
+             _c_int, _c_int, _c_int, _vp]
+
+
+class FaError(RuntimeError):
+    """A nonzero status from the C ABI."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"fa_fwd failed ({code}): {message}")
+        self.code = code
+
+
+def _declare(lib):
+    lib.fa_fwd.argtypes = _FWD_ARGS
+    lib.fa_fwd.restype = _c_int
+    lib.fa_fwd_config.argtypes = _FWD_ARGS + [_c_int]
+    lib.fa_fwd_config.restype = _c_int
+    lib.fa_select_config.argtypes = [_c_int] * 9
+    lib.fa_select_config.restype = _c_int
+    lib.fa_num_configs.argtypes = []
+    lib.fa_num_configs.restype = _c_int
+    lib.fa_config_name.argtypes = [_c_int]
+    lib.fa_config_name.restype = ctypes.c_char_p
+    lib.fa_strerror.argtypes = [_c_int]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    return lib
+
+
+def load_library(path: str = LIB_PATH):
+    """Load ``libfa_fwd.so`` and declare the C signatures.
+
+    The in-tree library is loaded once and cached; another ``path`` is loaded
+    on its own.  Raises RuntimeError if the file does not exist.
+    """
+    global _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"HIP attention library not built: {path} is missing "
+            "(run `python -m attention_fa_fwd_amd.build` or __graft_entry__.build())")
+    if path != LIB_PATH:
+        return _declare(ctypes.CDLL(path))
+    with _lock:
+        if _lib is None:
+            _lib = _declare(ctypes.CDLL(path))
+        return _lib
+
+
+def _dtype_code(dtype) -> int:
+    import torch
+
+    if dtype == torch.float16:
+        return FA_DTYPE_FP16
+    if dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {dtype}: expected torch.float16 or torch.bfloat16")
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise FaError(rc, load_library().fa_strerror(rc).decode())
+
+
+def fa_fwd_into(q, k, v, out, lse, scale=None, causal=True, input_pos=0, config=-1, stream=None):
+    """Run the kernel into caller-provided ``out`` [B,Hq,Sq,D] and ``lse`` [B,Hq,Sq] (fp32).
+
+    All tensors must be contiguous and on the same GPU.  ``stream`` is a raw
+    hipStream_t value; by default torch's current stream on q's device.
+    """
+    import torch
+
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, S, D]")
+    if k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
+        raise TypeError("q, k, v and out must share one dtype")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Skv, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("out must match q and lse must be [B, Hq, Sq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        rc = lib.fa_fwd_config(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), B, Hq, Hkv, Sq, Skv, D, float(scale),
+                               1 if causal else 0, int(input_pos), _dtype_code(q.dtype),
+                               stream, int(config))
+    _check(rc)
+    return out, lse
+
+
+def fa_fwd(q, k, v, scale=None, causal=True, input_pos=0, config=-1):
+    """Attention forward: returns (out [B,Hq,Sq,D] in q's dtype, lse [B,Hq,Sq] fp32).
+
+    q: [B,Hq,Sq,D]; k, v: [B,Hkv,Skv,D]; fp16 or bf16 on one GPU.  ``scale``
+    defaults to 1/sqrt(D); ``causal`` to True; under causal masking query i
+    sees key j iff j <= input_pos + i.  Inputs are made contiguous.
+    """
+    import torch
+
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    return fa_fwd_into(q, k, v, out, lse, scale=scale, causal=causal, input_pos=input_pos,
+                       config=config)
+
+
+def select_config(B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype) -> int:
+    """Configuration id the dispatch table picks (dtype: torch dtype or FA code)."""
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    rc = load_library().fa_select_config(B, Hq, Hkv, Sq, Skv, D, 1 if causal else 0, input_pos, code)
+    _check(rc if rc < 0 else 0)
+    return rc
+
+
+def num_configs() -> int:
+    return load_library().fa_num_configs()
+
+
+def config_names():
+    lib = load_library()
+    return [lib.fa_config_name(i).decode() for i in range(lib.fa_num_configs())]

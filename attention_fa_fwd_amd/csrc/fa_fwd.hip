@@ -1,0 +1,216 @@
+// fa_fwd.hip -- host side of the attention forward library: argument validation, the
+// static dispatch table, kernel launch, and the exported C ABI declared in fa_fwd.h.
+//
+// The dispatch table replaces the runtime autotuner of "Tuning Flash Attention for peak
+// performance in NVIDIA CUDA Tile" (Part 2 "Autotuning") and the length threshold of
+// "How I Beat PyTorch's Flash Attention" ("Phase 5: Adaptive Tile Dispatch"): a fixed
+// list of compiled tile configurations and a deterministic rule that picks one from the
+// problem shape, so the same call always runs the same kernel.
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+
+#include "fa_fwd.h"
+#include "fa_fwd_kernel.hpp"
+
+namespace {
+
+using fa::Cfg;
+using fa::Params;
+
+typedef hipError_t (*LaunchFn)(const Params&, hipStream_t);
+
+struct ConfigEntry {
+    const char* name;
+    int D, bf16, causal;
+    int BN, QB, WPH, HPW;
+    LaunchFn launch;
+};
+
+template <class C>
+hipError_t launch_cfg(const Params& p, hipStream_t s) {
+    const long long wgs = (long long)p.n_tiles * p.B * p.n_hgroups;
+    hipLaunchKernelGGL(fa::fa_fwd_kernel<C>, dim3((unsigned)wgs), dim3(C::NT), 0, s, p);
+    return hipGetLastError();
+}
+
+#define FA_STR2(x) #x
+#define FA_STR(x) FA_STR2(x)
+#define FA_ENTRY(D, BN, QB, WPH, HPW, CAUSAL, BF16, CNAME, TNAME)                             \
+    ConfigEntry{"D" FA_STR(D) "_BN" FA_STR(BN) "_Mw" FA_STR(QB) "x32_WPH" FA_STR(WPH)        \
+                "_HPW" FA_STR(HPW) "_" CNAME "_" TNAME,                                        \
+                D, BF16, CAUSAL, BN, QB, WPH, HPW,                                              \
+                &launch_cfg<Cfg<D, BN, QB, WPH, HPW, CAUSAL, BF16>>}
+
+#define FA_TILES(D, CAUSAL, BF16, CNAME, TNAME)                    \
+    FA_ENTRY(D, 64, 1, 4, 1, CAUSAL, BF16, CNAME, TNAME),          \
+    FA_ENTRY(D, 64, 1, 1, 4, CAUSAL, BF16, CNAME, TNAME),          \
+    FA_ENTRY(D, 64, 1, 2, 2, CAUSAL, BF16, CNAME, TNAME),          \
+    FA_ENTRY(D, 64, 2, 4, 1, CAUSAL, BF16, CNAME, TNAME)
+
+const ConfigEntry kConfigs[] = {
+    FA_TILES(128, 1, 1, "causal", "bf16"), FA_TILES(128, 0, 1, "full", "bf16"),
+    FA_TILES(128, 1, 0, "causal", "fp16"), FA_TILES(128, 0, 0, "full", "fp16"),
+    FA_TILES(64, 1, 1, "causal", "bf16"),  FA_TILES(64, 0, 1, "full", "bf16"),
+    FA_TILES(64, 1, 0, "causal", "fp16"),  FA_TILES(64, 0, 0, "full", "fp16"),
+};
+constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
+
+bool overlaps(uintptr_t a, size_t na, uintptr_t b, size_t nb) {
+    return a < b + nb && b < a + na;
+}
+
+// Pure host validation: no HIP call.  Returns FA_OK or the first failing check.
+int validate(const void* q, const void* k, const void* v, void* out, float* lse,
+             int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
+             int input_pos, int dtype) {
+    if (!q || !k || !v || !out || !lse) return FA_ERR_NULL_POINTER;
+    if (B < 0 || Hq < 0 || Sq < 0 || Hkv < 1 || Skv < 1) return FA_ERR_INVALID_SHAPE;
+    // Head indices b*H + h are 32-bit in the kernel; byte sizes stay below 2^50.
+    if ((long long)B * Hq > INT_MAX || (long long)B * Hkv > INT_MAX) return FA_ERR_INVALID_SHAPE;
+    const double qe = (double)B * Hq * Sq * 128.0 * 2.0;
+    const double ke = (double)B * Hkv * Skv * 128.0 * 2.0;
+    if (qe > 1125899906842624.0 || ke > 1125899906842624.0) return FA_ERR_INVALID_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_HEAD_GROUP;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_SCALE;
+    if (input_pos < 0 || (long long)input_pos + Sq > INT_MAX) return FA_ERR_INVALID_INPUT_POS;
+    (void)causal;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15u) return FA_ERR_MISALIGNED;
+    if ((uintptr_t)lse & 3u) return FA_ERR_MISALIGNED;
+    const size_t qb = (size_t)B * Hq * Sq * D * 2, kb = (size_t)B * Hkv * Skv * D * 2;
+    const size_t lb = (size_t)B * Hq * Sq * 4;
+    const uintptr_t o = (uintptr_t)out, l = (uintptr_t)lse;
+    if (qb > 0 && (overlaps(o, qb, (uintptr_t)q, qb) || overlaps(o, qb, (uintptr_t)k, kb) ||
+                   overlaps(o, qb, (uintptr_t)v, kb) || overlaps(o, qb, l, lb) ||
+                   overlaps(l, lb, (uintptr_t)q, qb) || overlaps(l, lb, (uintptr_t)k, kb) ||
+                   overlaps(l, lb, (uintptr_t)v, kb)))
+        return FA_ERR_ALIAS;
+    return FA_OK;
+}
+
+bool applicable(const ConfigEntry& c, int Hq, int Hkv, int D, int causal, int dtype) {
+    const int group = Hq / Hkv;
+    return c.D == D && c.bf16 == (dtype == FA_DTYPE_BF16) && c.causal == (causal != 0) &&
+           group % c.HPW == 0;
+}
+
+int find(int D, int bf16, int causal, int BN, int QB, int WPH, int HPW) {
+    for (int i = 0; i < kNumConfigs; ++i) {
+        const ConfigEntry& c = kConfigs[i];
+        if (c.D == D && c.bf16 == bf16 && c.causal == causal && c.BN == BN && c.QB == QB &&
+            c.WPH == WPH && c.HPW == HPW)
+            return i;
+    }
+    return -1;
+}
+
+// The dispatch rule.  Grouped-query problems pack 4 query heads of a group into one
+// workgroup, so each K/V tile is read once for all of them; groups of 2 pack 2 heads;
+// the rest use 128 positions of one head.
+int select(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal, int input_pos, int dtype) {
+    (void)B;
+    (void)Sq;
+    (void)Skv;
+    (void)input_pos;
+    const int bf16 = dtype == FA_DTYPE_BF16;
+    const int cz = causal != 0;
+    const int group = Hq / Hkv;
+    if (group % 4 == 0) return find(D, bf16, cz, 64, 1, 1, 4);
+    if (group % 2 == 0) return find(D, bf16, cz, 64, 1, 2, 2);
+    return find(D, bf16, cz, 64, 1, 4, 1);
+}
+
+int run(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+        int Hkv, int Sq, int Skv, int D, float scale, int causal, int input_pos, int dtype,
+        void* stream, int config) {
+    int rc = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos, dtype);
+    if (rc != FA_OK) return rc;
+    if (config < -1 || config >= kNumConfigs) return FA_ERR_INVALID_CONFIG;
+    if (config == -1) config = select(B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype);
+    if (config < 0) return FA_ERR_INVALID_CONFIG;
+    const ConfigEntry& c = kConfigs[config];
+    if (!applicable(c, Hq, Hkv, D, causal, dtype)) return FA_ERR_INVALID_CONFIG;
+    if ((long long)B * Hq * Sq == 0) return FA_OK;
+
+    const int bmp = 32 * c.QB * c.WPH;
+    Params p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = out;
+    p.lse = lse;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Sq = Sq;
+    p.Skv = Skv;
+    p.input_pos = causal ? input_pos : 0;
+    p.c = (float)((double)scale * 1.4426950408889634073599246810019);  // scale * log2(e)
+    p.group = Hq / Hkv;
+    p.n_tiles = (Sq + bmp - 1) / bmp;
+    p.n_hgroups = Hq / c.HPW;
+    const long long wgs = (long long)p.n_tiles * B * p.n_hgroups;
+    if (wgs > 0x7fffffffLL) return FA_ERR_INVALID_SHAPE;
+    return c.launch(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+           int Hkv, int Sq, int Skv, int D, float scale, int causal, int input_pos, int dtype,
+           void* stream) {
+    return run(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos, dtype,
+               stream, -1);
+}
+
+int fa_fwd_config(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                  int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
+                  int input_pos, int dtype, void* stream, int config) {
+    return run(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos, dtype,
+               stream, config);
+}
+
+int fa_select_config(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal, int input_pos,
+                     int dtype) {
+    if (B < 0 || Hq < 0 || Sq < 0 || Hkv < 1 || Skv < 1) return FA_ERR_INVALID_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_HEAD_GROUP;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
+    if (input_pos < 0) return FA_ERR_INVALID_INPUT_POS;
+    const int c = select(B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype);
+    return c < 0 ? FA_ERR_INVALID_CONFIG : c;
+}
+
+int fa_num_configs(void) { return kNumConfigs; }
+
+const char* fa_config_name(int config) {
+    return (config >= 0 && config < kNumConfigs) ? kConfigs[config].name : nullptr;
+}
+
+const char* fa_strerror(int code) {
+    switch (code) {
+        case FA_OK: return "success";
+        case FA_ERR_NULL_POINTER: return "a tensor pointer is NULL";
+        case FA_ERR_INVALID_SHAPE: return "invalid sizes (B, Hq, Sq >= 0; Hkv, Skv >= 1; sizes too large)";
+        case FA_ERR_HEAD_GROUP: return "Hq is not a multiple of Hkv";
+        case FA_ERR_UNSUPPORTED_HEAD_DIM: return "head dim must be 64 or 128";
+        case FA_ERR_UNSUPPORTED_DTYPE: return "dtype must be FA_DTYPE_FP16 or FA_DTYPE_BF16";
+        case FA_ERR_INVALID_SCALE: return "scale must be finite and > 0";
+        case FA_ERR_INVALID_INPUT_POS: return "input_pos must be >= 0 and input_pos + Sq must fit in int";
+        case FA_ERR_MISALIGNED: return "q/k/v/out must be 16-byte aligned and lse 4-byte aligned";
+        case FA_ERR_ALIAS: return "out or lse overlaps an input or each other";
+        case FA_ERR_INVALID_CONFIG: return "kernel configuration id out of range or not applicable to this call";
+        case FA_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status code";
+    }
+}
+
+}  // extern "C"

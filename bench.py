@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X attention forward kernel.
+
+Prints one JSON line: attention-forward TFLOP/s on the causal grouped-query workload
+(B=1, Hq=32, Hkv=4, Sq=Skv=8192, D=128, bf16), its fraction of the MI355X dense bf16
+MFMA peak, and the fp64 CPU oracle timed on a bounded sample of the same workload.
+
+FLOPs are counted as 4*B*Hq*Sq*Skv*D, halved when causal.  Inputs are resident in HBM
+before the timed region; each step is one call of the library's fa_fwd on torch's
+current stream, timed with HIP events recorded on that stream.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s and % of MI355X dense bf16 MFMA peak (causal, D=128)"
+HEADLINE = "gqa8_causal_s8192_d128_bf16"
+# MI355X dense bf16/fp16 MFMA peak: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU.
+PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "attention_fa_fwd_amd", "csrc", f)
+                  for f in ("fa_fwd_kernel.hpp", "fa_fwd.hip")]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def literal_flops(w):
+    f = 4.0 * w["B"] * w["Hq"] * w["Sq"] * w["Skv"] * w["D"]
+    return f / 2 if w["causal"] else f
+
+
+def exact_flops(w):
+    """4*D per visible (query, key) pair."""
+    Sq, Skv, pos = w["Sq"], w["Skv"], w["input_pos"]
+    if not w["causal"]:
+        pairs = Sq * Skv
+    else:
+        pairs = 0
+        # visible keys of row i: min(Skv, pos + i + 1)
+        full_from = max(0, Skv - pos - 1)  # rows i >= full_from see every key
+        n_part = min(Sq, full_from)
+        pairs += n_part * (pos + 1) + n_part * (n_part - 1) // 2
+        pairs += (Sq - n_part) * Skv
+    return 4.0 * w["D"] * w["B"] * w["Hq"] * pairs
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_bytes(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None if the
+    kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    e = t.get("workloads", {}).get(workload)
+    if not e:
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def time_gpu(name, steps, warmup, config=-1):
+    import torch
+
+    import attention_fa_fwd_amd as fa
+    from attention_fa_fwd_amd.inputs import WORKLOADS, make_workload
+
+    w = WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v, kw = make_workload(name, seed=0)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def step():
+        fa.fa_fwd_into(q, k, v, out, lse, scale=kw["scale"], causal=kw["causal"],
+                       input_pos=kw["input_pos"], config=config, stream=sp)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))  # ms per launch
+    total_ms = evs[0].elapsed_time(evs[-1])
+    cfg = config if config >= 0 else fa.select_config(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"],
+                                                      w["D"], w["causal"], w["input_pos"], q.dtype)
+    return dict(total_ms=total_ms, wall_s=wall, per_ms=per, kernel=fa.config_names()[cfg])
+
+
+def cpu_baseline(name):
+    """The fp64 oracle on one GQA group of query heads of batch 0 (bounded sample)."""
+    import numpy as np
+
+    import oracle
+    from attention_fa_fwd_amd.inputs import WORKLOADS, make_workload
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = len(os.sched_getaffinity(0))
+    w = dict(WORKLOADS[name])
+    q, k, v, kw = make_workload(name, seed=0)
+    G = w["Hq"] // w["Hkv"]
+    qs = q[:1, :G].double().numpy()
+    ks = k[:1, :1].double().numpy()
+    vs = v[:1, :1].double().numpy()
+    t0 = time.perf_counter()
+    oracle.attention_blocked(qs, ks, vs, kw["scale"], kw["causal"], kw["input_pos"])
+    dt = time.perf_counter() - t0
+    ws = dict(w, B=1, Hq=G, Hkv=1)
+    return dict(value=literal_flops(ws) / dt / 1e12, unit="TFLOP/s", cores=int(threads),
+                kind="oracle",
+                sample=f"batch 0, query heads 0..{G - 1} (one K/V head) of {name}; "
+                       f"{dt:.1f} s wall; same FLOP count rule",
+                wall_s=round(dt, 3))
+
+
+def bench_line(name, steps, warmup, config=-1, with_cpu=True):
+    from attention_fa_fwd_amd.inputs import WORKLOADS
+
+    w = WORKLOADS[name]
+    log(f"workload {name}: {w}")
+    r = time_gpu(name, steps, warmup, config)
+    ms_step = r["total_ms"] / steps
+    flops = literal_flops(w)
+    value = flops / (ms_step * 1e-3) / 1e12
+    mean_kernel_ms = sum(r["per_ms"]) / len(r["per_ms"])
+    achieved = flops / (mean_kernel_ms * 1e-3) / 1e12
+    med = r["per_ms"][len(r["per_ms"]) // 2]
+    p95 = r["per_ms"][min(len(r["per_ms"]) - 1, int(math.ceil(0.95 * len(r["per_ms"]))) - 1)]
+    log(f"kernel {r['kernel']}: mean {mean_kernel_ms * 1e3:.1f} us, median {med * 1e3:.1f} us, "
+        f"p95 {p95 * 1e3:.1f} us, min {r['per_ms'][0] * 1e3:.1f} us")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic: seeded N(0,1) q, k, v rounded to the storage dtype",
+        "config": {"workload": name, "B": w["B"], "Hq": w["Hq"], "Hkv": w["Hkv"], "Sq": w["Sq"],
+                   "Skv": w["Skv"], "D": w["D"], "causal": w["causal"],
+                   "input_pos": w["input_pos"], "kernel": r["kernel"], "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2),
+        "tflops_exact_pairs": round(exact_flops(w) / (ms_step * 1e-3) / 1e12, 2),
+        "kernel_us": {"mean": round(mean_kernel_ms * 1e3, 2), "median": round(med * 1e3, 2),
+                      "p95": round(p95 * 1e3, 2), "min": round(r["per_ms"][0] * 1e3, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_TFLOPS, 1),
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+                     "traffic": traffic_bytes(name)},
+    }
+    if with_cpu:
+        log("timing the fp64 CPU oracle on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline(name)
+    return line
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--config", type=int, default=-1, help="force a kernel configuration id")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true",
+                    help="also time every named workload (extra JSON lines on stderr)")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {a.gpus} is not supported "
+              "(the attention forward pass here has no multi-GPU path)", file=sys.stderr)
+        return 2
+    if a.steps < 1 or a.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+    line = bench_line(a.workload, a.steps, a.warmup, a.config, with_cpu=not a.no_cpu_baseline)
+    if a.all:
+        from attention_fa_fwd_amd.inputs import WORKLOADS
+
+        for name in WORKLOADS:
+            if name != a.workload:
+                extra = bench_line(name, a.steps, a.warmup, -1, with_cpu=False)
+                print("[bench-extra] " + json.dumps(extra), file=sys.stderr, flush=True)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())

@@ -1,0 +1,109 @@
+/*
+ * fa_fwd.h -- C ABI of the MI355X (gfx950) FlashAttention-style attention forward pass.
+ *
+ * The operation (sources cited by page title and section):
+ *   "Tuning Flash Attention for peak performance in NVIDIA CUDA Tile" (NVIDIA cuTile post):
+ *     "What is attention?"        O = softmax(scale * Q K^T + M) V per (batch, query head);
+ *     "Causal attention"          M = 0 where key j <= input_pos + i, -inf elsewhere;
+ *     "Grouped-query attention"   query head h reads K/V head h / (Hq / Hkv);
+ *     Part 1 "Initializing accumulators" / "The main loop over K/V tiles": the query
+ *       position carries an offset input_pos (a chunk of new queries against a cache);
+ *     "Launching the kernel: Host-side code": contiguous [B, H, S, D] tensors, an output
+ *       of the query's dtype, default scale 1/sqrt(D), launch on the caller's stream.
+ *   The log-sum-exp output is on no page: LSE[b,h,i] = ln sum_{j visible} exp(scale q_i.k_j),
+ *   the natural-log normaliser of each softmax row.
+ *
+ * Layout (row-major, contiguous, no strides):
+ *   q, out : [B, Hq,  Sq,  D]  elements of `dtype` (out has q's dtype)
+ *   k, v   : [B, Hkv, Skv, D]  elements of `dtype`
+ *   lse    : [B, Hq,  Sq]      float32
+ * All pointers are device pointers.  q, k, v and out must be 16-byte aligned (the kernels
+ * move 128-bit vectors); lse must be 4-byte aligned.  out and lse must not overlap the
+ * inputs or each other.
+ *
+ * Ownership: the caller owns every buffer.  The library allocates nothing, keeps no state
+ * besides constant tables, and may be called from several host threads at once.
+ *
+ * Asynchrony: the call validates its arguments on the host (no HIP call), enqueues one
+ * kernel on `stream` (a hipStream_t passed as void*; NULL = the null stream) and returns
+ * without synchronising.  Faults inside the kernel surface on the next synchronisation.
+ *
+ * Errors: a nonzero return leaves out and lse untouched and launches nothing, except
+ * FA_ERR_LAUNCH, which reports a failed launch.  Checks run in the order of the codes below.
+ */
+#ifndef FA_FWD_H
+#define FA_FWD_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of q, k, v and out.  Scores, softmax state and the accumulator are fp32. */
+enum fa_dtype {
+    FA_DTYPE_FP16 = 0,
+    FA_DTYPE_BF16 = 1
+};
+
+/* Status codes, in the order the arguments are checked. */
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL_POINTER = -1,         /* q, k, v, out or lse is NULL                         */
+    FA_ERR_INVALID_SHAPE = -2,        /* B, Hq, Sq < 0; Hkv, Skv < 1; B*H > INT_MAX; >= 2^50 B */
+    FA_ERR_HEAD_GROUP = -3,           /* Hq is not a multiple of Hkv                          */
+    FA_ERR_UNSUPPORTED_HEAD_DIM = -4, /* D not in {64, 128}                                   */
+    FA_ERR_UNSUPPORTED_DTYPE = -5,    /* dtype not an fa_dtype                                */
+    FA_ERR_INVALID_SCALE = -6,        /* scale not finite or not > 0                          */
+    FA_ERR_INVALID_INPUT_POS = -7,    /* input_pos < 0, or input_pos + Sq overflows int       */
+    FA_ERR_MISALIGNED = -8,           /* q/k/v/out not 16-byte or lse not 4-byte aligned      */
+    FA_ERR_ALIAS = -9,                /* out or lse overlaps an input or each other           */
+    FA_ERR_INVALID_CONFIG = -10,      /* fa_fwd_config: config id unknown or not applicable  */
+    FA_ERR_LAUNCH = -11               /* the kernel launch failed (hipGetLastError)           */
+};
+
+/*
+ * Attention forward pass: out = softmax(scale * q k^T + mask) v and lse, per (b, hq).
+ *
+ *   B, Hq, Hkv, Sq, Skv, D   sizes as in the layouts above; Hq % Hkv == 0, D in {64, 128}.
+ *   scale                    multiplies q.k before the softmax; finite and > 0 (1/sqrt(D)
+ *                            is the usual value).
+ *   causal                   nonzero: query i sees key j iff j <= input_pos + i.
+ *                            zero: every key is visible and input_pos is ignored.
+ *   input_pos                position of query 0 (>= 0); input_pos = Skv - Sq aligns the
+ *                            last query with the last key (a new chunk against a cache).
+ *   dtype                    an fa_dtype.
+ *   stream                   hipStream_t to enqueue on (NULL = null stream).
+ * B*Hq*Sq == 0 returns FA_OK without a launch.  Returns an fa_status.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+           int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+           int causal, int input_pos, int dtype, void* stream);
+
+/*
+ * Same as fa_fwd, but runs kernel configuration `config` (0 <= config < fa_num_configs())
+ * instead of the one the dispatch table picks; config = -1 uses the table.  A configuration
+ * whose head dim, dtype, causality or head grouping does not fit the call returns
+ * FA_ERR_INVALID_CONFIG.  Meant for tests and tile sweeps.
+ */
+int fa_fwd_config(const void* q, const void* k, const void* v, void* out, float* lse,
+                  int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+                  int causal, int input_pos, int dtype, void* stream, int config);
+
+/* Configuration the dispatch table picks for these arguments, or a negative fa_status. */
+int fa_select_config(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                     int input_pos, int dtype);
+
+/* Number of kernel configurations compiled into the library. */
+int fa_num_configs(void);
+
+/* Static description of configuration `config` (tile sizes, waves, head packing, dtype,
+ * head dim, causality), or NULL for an unknown id.  The string is owned by the library. */
+const char* fa_config_name(int config);
+
+/* Static, human-readable text for an fa_status code.  Never NULL. */
+const char* fa_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_FWD_H */

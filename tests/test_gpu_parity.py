@@ -1,0 +1,190 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle.
+
+Tolerances: max |O_gpu - O_oracle| <= 4e-3 (fp16) or 1.6e-2 (bf16); max |LSE_gpu -
+LSE_oracle| <= 1e-3; no NaN or Inf.  Small shapes are compared element by element;
+the named full-size workloads on sampled rows (the oracle evaluates each row from its
+definition), in the configuration the benchmark times.
+"""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_fa_fwd_amd as fa
+import oracle
+from attention_fa_fwd_amd.inputs import WORKLOADS, make_qkv, make_workload
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {torch.float16: 4e-3, torch.bfloat16: 1.6e-2}
+TOL_LSE = 1e-3
+DT = {"fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _say(*a):
+    print("[parity]", *a, file=sys.stderr, flush=True)
+
+
+def _f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def run_gpu(q, k, v, scale, causal, pos, config=-1):
+    dev = torch.device("cuda:0")
+    out, lse = fa.fa_fwd(q.to(dev), k.to(dev), v.to(dev), scale=scale, causal=causal,
+                         input_pos=pos, config=config)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def check_full(q, k, v, scale, causal, pos, out, lse, what=""):
+    O, L = oracle.attention_blocked(_f64(q), _f64(k), _f64(v), scale, causal, pos)
+    o, l = _f64(out), _f64(lse)
+    assert np.isfinite(o).all() and np.isfinite(l).all(), f"non-finite output {what}"
+    eo = float(np.max(np.abs(o - O))) if o.size else 0.0
+    el = float(np.max(np.abs(l - L))) if l.size else 0.0
+    assert eo <= TOL_O[q.dtype], f"O max abs err {eo:.3e} {what}"
+    assert el <= TOL_LSE, f"LSE max abs err {el:.3e} {what}"
+    return eo, el
+
+
+SMALL = [
+    # B, Hq, Hkv, Sq, Skv, D, causal, pos
+    (1, 2, 2, 128, 128, 64, False, 0),
+    (1, 2, 2, 128, 128, 64, True, 0),
+    (2, 4, 4, 300, 300, 128, True, 0),        # several tiles + ragged tail
+    (1, 8, 2, 257, 391, 128, True, 134),      # ragged both, GQA 4, offset
+    (1, 8, 1, 65, 129, 64, False, 0),         # MQA
+    (1, 8, 8, 1, 1, 128, True, 0),            # single query, single key
+    (1, 4, 4, 1, 700, 128, True, 699),        # decode-like row, full visibility
+    (1, 4, 2, 17, 1, 64, True, 0),            # one key for every row
+    (1, 4, 4, 63, 65, 128, False, 0),
+    (1, 8, 4, 200, 200, 128, True, 500),      # input_pos + i beyond Skv: all keys visible
+    (3, 6, 3, 129, 64, 64, True, 0),          # Sq > Skv
+    (1, 32, 4, 256, 256, 128, True, 0),
+]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_small_shapes(shape, dtype):
+    B, Hq, Hkv, Sq, Skv, D, causal, pos = shape
+    _say("small", shape, dtype)
+    q, k, v = make_qkv(B, Hq, Hkv, Sq, Skv, D, dtype, seed=sum(shape))
+    scale = 1.0 / math.sqrt(D)
+    out, lse = run_gpu(q, k, v, scale, causal, pos)
+    check_full(q, k, v, scale, causal, pos, out, lse, f"{shape} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_every_config_on_same_input(dtype, causal):
+    """Every compiled configuration that fits the call agrees with the oracle."""
+    q, k, v = make_qkv(1, 8, 2, 333, 333, 128, dtype, seed=5)
+    pos = 7 if causal else 0
+    names = fa.config_names()
+    tested = 0
+    for cid, name in enumerate(names):
+        if not name.startswith("D128_") or (("_causal_" in name) != causal) or \
+                (("_bf16" in name) != (dtype == "bf16")):
+            continue
+        _say("config", name)
+        out, lse = run_gpu(q, k, v, 0.09, causal, pos, config=cid)
+        check_full(q, k, v, 0.09, causal, pos, out, lse, name)
+        tested += 1
+    assert tested >= 3
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_named_workload(name):
+    """Full-size workloads, dispatch-table config; sampled rows against the oracle."""
+    w = WORKLOADS[name]
+    _say("workload", name)
+    q, k, v, kw = make_workload(name, seed=0)
+    out, lse = run_gpu(q, k, v, kw["scale"], kw["causal"], kw["input_pos"])
+    o = out.to(torch.float64)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    rng = np.random.default_rng(1)
+    B, Hq, Sq = w["B"], w["Hq"], w["Sq"]
+    rows = {0, 1, 31, 32, 63, 64, 127, 128, 255, 256, Sq // 2, Sq - 2, Sq - 1}
+    samples = [(int(rng.integers(B)), int(rng.integers(Hq)), i) for i in sorted(rows) if i < Sq]
+    samples += [(int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(Sq)))
+                for _ in range(48)]
+    samples += [(B - 1, Hq - 1, Sq - 1), (0, 0, 0)]
+    qd, kd, vd = _f64(q), _f64(k), _f64(v)
+    O, L = oracle.attention_rows(qd, kd, vd, kw["scale"], kw["causal"], kw["input_pos"], samples)
+    for n, (b, h, i) in enumerate(samples):
+        eo = float(np.max(np.abs(o[b, h, i].numpy() - O[n])))
+        el = abs(float(lse[b, h, i]) - L[n])
+        assert eo <= TOL_O[q.dtype], f"{name} O row {(b, h, i)} err {eo:.3e}"
+        assert el <= TOL_LSE, f"{name} LSE row {(b, h, i)} err {el:.3e}"
+    if Sq * w["Skv"] <= 1 << 15:  # the smallest workload: every element
+        check_full(q, k, v, kw["scale"], kw["causal"], kw["input_pos"], out, lse, name)
+
+
+def test_causal_row0_is_exact():
+    """Query 0 sees only key 0: P = 1, l = 1, so O_0 = V_0 bit for bit."""
+    for dtype in ("fp16", "bf16"):
+        q, k, v = make_qkv(2, 8, 4, 100, 100, 128, dtype, seed=11)
+        out, lse = run_gpu(q, k, v, 0.1, True, 0)
+        G = 2
+        for h in range(8):
+            assert torch.equal(out[:, h, 0], v[:, h // G, 0])
+            want = 0.1 * (q[:, h, 0].double() * k[:, h // G, 0].double()).sum(-1)
+            assert torch.allclose(lse[:, h, 0].double(), want, atol=1e-4, rtol=0)
+
+
+def test_constant_keys_give_mean_of_values():
+    q, k, v = make_qkv(1, 4, 4, 150, 150, 64, "bf16", seed=12)
+    k[:] = k[:, :, :1]
+    out, _ = run_gpu(q, k, v, 0.125, True, 0)
+    csum = torch.cumsum(v.double(), dim=2)
+    mean = csum / torch.arange(1, 151, dtype=torch.float64)[None, None, :, None]
+    assert float((out.double() - mean).abs().max()) <= TOL_O[torch.bfloat16]
+
+
+def test_repeated_launches_bitwise_identical():
+    q, k, v = make_qkv(1, 32, 4, 1000, 1000, 128, "bf16", seed=13)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    ref = fa.fa_fwd(qd, kd, vd, causal=True)
+    for _ in range(3):
+        o, l = fa.fa_fwd(qd, kd, vd, causal=True)
+        assert torch.equal(o, ref[0]) and torch.equal(l, ref[1])
+
+
+def test_empty_and_errors_on_gpu():
+    dev = torch.device("cuda:0")
+    q = torch.zeros(1, 4, 0, 128, dtype=torch.bfloat16, device=dev)
+    k = torch.zeros(1, 4, 5, 128, dtype=torch.bfloat16, device=dev)
+    out, lse = fa.fa_fwd(q, k, k)
+    assert out.shape == (1, 4, 0, 128) and lse.shape == (1, 4, 0)
+    q = torch.zeros(1, 3, 4, 128, dtype=torch.bfloat16, device=dev)
+    k = torch.zeros(1, 2, 4, 128, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(fa.FaError):
+        fa.fa_fwd(q, k, k)
+    q = torch.zeros(1, 2, 4, 96, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(fa.FaError):
+        fa.fa_fwd(q, q, q)
+    q = torch.zeros(1, 2, 4, 128, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(fa.FaError):
+        fa.fa_fwd(q, q, q, scale=-1.0)
+    with pytest.raises(fa.FaError):
+        fa.fa_fwd(q, q, q, input_pos=-1)
+
+
+def test_runs_on_a_side_stream():
+    q, k, v = make_qkv(1, 8, 8, 200, 200, 128, "fp16", seed=14)
+    dev = torch.device("cuda:0")
+    s = torch.cuda.Stream(device=dev)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        out, lse = fa.fa_fwd(qd, kd, vd, causal=True)
+    s.synchronize()
+    check_full(q, k, v, 1 / math.sqrt(128), True, 0, out.cpu(), lse.cpu(), "side stream")
