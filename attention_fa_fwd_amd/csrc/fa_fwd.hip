@@ -68,7 +68,10 @@ bool overlaps(uintptr_t a, size_t na, uintptr_t b, size_t nb) {
 int validate(const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
              int input_pos, int dtype) {
-    if (!q || !k || !v || !out || !lse) return FA_ERR_NULL_POINTER;
+    // A pointer may be NULL only when its tensor has no elements (an empty problem).
+    const bool q_empty = B <= 0 || Hq <= 0 || Sq <= 0;
+    const bool kv_empty = B <= 0 || Hkv <= 0 || Skv <= 0;
+    if ((!q_empty && (!q || !out || !lse)) || (!kv_empty && (!k || !v))) return FA_ERR_NULL_POINTER;
     if (B < 0 || Hq < 0 || Sq < 0 || Hkv < 1 || Skv < 1) return FA_ERR_INVALID_SHAPE;
     // Head indices b*H + h are 32-bit in the kernel; byte sizes stay below 2^50.
     if ((long long)B * Hq > INT_MAX || (long long)B * Hkv > INT_MAX) return FA_ERR_INVALID_SHAPE;

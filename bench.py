@@ -196,6 +196,23 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True):
     return line
 
 
+COPY_BYTES = 1 << 30
+
+
+def calibrate_copy(reps=3):
+    """A plain device-to-device copy of COPY_BYTES (torch's copy kernel), for scaling the
+    rocprofv3 FETCH_SIZE / WRITE_SIZE counters: the kernel reads and writes COPY_BYTES."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copied {COPY_BYTES} bytes x {reps}")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,7 +223,12 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true",
                     help="also time every named workload (extra JSON lines on stderr)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
     a = ap.parse_args(argv)
+    if a.calibrate_copy:
+        calibrate_copy()
+        return 0
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {a.gpus} is not supported "
               "(the attention forward pass here has no multi-GPU path)", file=sys.stderr)

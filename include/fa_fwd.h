@@ -47,7 +47,7 @@ enum fa_dtype {
 /* Status codes, in the order the arguments are checked. */
 enum fa_status {
     FA_OK = 0,
-    FA_ERR_NULL_POINTER = -1,         /* q, k, v, out or lse is NULL                         */
+    FA_ERR_NULL_POINTER = -1,         /* a pointer is NULL although its tensor is not empty  */
     FA_ERR_INVALID_SHAPE = -2,        /* B, Hq, Sq < 0; Hkv, Skv < 1; B*H > INT_MAX; >= 2^50 B */
     FA_ERR_HEAD_GROUP = -3,           /* Hq is not a multiple of Hkv                          */
     FA_ERR_UNSUPPORTED_HEAD_DIM = -4, /* D not in {64, 128}                                   */
@@ -72,7 +72,8 @@ enum fa_status {
  *                            last query with the last key (a new chunk against a cache).
  *   dtype                    an fa_dtype.
  *   stream                   hipStream_t to enqueue on (NULL = null stream).
- * B*Hq*Sq == 0 returns FA_OK without a launch.  Returns an fa_status.
+ * B*Hq*Sq == 0 returns FA_OK without a launch; pointers of empty tensors may then be NULL.
+ * Returns an fa_status.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
            int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,

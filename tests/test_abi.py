@@ -80,7 +80,7 @@ def test_validation_codes(lib, over, code):
 
 def test_validation_order(lib):
     # several faults at once: the first check in header order wins
-    assert call(lib, q=0, B=-1, D=7) == -1
+    assert call(lib, q=0, Hq=3, D=7) == -1
     assert call(lib, B=-1, Hq=3, D=7) == -2
     assert call(lib, Hq=3, D=7, dtype=9) == -3
     assert call(lib, D=7, dtype=9, scale=0.0) == -4
@@ -90,6 +90,10 @@ def test_empty_problem_is_a_noop(lib):
     assert call(lib, B=0) == 0
     assert call(lib, Sq=0) == 0
     assert call(lib, Hq=0) == 0
+    # empty tensors may come with NULL pointers (torch gives them data_ptr() == 0)
+    assert call(lib, Sq=0, q=0, out=0, lse=0) == 0
+    assert call(lib, B=0, q=0, k=0, v=0, out=0, lse=0) == 0
+    assert call(lib, Sq=0, k=0) == -1   # K/V are not empty
 
 
 def test_config_table(lib):
