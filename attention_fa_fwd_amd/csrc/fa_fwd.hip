@@ -33,7 +33,7 @@ struct ConfigEntry {
 
 template <class C>
 hipError_t launch_cfg(const Params& p, hipStream_t s) {
-    const long long wgs = (long long)p.n_tiles * p.B * p.n_hgroups;
+    const long long wgs = (long long)p.n_tiles * p.hsub * p.B * p.Hkv;
     hipLaunchKernelGGL(fa::fa_fwd_kernel<C>, dim3((unsigned)wgs), dim3(C::NT), 0, s, p);
     return hipGetLastError();
 }
@@ -47,9 +47,12 @@ hipError_t launch_cfg(const Params& p, hipStream_t s) {
                 &launch_cfg<Cfg<D, BN, QB, WPH, HPW, CAUSAL, BF16>>}
 
 #define FA_TILES(D, CAUSAL, BF16, CNAME, TNAME)                    \
-    FA_ENTRY(D, 64, 1, 4, 1, CAUSAL, BF16, CNAME, TNAME),          \
     FA_ENTRY(D, 64, 1, 1, 4, CAUSAL, BF16, CNAME, TNAME),          \
+    FA_ENTRY(D, 64, 1, 2, 4, CAUSAL, BF16, CNAME, TNAME),          \
     FA_ENTRY(D, 64, 1, 2, 2, CAUSAL, BF16, CNAME, TNAME),          \
+    FA_ENTRY(D, 64, 1, 4, 2, CAUSAL, BF16, CNAME, TNAME),          \
+    FA_ENTRY(D, 64, 1, 4, 1, CAUSAL, BF16, CNAME, TNAME),          \
+    FA_ENTRY(D, 64, 1, 8, 1, CAUSAL, BF16, CNAME, TNAME),          \
     FA_ENTRY(D, 64, 2, 4, 1, CAUSAL, BF16, CNAME, TNAME)
 
 const ConfigEntry kConfigs[] = {
@@ -115,7 +118,7 @@ int find(int D, int bf16, int causal, int BN, int QB, int WPH, int HPW) {
 
 // The dispatch rule.  Grouped-query problems pack 4 query heads of a group into one
 // workgroup, so each K/V tile is read once for all of them; groups of 2 pack 2 heads;
-// the rest use 128 positions of one head.
+// the rest use 128 positions of one head.  Two 4-wave workgroups share a CU.
 int select(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal, int input_pos, int dtype) {
     (void)B;
     (void)Sq;
@@ -127,6 +130,22 @@ int select(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal, int input
     if (group % 4 == 0) return find(D, bf16, cz, 64, 1, 1, 4);
     if (group % 2 == 0) return find(D, bf16, cz, 64, 1, 2, 2);
     return find(D, bf16, cz, 64, 1, 4, 1);
+}
+
+// Workgroup -> XCD mapping.  The hardware hands workgroup w to XCD w % 8.  Mode 1 gives
+// each XCD whole (batch, K/V head) groups; mode 2 spreads each group over 8/ngrp XCDs.
+void xcd_mapping(int ngrp, int items_per_group, int* mode, int* arg) {
+    const long long n = (long long)ngrp * items_per_group;
+    *mode = 0;
+    *arg = 0;
+    if (n % fa::kNumXcd != 0) return;
+    if (ngrp % fa::kNumXcd == 0) {
+        *mode = 1;
+        *arg = ngrp / fa::kNumXcd;
+    } else if (fa::kNumXcd % ngrp == 0 && items_per_group % (fa::kNumXcd / ngrp) == 0) {
+        *mode = 2;
+        *arg = fa::kNumXcd / ngrp;
+    }
 }
 
 int run(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
@@ -157,9 +176,10 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
     p.c = (float)((double)scale * 1.4426950408889634073599246810019);  // scale * log2(e)
     p.group = Hq / Hkv;
     p.n_tiles = (Sq + bmp - 1) / bmp;
-    p.n_hgroups = Hq / c.HPW;
-    const long long wgs = (long long)p.n_tiles * B * p.n_hgroups;
+    p.hsub = p.group / c.HPW;
+    const long long wgs = (long long)p.n_tiles * p.hsub * B * Hkv;
     if (wgs > 0x7fffffffLL) return FA_ERR_INVALID_SHAPE;
+    xcd_mapping(B * Hkv, p.n_tiles * p.hsub, &p.map_mode, &p.map_arg);
     return c.launch(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -5,10 +5,11 @@
 // resident, streams K/V tiles through on-chip memory, and folds every tile into a running
 // row max m, row sum l and fp32 accumulator ("Understanding online softmax", "Online
 // softmax update"), normalising once at the end ("Final normalization and store").
-// Causal tiles past the diagonal are never visited and only diagonal/tail tiles build a
-// mask (Part 2 "K-loop split"); heavy causal tiles are launched first (Part 2 "ProgramId
-// remapping"); exp2 is used with log2(e) folded into the scale (Part 1 "Initializing
-// accumulators"; "How I Beat PyTorch's Flash Attention", "Phase 4").
+// Causal tiles past the diagonal are never visited, and the K loop is split into a
+// mask-free loop and a masked loop over the diagonal / key-tail tiles (Part 2 "K-loop
+// split"); heavy causal tiles are launched first (Part 2 "ProgramId remapping"); exp2 is
+// used with log2(e) folded into the scale (Part 1 "Initializing accumulators"; "How I
+// Beat PyTorch's Flash Attention", "Phase 4").
 //
 // The CDNA4 design (not the pages' sm_80/Blackwell one):
 //  * A wave owns 32*QB query rows of one head.  Scores are computed transposed,
@@ -19,18 +20,24 @@
 //  * The output is accumulated transposed too, O^T += V^T P^T.  The accumulator layout of
 //    S^T is exactly the B-operand layout P^T needs (keys 16*half + 8*(j/4) + 4*(l/32) +
 //    j%4 in slot j), so P goes from exp2 straight into the PV MFMA with no LDS round trip.
-//    V^T comes from LDS, where each V tile is stored transposed (d-major) with its rows
-//    in MFMA order, so each lane's 16 output values are 16 consecutive d (two 128-bit
-//    stores).
-//  * K/V tiles are double-buffered in LDS through registers: tile j+1 is fetched from
-//    HBM with 128-bit loads while tile j is computed.  Both LDS layouts are XOR-swizzled
-//    so the MFMA operand reads and the tile writes are bank-conflict free.
+//    V stays row-major in LDS; ds_read_b64_tr_b16 delivers V^T fragments: in each group
+//    of 16 lanes, lane i receives element (i mod 4) of the 8-byte rows addressed by lanes
+//    4j + i/4, j = 0..3.  The d-order of the fragments is chosen so that each lane ends
+//    with 16 consecutive d of its query (two 128-bit stores per 32-wide block).
+//  * K and V tiles are double-buffered in LDS through registers: tile j+1 is fetched from
+//    HBM with 128-bit loads while tile j is computed.  16-byte chunks are XOR-swizzled per
+//    row so that tile writes, K operand reads and V transpose reads are bank-conflict free.
+//  * Register use is held to 256 per lane so that two waves share each SIMD: one wave's
+//    softmax and memory latency overlap the other's MFMAs.
 //  * The running max is rescaled lazily: m is only raised (and acc, l rescaled) when some
 //    row's max grows by more than 2^8 in the exp2 domain; otherwise the stale max is
 //    kept.  softmax is invariant to the shift, p stays <= 2^8, and the normalisation at
 //    the end uses the same m for acc and l, so the result is the same softmax.
 //  * A workgroup is HPW heads x WPH position blocks.  HPW > 1 packs query heads of one
 //    GQA group into a workgroup: they share every K/V tile ("Grouped-query attention").
+//  * Workgroups are dispatched round-robin over the 8 XCDs.  The workgroup id is remapped
+//    so that each XCD works on whole (batch, K/V head) groups, keeping their K/V tiles in
+//    its own L2, and within an XCD the heaviest causal tiles come first.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -42,12 +49,15 @@ namespace fa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kNumXcd = 8;
 
 // Kernel arguments (one struct, passed by value).
 struct Params {
@@ -61,7 +71,9 @@ struct Params {
     float c;         // scale * log2(e): exp(scale*s - m) = exp2(c*s - m')
     int group;       // Hq / Hkv
     int n_tiles;     // query tiles per (batch, head group)
-    int n_hgroups;   // Hq / HPW
+    int hsub;        // head groups per K/V head: group / HPW
+    int map_mode;    // workgroup -> XCD mapping: 0 plain, 1 groups per XCD, 2 XCDs per group
+    int map_arg;     // mode 1: groups per XCD; mode 2: XCDs per group
 };
 
 // Compile-time configuration of one kernel instance.
@@ -77,9 +89,12 @@ struct Cfg {
     static constexpr int NW = WPH * HPW;
     static constexpr int NT = 64 * NW;
     static constexpr int BMP = 32 * QB * WPH;   // query positions per workgroup
+    static constexpr int LDS_BYTES = 2 * 2 * BN * D * 2;   // 2 buffers x (K + V)
+    static constexpr int WAVES_PER_SIMD = QB == 1 ? 2 : 1;  // register budget 256 / 512
     static_assert(D == 64 || D == 128, "head dim");
     static_assert(BN == 64 || BN == 128, "key tile");
     static_assert(QB == 1 || QB == 2, "query blocks per wave");
+    static_assert(NW == 4 || NW == 8, "waves per workgroup");
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -118,58 +133,49 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     }
 }
 
-// Low / high 16-bit halves of x (low half of the result) and y (high half).
-__device__ __forceinline__ uint32_t pack_lo16(uint32_t x, uint32_t y) {
-    return __builtin_amdgcn_perm(y, x, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pack_hi16(uint32_t x, uint32_t y) {
-    return __builtin_amdgcn_perm(y, x, 0x07060302u);
+// 8 bytes (4 x 16 bit) of a transposed LDS read; see the header comment for the lanes.
+__device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* p) {
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(p));
+    return __builtin_bit_cast(u32x2, r);
 }
 
-// --- LDS layouts -----------------------------------------------------------------------
-// K tile: [BN][D] row-major, 16-byte chunks XOR-swizzled by (row mod 8).
+// --- LDS tile layout: [BN][D] row-major, 16-byte chunks XOR-swizzled per row ------------
+// K rows (read 32 rows x one chunk per MFMA operand): chunk ^ (row mod 16) for D=128;
+// for D=64 (8 chunks) the swizzle also folds row bit 3 so 16 consecutive rows differ.
 template <int D>
-__device__ __forceinline__ int k_off(int row, int chunk16) {
-    return row * (D * 2) + ((chunk16 ^ (row & 7)) << 4);
+__device__ __forceinline__ int k_swz(int row) {
+    if constexpr (D == 128) return row & 15;
+    else return (row & 7) ^ ((row >> 3) & 1);
 }
-// V^T tile: [D][BN]; row R holds d = vt_row_to_d(R) so that MFMA row m of output block db
-// is d = db*32 + 16*(m/4 mod 2) + 4*(m/8) + m%4, i.e. a lane's accumulator values are 16
-// consecutive d.  8-byte chunks (4 keys) are XOR-swizzled per row.
-__device__ __forceinline__ int d_to_vt_row(int d) {
-    const int x = d & 31;                // x = 16*hh + 4*g + e
-    const int hh = x >> 4, g = (x >> 2) & 3, e = x & 3;
-    return (d & ~31) | (g << 3) | (hh << 2) | e;
+// V rows (transpose reads touch 4 consecutive keys x 4 chunks per 16 lanes): a swizzle
+// taken from key mod 4 that spreads those 16 pieces over distinct banks.
+__device__ __forceinline__ int v_swz_of(int key_mod4) {
+    return ((key_mod4 & 1) << 2) | ((key_mod4 >> 1) & 1) | (((key_mod4 >> 1) & 1) << 3);
 }
-template <int BN>
-__device__ __forceinline__ int vt_swz(int R) {
-    const int u = (R >> 4) & 7;
-    const int phi = (u & 3) | ((u & 4) << 1);
-    return ((R & 15) ^ phi) & (BN / 4 - 1);
-}
-template <int BN>
-__device__ __forceinline__ int vt_off(int R, int chunk8) {
-    return R * (BN * 2) + ((chunk8 ^ vt_swz<BN>(R)) << 3);
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+    return v_swz_of(row & 3) & (D / 8 - 1);
 }
 
 template <class C>
-__global__ __attribute__((amdgpu_flat_work_group_size(C::NT, C::NT), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(C::NT, C::NT), amdgpu_waves_per_eu(C::WAVES_PER_SIMD, C::WAVES_PER_SIMD)))
 void fa_fwd_kernel(Params p) {
     constexpr int D = C::D, BN = C::BN, QB = C::QB, NT = C::NT, WPH = C::WPH, HPW = C::HPW;
     constexpr bool CAUSAL = C::CAUSAL, BF16 = C::BF16;
     constexpr int KB = BN / 32;          // 32-key blocks per tile
     constexpr int DK = D / 16;           // k-steps of Q K^T
     constexpr int DB = D / 32;           // 32-wide d blocks of O
-    constexpr int K_BYTES = BN * D * 2;
-    constexpr int BUF = 2 * K_BYTES;     // K tile + V^T tile
-    constexpr int KCH = BN * D / 8;      // 16-byte chunks per K tile
-    constexpr int KLD = KCH / NT;
-    constexpr int VBL = (BN / 4) * (D / 8);   // 4-key x 8-d blocks per V tile
-    constexpr int VLD = (VBL + NT - 1) / NT;
+    constexpr int ROWB = D * 2;          // bytes per K/V row
+    constexpr int TILE = BN * ROWB;      // bytes per K (or V) tile
+    constexpr int BUF = 2 * TILE;        // K tile + V tile
+    constexpr int CPR = D / 8;           // 16-byte chunks per row
+    constexpr int LD = BN * CPR / NT;    // 16-byte chunks of each tile per thread
     constexpr float TAU = 8.0f;          // lazy-rescale threshold (log2 domain)
     constexpr float LN2 = 0.69314718055994530942f;
-    static_assert(KCH % NT == 0, "K tile chunks per thread");
+    static_assert(BN * CPR % NT == 0, "tile chunks per thread");
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -177,15 +183,32 @@ void fa_fwd_kernel(Params p) {
     const int l32 = lane & 31;
     const int h = lane >> 5;
 
-    // Workgroup -> (query tile, batch, head group).  Causal: heaviest tiles first.
-    const int bg = p.B * p.n_hgroups;
-    int tile = blockIdx.x / bg;
-    const int rem = blockIdx.x - tile * bg;
-    if (CAUSAL) tile = p.n_tiles - 1 - tile;
-    const int b = rem / p.n_hgroups;
-    const int hg = rem - b * p.n_hgroups;
-    const int hq = hg * HPW + w / WPH;
-    const int kvh = (hg * HPW) / p.group;
+    // Workgroup -> (batch, K/V head, head subgroup, query tile); see the header comment.
+    const int ipg = p.n_tiles * p.hsub;          // work items per (batch, K/V head) group
+    const int ngrp = p.B * p.Hkv;
+    int grp, item;
+    {
+        const int wg = blockIdx.x;
+        if (p.map_mode == 1) {
+            const int x = wg % kNumXcd, s = wg / kNumXcd;
+            grp = x * p.map_arg + s % p.map_arg;
+            item = s / p.map_arg;
+        } else if (p.map_mode == 2) {
+            const int x = wg % kNumXcd, s = wg / kNumXcd;
+            grp = x / p.map_arg;
+            item = s * p.map_arg + x % p.map_arg;
+        } else {
+            grp = wg % ngrp;
+            item = wg / ngrp;
+        }
+    }
+    const int b = grp / p.Hkv;
+    const int kvh = grp - b * p.Hkv;
+    const int trank = item / p.hsub;
+    const int hs = item - trank * p.hsub;
+    const int tile = CAUSAL ? p.n_tiles - 1 - trank : trank;
+    (void)ipg;
+    const int hq = kvh * p.group + hs * HPW + w / WPH;
     const int q0 = tile * C::BMP;
     const int qw0 = q0 + (w % WPH) * (32 * QB);
 
@@ -195,33 +218,27 @@ void fa_fwd_kernel(Params p) {
     const T* vp = (const T*)p.v + (size_t)(b * p.Hkv + kvh) * p.Skv * D;
 
     // Queries of this wave, as the B operand of S^T = K Q^T: lane l holds row l%32 of
-    // query block qb, elements dk*16 + 8*(l/32) .. +8.
+    // query block qb, elements dk*16 + 8*(l/32) .. +8.  Rows past Sq read row Sq-1; their
+    // results are never stored.
     u32x4 qf[QB][DK];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const int row = qw0 + qb * 32 + l32;
+        const int row = min(qw0 + qb * 32 + l32, p.Sq - 1);
         const u32x4* src = (const u32x4*)(qp + (size_t)row * D);
 #pragma unroll
-        for (int dk = 0; dk < DK; ++dk) {
-            qf[qb][dk] = row < p.Sq ? src[dk * 2 + h] : (u32x4){0u, 0u, 0u, 0u};
-        }
+        for (int dk = 0; dk < DK; ++dk) qf[qb][dk] = src[dk * 2 + h];
     }
 
-    // Loop bounds.  Workgroup: Tc tiles.  Wave: tiles >= wave_tc are fully masked for
-    // its rows; tiles >= wave_ms need the mask (diagonal or key tail).
+    // Loop bounds.  Workgroup: Tc tiles, of which the first n_free need no mask.  Wave:
+    // tiles >= wave_tc are fully masked for its rows and skipped.
     const int q_last = min(q0 + C::BMP, p.Sq) - 1;
     const int Tc = CAUSAL ? (min(p.input_pos + q_last + 1, p.Skv) + BN - 1) / BN
                           : (p.Skv + BN - 1) / BN;
+    const int n_free = min(CAUSAL ? min((p.input_pos + q0) / BN, p.Skv / BN) : p.Skv / BN, Tc);
     const int qw_last = min(qw0 + 32 * QB, p.Sq) - 1;
-    int wave_tc;
-    if (qw_last < qw0) {
-        wave_tc = 0;
-    } else if (CAUSAL) {
-        wave_tc = (min(p.input_pos + qw_last + 1, p.Skv) + BN - 1) / BN;
-    } else {
-        wave_tc = Tc;
-    }
-    const int wave_ms = CAUSAL ? min((p.input_pos + qw0) / BN, p.Skv / BN) : p.Skv / BN;
+    const int wave_tc = qw_last < qw0 ? 0
+                        : CAUSAL ? (min(p.input_pos + qw_last + 1, p.Skv) + BN - 1) / BN
+                                 : Tc;
 
     // Running state: m (exp2 domain, possibly stale), l, acc (= O^T blocks).
     float m_run[QB], l_run[QB];
@@ -234,84 +251,61 @@ void fa_fwd_kernel(Params p) {
         for (int db = 0; db < DB; ++db) acc[db][qb] = (f32x16){};
     }
 
-    // Register staging of the next tile.
-    u32x4 kreg[KLD];
-    u32x4 vreg[VLD][4];
-
+    // Tile staging: thread t moves chunks cid = t + i*NT (row cid / CPR, chunk cid % CPR)
+    // of both the K and the V tile.  Keys past Skv read row Skv-1 (masked later).
+    u32x4 kreg[LD], vreg[LD];
     auto fetch = [&](int j) {
         const int j0 = j * BN;
 #pragma unroll
-        for (int i = 0; i < KLD; ++i) {
+        for (int i = 0; i < LD; ++i) {
             const int cid = tid + i * NT;
-            const int row = cid / (D / 8), c = cid % (D / 8);
-            const int key = j0 + row;
-            kreg[i] = key < p.Skv ? *(const u32x4*)(kp + (size_t)key * D + c * 8)
-                                  : (u32x4){0u, 0u, 0u, 0u};
+            const int key = min(j0 + cid / CPR, p.Skv - 1);
+            const size_t off = (size_t)key * D + (cid % CPR) * 8;
+            kreg[i] = *(const u32x4*)(kp + off);
+            vreg[i] = *(const u32x4*)(vp + off);
         }
+    };
+    auto stash = [&](int buf) {
+        unsigned char* kb = smem + buf * BUF;
+        unsigned char* vb = kb + TILE;
 #pragma unroll
-        for (int i = 0; i < VLD; ++i) {
-            const int bid = tid + i * NT;
-            if (VBL % NT == 0 || bid < VBL) {
-                const int c = bid % (D / 8), r = bid / (D / 8);
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int key = j0 + 4 * r + kk;
-                    vreg[i][kk] = key < p.Skv ? *(const u32x4*)(vp + (size_t)key * D + c * 8)
-                                              : (u32x4){0u, 0u, 0u, 0u};
-                }
-            }
+        for (int i = 0; i < LD; ++i) {
+            const int cid = tid + i * NT;
+            const int row = cid / CPR, c = cid % CPR;
+            *(u32x4*)(kb + row * ROWB + ((c ^ k_swz<D>(row)) << 4)) = kreg[i];
+            *(u32x4*)(vb + row * ROWB + ((c ^ v_swz<D>(row)) << 4)) = vreg[i];
         }
     };
 
-    auto stash = [&](int buf) {
-        unsigned char* kb = smem + buf * BUF;
-        unsigned char* vb = kb + K_BYTES;
-#pragma unroll
-        for (int i = 0; i < KLD; ++i) {
-            const int cid = tid + i * NT;
-            const int row = cid / (D / 8), c = cid % (D / 8);
-            *(u32x4*)(kb + k_off<D>(row, c)) = kreg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VLD; ++i) {
-            const int bid = tid + i * NT;
-            if (VBL % NT == 0 || bid < VBL) {
-                const int c = bid % (D / 8), r = bid / (D / 8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int wd = e >> 1;
-                    uint32_t lo, hi;
-                    if (e & 1) {
-                        lo = pack_hi16(vreg[i][0][wd], vreg[i][1][wd]);
-                        hi = pack_hi16(vreg[i][2][wd], vreg[i][3][wd]);
-                    } else {
-                        lo = pack_lo16(vreg[i][0][wd], vreg[i][1][wd]);
-                        hi = pack_lo16(vreg[i][2][wd], vreg[i][3][wd]);
-                    }
-                    const int R = d_to_vt_row(8 * c + e);
-                    *(u32x2*)(vb + vt_off<BN>(R, r)) = (u32x2){lo, hi};
-                }
-            }
-        }
-    };
+    // Per-lane LDS offsets.  K operand: row kb*32 + l32, chunk (2dk + h) ^ k_swz(row); the
+    // swizzle depends only on l32, so chunk = (2dk) ^ ku with ku = h ^ k_swz(l32).
+    const int ku = h ^ k_swz<D>(l32);
+    const int k_lane = l32 * ROWB;
+    // V^T operand (two transpose reads per MFMA): this lane addresses key
+    // 4*h + jj (+ kb*32 + 16*hf + 8*r) and the 8-byte piece of d = db*32 + 16*(qq&1) +
+    // 8*(g&1) + 4*(qq>>1), with jj, qq from the lane's index in its 16-lane group g.
+    const int vs = lane & 15, vj = vs >> 2, vq = vs & 3, vg = lane >> 4;
+    const int v_lane_row = 4 * (vg >> 1) + vj;
+    const int vu = (2 * (vq & 1) + (vg & 1)) ^ (v_swz_of(vj) & (CPR - 1));   // chunk ^ 4*db
+    const int v_lane = v_lane_row * ROWB + (vq >> 1) * 8;
 
     auto compute = [&](int j, int buf, auto masked_tag) {
         constexpr bool MASKED = decltype(masked_tag)::value;
         const unsigned char* kb = smem + buf * BUF;
-        const unsigned char* vb = kb + K_BYTES;
+        const unsigned char* vb = kb + TILE;
 
         // S^T = K Q^T for this tile.
         f32x16 s[KB][QB];
 #pragma unroll
-        for (int kb2 = 0; kb2 < KB; ++kb2) {
+        for (int k2 = 0; k2 < KB; ++k2) {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[kb2][qb] = (f32x16){};
-            const int row = kb2 * 32 + l32;
+            for (int qb = 0; qb < QB; ++qb) s[k2][qb] = (f32x16){};
 #pragma unroll
             for (int dk = 0; dk < DK; ++dk) {
-                const u32x4 a = *(const u32x4*)(kb + k_off<D>(row, 2 * dk + h));
+                const u32x4 a = *(const u32x4*)(kb + k2 * 32 * ROWB + k_lane +
+                                                (((2 * dk) ^ ku) << 4));
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) s[kb2][qb] = mfma32<BF16>(a, qf[qb][dk], s[kb2][qb]);
+                for (int qb = 0; qb < QB; ++qb) s[k2][qb] = mfma32<BF16>(a, qf[qb][dk], s[k2][qb]);
             }
         }
 
@@ -320,13 +314,13 @@ void fa_fwd_kernel(Params p) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 const int qpos = p.input_pos + qw0 + qb * 32 + l32;
+                const int lim = CAUSAL ? min(qpos, p.Skv - 1) : p.Skv - 1;   // last visible key
 #pragma unroll
-                for (int kb2 = 0; kb2 < KB; ++kb2) {
+                for (int k2 = 0; k2 < KB; ++k2) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const int key = j0 + kb2 * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-                        const bool vis = key < p.Skv && (!CAUSAL || key <= qpos);
-                        if (!vis) s[kb2][qb][i] = -__builtin_inff();
+                        const int key = j0 + k2 * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+                        if (key > lim) s[k2][qb][i] = -__builtin_inff();
                     }
                 }
             }
@@ -338,9 +332,9 @@ void fa_fwd_kernel(Params p) {
         for (int qb = 0; qb < QB; ++qb) {
             float mx = -__builtin_inff();
 #pragma unroll
-            for (int kb2 = 0; kb2 < KB; ++kb2)
+            for (int k2 = 0; k2 < KB; ++k2)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb2][qb][i]);
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[k2][qb][i]);
             mx = xhalf_max(mx);
             const float m_new = fmaxf(m_run[qb], mx * p.c);
             if (__builtin_amdgcn_ballot_w64(m_new > m_run[qb] + TAU) != 0) {
@@ -353,20 +347,20 @@ void fa_fwd_kernel(Params p) {
             const float neg_m = -m_run[qb];
             float ls = 0.0f;
 #pragma unroll
-            for (int kb2 = 0; kb2 < KB; ++kb2) {
+            for (int k2 = 0; k2 < KB; ++k2) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float pv = fast_exp2(__builtin_fmaf(s[kb2][qb][i], p.c, neg_m));
-                    s[kb2][qb][i] = pv;
+                    const float pv = fast_exp2(__builtin_fmaf(s[k2][qb][i], p.c, neg_m));
+                    s[k2][qb][i] = pv;
                     ls += pv;
                 }
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
-                    pk[kb2][qb][hf] = (u32x4){
-                        pack2<BF16>(s[kb2][qb][8 * hf + 0], s[kb2][qb][8 * hf + 1]),
-                        pack2<BF16>(s[kb2][qb][8 * hf + 2], s[kb2][qb][8 * hf + 3]),
-                        pack2<BF16>(s[kb2][qb][8 * hf + 4], s[kb2][qb][8 * hf + 5]),
-                        pack2<BF16>(s[kb2][qb][8 * hf + 6], s[kb2][qb][8 * hf + 7])};
+                    pk[k2][qb][hf] = (u32x4){
+                        pack2<BF16>(s[k2][qb][8 * hf + 0], s[k2][qb][8 * hf + 1]),
+                        pack2<BF16>(s[k2][qb][8 * hf + 2], s[k2][qb][8 * hf + 3]),
+                        pack2<BF16>(s[k2][qb][8 * hf + 4], s[k2][qb][8 * hf + 5]),
+                        pack2<BF16>(s[k2][qb][8 * hf + 6], s[k2][qb][8 * hf + 7])};
                 }
             }
             l_run[qb] += xhalf_sum(ls);
@@ -375,33 +369,39 @@ void fa_fwd_kernel(Params p) {
         // O^T += V^T P^T.
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const int R = db * 32 + l32;
+            const unsigned char* vrow = vb + v_lane + (((4 * db) ^ vu) << 4);
 #pragma unroll
-            for (int kb2 = 0; kb2 < KB; ++kb2) {
+            for (int k2 = 0; k2 < KB; ++k2) {
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
-                    const int ch0 = kb2 * 8 + 4 * hf + h;
-                    const u32x2 x0 = *(const u32x2*)(vb + vt_off<BN>(R, ch0));
-                    const u32x2 x1 = *(const u32x2*)(vb + vt_off<BN>(R, ch0 + 2));
+                    const unsigned char* pr = vrow + (k2 * 32 + 16 * hf) * ROWB;
+                    const u32x2 x0 = lds_read_tr16(pr);
+                    const u32x2 x1 = lds_read_tr16(pr + 8 * ROWB);
                     const u32x4 a = {x0[0], x0[1], x1[0], x1[1]};
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) acc[db][qb] = mfma32<BF16>(a, pk[kb2][qb][hf], acc[db][qb]);
+                    for (int qb = 0; qb < QB; ++qb)
+                        acc[db][qb] = mfma32<BF16>(a, pk[k2][qb][hf], acc[db][qb]);
                 }
             }
         }
     };
 
+    // Prologue, then the K loop in two parts: tiles without any mask, then the diagonal /
+    // key-tail tiles that need one.
     fetch(0);
     stash(0);
     __syncthreads();
-    for (int j = 0; j < Tc; ++j) {
-        const int buf = j & 1;
+    int j = 0;
+    for (; j < n_free; ++j) {
         if (j + 1 < Tc) fetch(j + 1);
-        if (j < wave_tc) {
-            if (j >= wave_ms) compute(j, buf, std::true_type{});
-            else compute(j, buf, std::false_type{});
-        }
-        if (j + 1 < Tc) stash(buf ^ 1);
+        compute(j, j & 1, std::false_type{});
+        if (j + 1 < Tc) stash((j + 1) & 1);
+        __syncthreads();
+    }
+    for (; j < Tc; ++j) {
+        if (j + 1 < Tc) fetch(j + 1);
+        if (j < wave_tc) compute(j, j & 1, std::true_type{});
+        if (j + 1 < Tc) stash((j + 1) & 1);
         __syncthreads();
     }
 
