@@ -1,0 +1,170 @@
+#!/usr/bin/env python3
+"""Summaries of rocprofv3 results (its SQLite ``*_results.db`` files) for ``profiles/``.
+
+  python rocprof_summary.py trace DB --command CMD
+      kernel-trace summary: calls, mean / median / min / max duration per kernel.
+  python rocprof_summary.py pmc DB --command CMD
+      per-kernel mean of each collected counter, plus MFMA utilisation, LDS bank-conflict
+      rate and VALU instruction mix when their counters are present.
+  python rocprof_summary.py traffic --fetch DB --write DB --copy-fetch DB --copy-write DB
+                           --workload NAME --command CMD [--out JSON]
+      HBM bytes per launch of the attention kernel: FETCH_SIZE and WRITE_SIZE (KiB per
+      dispatch), each scaled by what the same counter reads for a plain copy of known
+      size (bench.py --calibrate-copy).  Writes the JSON bench.py reads, stamped with the
+      hash of the kernel sources, so bench.py reports null once the kernel has changed.
+
+Summaries are printed as text; redirect them into profiles/.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sqlite3
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_KEY = "fa_fwd_kernel"
+SIMDS = 256 * 4
+XCCS = 8
+
+
+def _rows(db, sql):
+    con = sqlite3.connect(db)
+    try:
+        return list(con.execute(sql))
+    finally:
+        con.close()
+
+
+def short(name, n=96):
+    return name if len(name) <= n else name[:n - 3] + "..."
+
+
+def trace(db, command):
+    rows = _rows(db, "select name, duration from kernels")
+    by = {}
+    for name, dur in rows:
+        by.setdefault(name, []).append(dur / 1e3)  # ns -> us
+    out = [f"# rocprofv3 kernel trace summary", f"# command: {command}",
+           f"# source: {os.path.basename(db)}", "",
+           f"{'kernel':<98} {'calls':>5} {'mean_us':>9} {'median_us':>9} {'min_us':>9} {'max_us':>9}"]
+    for name, d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"{short(name):<98} {len(d):>5} {statistics.mean(d):>9.1f} "
+                   f"{statistics.median(d):>9.1f} {min(d):>9.1f} {max(d):>9.1f}")
+    return "\n".join(out)
+
+
+def pmc_means(db):
+    rows = _rows(db, "select name, dispatch_id, counter_name, counter_value from pmc_events")
+    per = {}
+    for name, disp, cname, val in rows:
+        d = per.setdefault(name, {}).setdefault(cname, {})
+        d[disp] = d.get(disp, 0.0) + val   # sum the counter's instances within a dispatch
+    return {k: {c: statistics.mean(v.values()) for c, v in cs.items()} for k, cs in per.items()}
+
+
+def pmc(db, command):
+    means = pmc_means(db)
+    out = [f"# rocprofv3 counter summary (mean per dispatch)", f"# command: {command}",
+           f"# source: {os.path.basename(db)}", ""]
+    for name, cs in means.items():
+        out.append(f"kernel: {short(name, 140)}")
+        for c in sorted(cs):
+            out.append(f"  {c:<32} {cs[c]:>18.1f}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in cs and "GRBM_GUI_ACTIVE" in cs:
+            gui = cs["GRBM_GUI_ACTIVE"] / XCCS
+            out.append(f"  {'derived MFMA busy %':<32} {100 * cs['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * SIMDS):>18.1f}"
+                       f"   (MFMA busy cycles / (GUI-active cycles per XCC x {SIMDS} SIMDs))")
+        if "SQ_LDS_BANK_CONFLICT" in cs and "SQ_LDS_IDX_ACTIVE" in cs:
+            act = cs["SQ_LDS_IDX_ACTIVE"]
+            conf = cs["SQ_LDS_BANK_CONFLICT"]
+            out.append(f"  {'derived LDS conflict cycles %':<32} {100 * conf / act if act else 0:>18.2f}"
+                       f"   (bank-conflict stall cycles / LDS indexed-active cycles)")
+        if "SQ_INSTS_VALU" in cs and "SQ_INSTS_MFMA" in cs:
+            out.append(f"  {'derived VALU / MFMA insts':<32} {cs['SQ_INSTS_VALU'] / max(1, cs['SQ_INSTS_MFMA']):>18.2f}")
+        out.append("")
+    return "\n".join(out)
+
+
+def _counter(db, cname, key):
+    for name, cs in pmc_means(db).items():
+        if key in name and cname in cs:
+            return cs[cname]
+    raise SystemExit(f"{cname} for a kernel matching '{key}' not found in {db}")
+
+
+def traffic(a):
+    sys.path.insert(0, ROOT)
+    import bench
+    from attention_fa_fwd_amd.inputs import WORKLOADS
+
+    fetch_kib = _counter(a.fetch, "FETCH_SIZE", KERNEL_KEY)
+    write_kib = _counter(a.write, "WRITE_SIZE", KERNEL_KEY)
+    cf_kib = _counter(a.copy_fetch, "FETCH_SIZE", "copyBuffer")
+    cw_kib = _counter(a.copy_write, "WRITE_SIZE", "copyBuffer")
+    f_fetch = bench.COPY_BYTES / (cf_kib * 1024.0)
+    f_write = bench.COPY_BYTES / (cw_kib * 1024.0)
+    hbm = fetch_kib * 1024.0 * f_fetch + write_kib * 1024.0 * f_write
+    w = WORKLOADS[a.workload]
+    algo = (2 * w["B"] * w["Hq"] * w["Sq"] * w["D"] * 2 + 2 * w["B"] * w["Hkv"] * w["Skv"] * w["D"] * 2
+            + w["B"] * w["Hq"] * w["Sq"] * 4)
+    path = a.out or bench.TRAFFIC_FILE
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    sha = bench.kernel_source_hash()
+    if data.get("kernel_source_sha") != sha:
+        data = {"kernel_source_sha": sha, "workloads": {}}
+    data["workloads"][a.workload] = {
+        "hbm_bytes_per_launch": round(hbm),
+        "fetch_kib_raw": fetch_kib, "write_kib_raw": write_kib,
+        "copy_fetch_kib_raw": cf_kib, "copy_write_kib_raw": cw_kib,
+        "fetch_scale": f_fetch, "write_scale": f_write,
+        "algorithmic_bytes": algo, "command": a.command,
+    }
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return "\n".join([
+        "# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a copy calibration",
+        f"# command: {a.command}",
+        f"# kernel sources sha256[:16]: {sha}", "",
+        f"workload                     {a.workload}",
+        f"FETCH_SIZE (KiB/dispatch)    {fetch_kib:.1f}   x scale {f_fetch:.4f}",
+        f"WRITE_SIZE (KiB/dispatch)    {write_kib:.1f}   x scale {f_write:.4f}",
+        f"copy of {bench.COPY_BYTES} B: FETCH_SIZE {cf_kib:.1f} KiB, WRITE_SIZE {cw_kib:.1f} KiB",
+        f"HBM bytes per launch         {hbm:.0f}  ({hbm / 2**20:.1f} MiB)",
+        f"algorithmic bytes            {algo}  ({algo / 2**20:.1f} MiB: q, k, v read once; o, lse written once)",
+        f"ratio                        {hbm / algo:.2f}",
+    ])
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    for n in ("trace", "pmc"):
+        s = sub.add_parser(n)
+        s.add_argument("db")
+        s.add_argument("--command", default="")
+    t = sub.add_parser("traffic")
+    for k in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--workload"):
+        t.add_argument(k, required=True)
+    t.add_argument("--command", default="")
+    t.add_argument("--out", default=None)
+    a = ap.parse_args(argv)
+    if a.cmd == "trace":
+        print(trace(a.db, a.command))
+    elif a.cmd == "pmc":
+        print(pmc(a.db, a.command))
+    else:
+        print(traffic(a))
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())
