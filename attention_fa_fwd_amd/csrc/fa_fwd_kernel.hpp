@@ -25,7 +25,8 @@
 //    4j + i/4, j = 0..3.  The d-order of the fragments is chosen so that each lane ends
 //    with 16 consecutive d of its query (two 128-bit stores per 32-wide block).
 //  * K and V tiles are double-buffered in LDS through registers: tile j+1 is fetched from
-//    HBM with 128-bit loads while tile j is computed.  16-byte chunks are XOR-swizzled per
+//    HBM with 128-bit buffer loads while tile j is computed; the buffer range ends at key
+//    Skv, so a ragged key tail reads as zero without per-lane address clamping.  16-byte chunks are XOR-swizzled per
 //    row so that tile writes, K operand reads and V transpose reads are bank-conflict free.
 //  * Register use is held to 256 per lane so that two waves share each SIMD: one wave's
 //    softmax and memory latency overlap the other's MFMAs.
@@ -140,6 +141,38 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* p) {
     return __builtin_bit_cast(u32x2, r);
 }
 
+// Balanced reductions of N floats held in registers: a max tree of v_max3 and a pairwise
+// sum tree, so the dependency depth is log(N) rather than N.  `a` is overwritten.
+template <int N>
+struct Tree {
+    __device__ __forceinline__ static float max(float* a) {
+        constexpr int M = (N + 2) / 3;
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            if (3 * i + 2 < N) a[i] = fmaxf(fmaxf(a[3 * i], a[3 * i + 1]), a[3 * i + 2]);
+            else if (3 * i + 1 < N) a[i] = fmaxf(a[3 * i], a[3 * i + 1]);
+            else a[i] = a[3 * i];
+        }
+        return Tree<M>::max(a);
+    }
+    __device__ __forceinline__ static float sum(float* a) {
+        constexpr int M = (N + 1) / 2;
+#pragma unroll
+        for (int i = 0; i < M; ++i) a[i] = (2 * i + 1 < N) ? a[2 * i] + a[2 * i + 1] : a[2 * i];
+        return Tree<M>::sum(a);
+    }
+};
+template <>
+struct Tree<1> {
+    __device__ __forceinline__ static float max(float* a) { return a[0]; }
+    __device__ __forceinline__ static float sum(float* a) { return a[0]; }
+};
+
+// Buffer resource for a raw byte range (gfx9-family descriptor: stride 0, 32-bit records).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
+}
+
 // --- LDS tile layout: [BN][D] row-major, 16-byte chunks XOR-swizzled per row ------------
 // K rows (read 32 rows x one chunk per MFMA operand): chunk ^ (row mod 16) for D=128;
 // for D=64 (8 chunks) the swizzle also folds row bit 3 so 16 consecutive rows differ.
@@ -179,7 +212,7 @@ void fa_fwd_kernel(Params p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
     const int l32 = lane & 31;
     const int h = lane >> 5;
 
@@ -252,17 +285,19 @@ void fa_fwd_kernel(Params p) {
     }
 
     // Tile staging: thread t moves chunks cid = t + i*NT (row cid / CPR, chunk cid % CPR)
-    // of both the K and the V tile.  Keys past Skv read row Skv-1 (masked later).
+    // of both the K and the V tile, through buffer loads whose range ends at key Skv:
+    // rows past Skv read as zero (and are masked later).
     u32x4 kreg[LD], vreg[LD];
     auto fetch = [&](int j) {
         const int j0 = j * BN;
+        const int nbytes = min(p.Skv - j0, BN) * ROWB;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + (size_t)j0 * D, nbytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + (size_t)j0 * D, nbytes);
 #pragma unroll
         for (int i = 0; i < LD; ++i) {
-            const int cid = tid + i * NT;
-            const int key = min(j0 + cid / CPR, p.Skv - 1);
-            const size_t off = (size_t)key * D + (cid % CPR) * 8;
-            kreg[i] = *(const u32x4*)(kp + off);
-            vreg[i] = *(const u32x4*)(vp + off);
+            const int off = (tid + i * NT) * 16;   // = row * ROWB + chunk * 16
+            kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+            vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
         }
     };
     auto stash = [&](int buf) {
@@ -280,14 +315,19 @@ void fa_fwd_kernel(Params p) {
     // Per-lane LDS offsets.  K operand: row kb*32 + l32, chunk (2dk + h) ^ k_swz(row); the
     // swizzle depends only on l32, so chunk = (2dk) ^ ku with ku = h ^ k_swz(l32).
     const int ku = h ^ k_swz<D>(l32);
-    const int k_lane = l32 * ROWB;
+    int koff[DK];
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) koff[dk] = l32 * ROWB + (((2 * dk) ^ ku) << 4);
     // V^T operand (two transpose reads per MFMA): this lane addresses key
     // 4*h + jj (+ kb*32 + 16*hf + 8*r) and the 8-byte piece of d = db*32 + 16*(qq&1) +
     // 8*(g&1) + 4*(qq>>1), with jj, qq from the lane's index in its 16-lane group g.
     const int vs = lane & 15, vj = vs >> 2, vq = vs & 3, vg = lane >> 4;
     const int v_lane_row = 4 * (vg >> 1) + vj;
     const int vu = (2 * (vq & 1) + (vg & 1)) ^ (v_swz_of(vj) & (CPR - 1));   // chunk ^ 4*db
-    const int v_lane = v_lane_row * ROWB + (vq >> 1) * 8;
+    int voff[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+        voff[db] = v_lane_row * ROWB + (vq >> 1) * 8 + (((4 * db) ^ vu) << 4);
 
     auto compute = [&](int j, int buf, auto masked_tag) {
         constexpr bool MASKED = decltype(masked_tag)::value;
@@ -302,8 +342,7 @@ void fa_fwd_kernel(Params p) {
             for (int qb = 0; qb < QB; ++qb) s[k2][qb] = (f32x16){};
 #pragma unroll
             for (int dk = 0; dk < DK; ++dk) {
-                const u32x4 a = *(const u32x4*)(kb + k2 * 32 * ROWB + k_lane +
-                                                (((2 * dk) ^ ku) << 4));
+                const u32x4 a = *(const u32x4*)(kb + k2 * 32 * ROWB + koff[dk]);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) s[k2][qb] = mfma32<BF16>(a, qf[qb][dk], s[k2][qb]);
             }
@@ -330,12 +369,12 @@ void fa_fwd_kernel(Params p) {
         u32x4 pk[KB][QB][2];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            float mx = -__builtin_inff();
+            float t[KB * 16];
 #pragma unroll
             for (int k2 = 0; k2 < KB; ++k2)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[k2][qb][i]);
-            mx = xhalf_max(mx);
+                for (int i = 0; i < 16; ++i) t[k2 * 16 + i] = s[k2][qb][i];
+            const float mx = xhalf_max(Tree<KB * 16>::max(t));
             const float m_new = fmaxf(m_run[qb], mx * p.c);
             if (__builtin_amdgcn_ballot_w64(m_new > m_run[qb] + TAU) != 0) {
                 const float alpha = fast_exp2(m_run[qb] - m_new);
@@ -345,14 +384,13 @@ void fa_fwd_kernel(Params p) {
                 for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
             }
             const float neg_m = -m_run[qb];
-            float ls = 0.0f;
 #pragma unroll
             for (int k2 = 0; k2 < KB; ++k2) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float pv = fast_exp2(__builtin_fmaf(s[k2][qb][i], p.c, neg_m));
                     s[k2][qb][i] = pv;
-                    ls += pv;
+                    t[k2 * 16 + i] = pv;
                 }
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
@@ -363,13 +401,13 @@ void fa_fwd_kernel(Params p) {
                         pack2<BF16>(s[k2][qb][8 * hf + 6], s[k2][qb][8 * hf + 7])};
                 }
             }
-            l_run[qb] += xhalf_sum(ls);
+            l_run[qb] += xhalf_sum(Tree<KB * 16>::sum(t));
         }
 
         // O^T += V^T P^T.
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const unsigned char* vrow = vb + v_lane + (((4 * db) ^ vu) << 4);
+            const unsigned char* vrow = vb + voff[db];
 #pragma unroll
             for (int k2 = 0; k2 < KB; ++k2) {
 #pragma unroll
