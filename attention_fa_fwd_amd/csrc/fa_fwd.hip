@@ -52,8 +52,7 @@ hipError_t launch_cfg(const Params& p, hipStream_t s) {
     FA_ENTRY(D, 64, 1, 2, 2, CAUSAL, BF16, CNAME, TNAME),          \
     FA_ENTRY(D, 64, 1, 4, 2, CAUSAL, BF16, CNAME, TNAME),          \
     FA_ENTRY(D, 64, 1, 4, 1, CAUSAL, BF16, CNAME, TNAME),          \
-    FA_ENTRY(D, 64, 1, 8, 1, CAUSAL, BF16, CNAME, TNAME),          \
-    FA_ENTRY(D, 64, 2, 4, 1, CAUSAL, BF16, CNAME, TNAME)
+    FA_ENTRY(D, 64, 1, 8, 1, CAUSAL, BF16, CNAME, TNAME)
 
 const ConfigEntry kConfigs[] = {
     FA_TILES(128, 1, 1, "causal", "bf16"), FA_TILES(128, 0, 1, "full", "bf16"),

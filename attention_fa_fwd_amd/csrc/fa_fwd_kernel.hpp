@@ -24,9 +24,12 @@
 //    of 16 lanes, lane i receives element (i mod 4) of the 8-byte rows addressed by lanes
 //    4j + i/4, j = 0..3.  The d-order of the fragments is chosen so that each lane ends
 //    with 16 consecutive d of its query (two 128-bit stores per 32-wide block).
-//  * K and V tiles are double-buffered in LDS through registers: tile j+1 is fetched from
-//    HBM with 128-bit buffer loads while tile j is computed; the buffer range ends at key
-//    Skv, so a ragged key tail reads as zero without per-lane address clamping.  16-byte chunks are XOR-swizzled per
+//  * K and V tiles are double-buffered in LDS and move there straight from HBM with
+//    gfx950's 128-bit buffer loads to LDS: no staging registers, no LDS write instructions.
+//    The buffer range ends at key Skv, so a ragged key tail lands as zeros.  The K loop is
+//    software-pipelined: step j issues the MFMAs of S(j+1) in the same block as the
+//    softmax and P V of tile j, so matrix work overlaps the exp2 work; K is loaded two
+//    tiles ahead and V one tile ahead in the same two-buffer LDS footprint.  16-byte chunks are XOR-swizzled per
 //    row so that tile writes, K operand reads and V transpose reads are bank-conflict free.
 //  * Register use is held to 256 per lane so that two waves share each SIMD: one wave's
 //    softmax and memory latency overlap the other's MFMAs.
@@ -90,7 +93,6 @@ struct Cfg {
     static constexpr int NW = WPH * HPW;
     static constexpr int NT = 64 * NW;
     static constexpr int BMP = 32 * QB * WPH;   // query positions per workgroup
-    static constexpr int LDS_BYTES = 2 * 2 * BN * D * 2;   // 2 buffers x (K + V)
     static constexpr int WAVES_PER_SIMD = QB == 1 ? 2 : 1;  // register budget 256 / 512
     static_assert(D == 64 || D == 128, "head dim");
     static_assert(BN == 64 || BN == 128, "key tile");
@@ -201,14 +203,12 @@ void fa_fwd_kernel(Params p) {
     constexpr int DB = D / 32;           // 32-wide d blocks of O
     constexpr int ROWB = D * 2;          // bytes per K/V row
     constexpr int TILE = BN * ROWB;      // bytes per K (or V) tile
-    constexpr int BUF = 2 * TILE;        // K tile + V tile
     constexpr int CPR = D / 8;           // 16-byte chunks per row
     constexpr int LD = BN * CPR / NT;    // 16-byte chunks of each tile per thread
     constexpr float TAU = 8.0f;          // lazy-rescale threshold (log2 domain)
     constexpr float LN2 = 0.69314718055994530942f;
     static_assert(BN * CPR % NT == 0, "tile chunks per thread");
-
-    __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS_BYTES];
+    static_assert(TILE % (NT * 16) == 0, "each load fills whole 1 KiB wave slots");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -284,32 +284,34 @@ void fa_fwd_kernel(Params p) {
         for (int db = 0; db < DB; ++db) acc[db][qb] = (f32x16){};
     }
 
-    // Tile staging: thread t moves chunks cid = t + i*NT (row cid / CPR, chunk cid % CPR)
-    // of both the K and the V tile, through buffer loads whose range ends at key Skv:
-    // rows past Skv read as zero (and are masked later).
-    u32x4 kreg[LD], vreg[LD];
-    auto fetch = [&](int j) {
-        const int j0 = j * BN;
-        const int nbytes = min(p.Skv - j0, BN) * ROWB;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + (size_t)j0 * D, nbytes);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp + (size_t)j0 * D, nbytes);
+    // LDS: K(j) lives in k_lds[j%2] and V(j) in v_lds[j%2].  Four separate arrays, so the
+    // compiler can tell a direct-to-LDS load into one from reads of another and does not
+    // wait for the load before those reads; the barrier that ends each step drains it.
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILE], k_lds1[TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TILE], v_lds1[TILE];
+    auto kl = [&](auto par) -> unsigned char* { return decltype(par)::value ? k_lds1 : k_lds0; };
+    auto vl = [&](auto par) -> unsigned char* { return decltype(par)::value ? v_lds1 : v_lds0; };
+
+    // Tiles move from HBM straight into LDS (buffer_load_dwordx4 ... lds): in load i, wave
+    // w fills the 1 KiB of LDS at chunk slots (i*NW + w)*64 + lane, so each lane fetches
+    // the chunk that the row swizzle places in its slot.  The buffer range ends at key Skv:
+    // rows past Skv, and whole tiles past the end, are out of range and land as zeros.
+    int ksrc[LD], vsrc[LD];
 #pragma unroll
-        for (int i = 0; i < LD; ++i) {
-            const int off = (tid + i * NT) * 16;   // = row * ROWB + chunk * 16
-            kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-            vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
-        }
-    };
-    auto stash = [&](int buf) {
-        unsigned char* kb = smem + buf * BUF;
-        unsigned char* vb = kb + TILE;
+    for (int i = 0; i < LD; ++i) {
+        const int slot = (i * C::NW + w) * 64 + lane;
+        const int row = slot / CPR, pc = slot % CPR;
+        ksrc[i] = row * ROWB + ((pc ^ k_swz<D>(row)) << 4);
+        vsrc[i] = row * ROWB + ((pc ^ v_swz<D>(row)) << 4);
+    }
+    auto fetch = [&](const T* base, int j, unsigned char* dst, const int (&src)[LD]) {
+        const int j0 = min(j * BN, p.Skv);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (size_t)j0 * D, min(p.Skv - j0, BN) * ROWB);
 #pragma unroll
-        for (int i = 0; i < LD; ++i) {
-            const int cid = tid + i * NT;
-            const int row = cid / CPR, c = cid % CPR;
-            *(u32x4*)(kb + row * ROWB + ((c ^ k_swz<D>(row)) << 4)) = kreg[i];
-            *(u32x4*)(vb + row * ROWB + ((c ^ v_swz<D>(row)) << 4)) = vreg[i];
-        }
+        for (int i = 0; i < LD; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (__attribute__((address_space(3))) void*)(dst + (i * C::NW + w) * 1024), 16,
+                src[i], 0, 0, 0);
     };
 
     // Per-lane LDS offsets.  K operand: row kb*32 + l32, chunk (2dk + h) ^ k_swz(row); the
@@ -329,13 +331,8 @@ void fa_fwd_kernel(Params p) {
     for (int db = 0; db < DB; ++db)
         voff[db] = v_lane_row * ROWB + (vq >> 1) * 8 + (((4 * db) ^ vu) << 4);
 
-    auto compute = [&](int j, int buf, auto masked_tag) {
-        constexpr bool MASKED = decltype(masked_tag)::value;
-        const unsigned char* kb = smem + buf * BUF;
-        const unsigned char* vb = kb + TILE;
-
-        // S^T = K Q^T for this tile.
-        f32x16 s[KB][QB];
+    // S^T = K Q^T of the tile in K buffer `kb`.
+    auto qk = [&](const unsigned char* kb, f32x16 (&s)[KB][QB]) {
 #pragma unroll
         for (int k2 = 0; k2 < KB; ++k2) {
 #pragma unroll
@@ -347,101 +344,132 @@ void fa_fwd_kernel(Params p) {
                 for (int qb = 0; qb < QB; ++qb) s[k2][qb] = mfma32<BF16>(a, qf[qb][dk], s[k2][qb]);
             }
         }
+    };
 
-        if constexpr (MASKED) {
-            const int j0 = j * BN;
+    // One K-loop step for tile j.  On entry s_cur holds S(j); the step issues S(j+1) into
+    // s_nxt in the same straight-line block as the softmax and P V of tile j, so the MFMAs
+    // of the next scores overlap the exp2 work of this tile.  Loads run two tiles ahead
+    // for K and one for V: the step reads k_lds[(j+1)%2] and v_lds[j%2] and loads K(j+2)
+    // into k_lds[j%2] and V(j+1) into v_lds[(j+1)%2], which nobody reads during step j.
+    auto step = [&](int j, auto par_tag, auto masked_tag, f32x16 (&s_cur)[KB][QB],
+                    f32x16 (&s_nxt)[KB][QB]) {
+        constexpr int PAR = decltype(par_tag)::value;      // j % 2
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        fetch(kp, j + 2, kl(par_tag), ksrc);
+        fetch(vp, j + 1, vl(std::integral_constant<int, PAR ^ 1>{}), vsrc);
+        if (!MASKED || j < wave_tc) {
+            if constexpr (MASKED) {
+                const int j0 = j * BN;
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    const int qpos = p.input_pos + qw0 + qb * 32 + l32;
+                    const int lim = CAUSAL ? min(qpos, p.Skv - 1) : p.Skv - 1;   // last visible key
+#pragma unroll
+                    for (int k2 = 0; k2 < KB; ++k2)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int key = j0 + k2 * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+                            if (key > lim) s_cur[k2][qb][i] = -__builtin_inff();
+                        }
+                }
+            }
+            // Row max of S(j); lazy rescale of the state (rare: the only branch).
+            float m_new[QB];
+            bool grow = false;
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                const int qpos = p.input_pos + qw0 + qb * 32 + l32;
-                const int lim = CAUSAL ? min(qpos, p.Skv - 1) : p.Skv - 1;   // last visible key
+                float t[KB * 16];
+#pragma unroll
+                for (int k2 = 0; k2 < KB; ++k2)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) t[k2 * 16 + i] = s_cur[k2][qb][i];
+                m_new[qb] = fmaxf(m_run[qb], xhalf_max(Tree<KB * 16>::max(t)) * p.c);
+                grow |= m_new[qb] > m_run[qb] + TAU;
+            }
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    const float alpha = fast_exp2(m_run[qb] - m_new[qb]);
+                    m_run[qb] = m_new[qb];
+                    l_run[qb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
+                }
+            }
+            // S(j+1) = K(j+1) Q^T: MFMA work independent of the softmax below.
+            qk(kl(std::integral_constant<int, PAR ^ 1>{}), s_nxt);
+            // P = exp2(c s - m) packed to the storage type, its row sum, and O^T += V^T P^T.
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const float neg_m = -m_run[qb];
+                float t[KB * 16];
+                u32x4 pk[KB][2];
 #pragma unroll
                 for (int k2 = 0; k2 < KB; ++k2) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = j0 + k2 * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-                        if (key > lim) s[k2][qb][i] = -__builtin_inff();
+                    for (int i = 0; i < 16; ++i)
+                        t[k2 * 16 + i] = fast_exp2(__builtin_fmaf(s_cur[k2][qb][i], p.c, neg_m));
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const float* e = t + k2 * 16 + 8 * hf;
+                        pk[k2][hf] = (u32x4){pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]),
+                                             pack2<BF16>(e[4], e[5]), pack2<BF16>(e[6], e[7])};
                     }
                 }
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+#pragma unroll
+                    for (int k2 = 0; k2 < KB; ++k2) {
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf) {
+                            const unsigned char* pr =
+                                vl(par_tag) + voff[db] + (k2 * 32 + 16 * hf) * ROWB;
+                            const u32x2 x0 = lds_read_tr16(pr);
+                            const u32x2 x1 = lds_read_tr16(pr + 8 * ROWB);
+                            const u32x4 a = {x0[0], x0[1], x1[0], x1[1]};
+                            acc[db][qb] = mfma32<BF16>(a, pk[k2][hf], acc[db][qb]);
+                        }
+                    }
+                }
+                l_run[qb] += xhalf_sum(Tree<KB * 16>::sum(t));
             }
         }
-
-        // Online softmax update per query block.
-        u32x4 pk[KB][QB][2];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            float t[KB * 16];
-#pragma unroll
-            for (int k2 = 0; k2 < KB; ++k2)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) t[k2 * 16 + i] = s[k2][qb][i];
-            const float mx = xhalf_max(Tree<KB * 16>::max(t));
-            const float m_new = fmaxf(m_run[qb], mx * p.c);
-            if (__builtin_amdgcn_ballot_w64(m_new > m_run[qb] + TAU) != 0) {
-                const float alpha = fast_exp2(m_run[qb] - m_new);
-                m_run[qb] = m_new;
-                l_run[qb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
-            }
-            const float neg_m = -m_run[qb];
-#pragma unroll
-            for (int k2 = 0; k2 < KB; ++k2) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float pv = fast_exp2(__builtin_fmaf(s[k2][qb][i], p.c, neg_m));
-                    s[k2][qb][i] = pv;
-                    t[k2 * 16 + i] = pv;
-                }
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    pk[k2][qb][hf] = (u32x4){
-                        pack2<BF16>(s[k2][qb][8 * hf + 0], s[k2][qb][8 * hf + 1]),
-                        pack2<BF16>(s[k2][qb][8 * hf + 2], s[k2][qb][8 * hf + 3]),
-                        pack2<BF16>(s[k2][qb][8 * hf + 4], s[k2][qb][8 * hf + 5]),
-                        pack2<BF16>(s[k2][qb][8 * hf + 6], s[k2][qb][8 * hf + 7])};
-                }
-            }
-            l_run[qb] += xhalf_sum(Tree<KB * 16>::sum(t));
-        }
-
-        // O^T += V^T P^T.
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const unsigned char* vrow = vb + voff[db];
-#pragma unroll
-            for (int k2 = 0; k2 < KB; ++k2) {
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const unsigned char* pr = vrow + (k2 * 32 + 16 * hf) * ROWB;
-                    const u32x2 x0 = lds_read_tr16(pr);
-                    const u32x2 x1 = lds_read_tr16(pr + 8 * ROWB);
-                    const u32x4 a = {x0[0], x0[1], x1[0], x1[1]};
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-                        acc[db][qb] = mfma32<BF16>(a, pk[k2][qb][hf], acc[db][qb]);
-                }
-            }
-        }
+        __syncthreads();
     };
 
-    // Prologue, then the K loop in two parts: tiles without any mask, then the diagonal /
-    // key-tail tiles that need one.
-    fetch(0);
-    stash(0);
+    // Prologue: K(0), V(0) to LDS; S(0) while K(1) arrives.
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    f32x16 s0[KB][QB], s1[KB][QB];
+    fetch(kp, 0, k_lds0, ksrc);
+    fetch(vp, 0, v_lds0, vsrc);
     __syncthreads();
+    fetch(kp, 1, k_lds1, ksrc);
+    qk(k_lds0, s0);
+    __syncthreads();
+
+    // The K loop in two parts (K-loop split): tiles needing no mask, then the diagonal /
+    // key-tail tiles.  Unrolled by two so buffer parity and the roles of s0 / s1 are fixed.
+    using F = std::false_type;
+    using TT = std::true_type;
     int j = 0;
-    for (; j < n_free; ++j) {
-        if (j + 1 < Tc) fetch(j + 1);
-        compute(j, j & 1, std::false_type{});
-        if (j + 1 < Tc) stash((j + 1) & 1);
-        __syncthreads();
+    for (; j + 1 < n_free; j += 2) {
+        step(j, P0{}, F{}, s0, s1);
+        step(j + 1, P1{}, F{}, s1, s0);
     }
-    for (; j < Tc; ++j) {
-        if (j + 1 < Tc) fetch(j + 1);
-        if (j < wave_tc) compute(j, j & 1, std::true_type{});
-        if (j + 1 < Tc) stash((j + 1) & 1);
-        __syncthreads();
+    if (j < n_free) {
+        step(j, P0{}, F{}, s0, s1);
+        ++j;
+        if (j < Tc) {
+            step(j, P1{}, TT{}, s1, s0);
+            ++j;
+        }
     }
+    for (; j + 1 < Tc; j += 2) {
+        step(j, P0{}, TT{}, s0, s1);
+        step(j + 1, P1{}, TT{}, s1, s0);
+    }
+    if (j < Tc) step(j, P0{}, TT{}, s0, s1);
 
     // Epilogue: O = acc / l (v_rcp_f32), rounded to the storage type; LSE = ln2 (m + log2 l).
     T* op = (T*)p.o + (size_t)(b * p.Hq + hq) * p.Sq * D;
