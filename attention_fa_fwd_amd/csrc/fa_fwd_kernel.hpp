@@ -175,6 +175,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane i writes lds + 16*i.  A device
+// function of its own, so the host compilation pass never sees the builtin.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                             voff, 0, 0, 0);
+}
+
 // --- LDS tile layout: [BN][D] row-major, 16-byte chunks XOR-swizzled per row ------------
 // K rows (read 32 rows x one chunk per MFMA operand): chunk ^ (row mod 16) for D=128;
 // for D=64 (8 chunks) the swizzle also folds row bit 3 so 16 consecutive rows differ.
@@ -309,9 +316,7 @@ void fa_fwd_kernel(Params p) {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (size_t)j0 * D, min(p.Skv - j0, BN) * ROWB);
 #pragma unroll
         for (int i = 0; i < LD; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (__attribute__((address_space(3))) void*)(dst + (i * C::NW + w) * 1024), 16,
-                src[i], 0, 0, 0);
+            buffer_load_lds16(r, dst + (i * C::NW + w) * 1024, src[i]);
     };
 
     // Per-lane LDS offsets.  K operand: row kb*32 + l32, chunk (2dk + h) ^ k_swz(row); the
