@@ -404,22 +404,25 @@ void fa_fwd_kernel(Params p) {
             // S(j+1) = K(j+1) Q^T: MFMA work independent of the softmax below.
             qk(kl(std::integral_constant<int, PAR ^ 1>{}), s_nxt);
             // P = exp2(c s - m) packed to the storage type, its row sum, and O^T += V^T P^T.
+            // Each 16-key block is summed as soon as it is packed, so its fp32 values die early.
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 const float neg_m = -m_run[qb];
-                float t[KB * 16];
+                float psum[KB];
                 u32x4 pk[KB][2];
 #pragma unroll
                 for (int k2 = 0; k2 < KB; ++k2) {
+                    float t[16];
 #pragma unroll
                     for (int i = 0; i < 16; ++i)
-                        t[k2 * 16 + i] = fast_exp2(__builtin_fmaf(s_cur[k2][qb][i], p.c, neg_m));
+                        t[i] = fast_exp2(__builtin_fmaf(s_cur[k2][qb][i], p.c, neg_m));
 #pragma unroll
                     for (int hf = 0; hf < 2; ++hf) {
-                        const float* e = t + k2 * 16 + 8 * hf;
+                        const float* e = t + 8 * hf;
                         pk[k2][hf] = (u32x4){pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]),
                                              pack2<BF16>(e[4], e[5]), pack2<BF16>(e[6], e[7])};
                     }
+                    psum[k2] = Tree<16>::sum(t);
                 }
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
@@ -436,7 +439,7 @@ void fa_fwd_kernel(Params p) {
                         }
                     }
                 }
-                l_run[qb] += xhalf_sum(Tree<KB * 16>::sum(t));
+                l_run[qb] += xhalf_sum(Tree<KB>::sum(psum));
             }
         }
         __syncthreads();
