@@ -177,9 +177,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 // 16 bytes per lane from a buffer straight into LDS: lane i writes lds + 16*i.  A device
 // function of its own, so the host compilation pass never sees the builtin.
-__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff) {
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff,
+                                                  int soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                             voff, 0, 0, 0);
+                                             voff, soff, 0, 0);
 }
 
 // --- LDS tile layout: [BN][D] row-major, 16-byte chunks XOR-swizzled per row ------------
@@ -303,20 +304,28 @@ void fa_fwd_kernel(Params p) {
     // w fills the 1 KiB of LDS at chunk slots (i*NW + w)*64 + lane, so each lane fetches
     // the chunk that the row swizzle places in its slot.  The buffer range ends at key Skv:
     // rows past Skv, and whole tiles past the end, are out of range and land as zeros.
-    int ksrc[LD], vsrc[LD];
-#pragma unroll
-    for (int i = 0; i < LD; ++i) {
-        const int slot = (i * C::NW + w) * 64 + lane;
+    // The row of a slot advances by 64*NW/CPR rows per load i; that is a multiple of 16, so
+    // the swizzles (row mod 16) do not depend on i: one per-lane offset plus i * stride.
+    static_assert((64 * C::NW / CPR) % 16 == 0, "load stride keeps the swizzle");
+    constexpr int LOAD_STRIDE = 64 * C::NW * 16;   // bytes of tile per load i
+    int ksrc, vsrc;
+    {
+        const int slot = w * 64 + lane;
         const int row = slot / CPR, pc = slot % CPR;
-        ksrc[i] = row * ROWB + ((pc ^ k_swz<D>(row)) << 4);
-        vsrc[i] = row * ROWB + ((pc ^ v_swz<D>(row)) << 4);
+        ksrc = row * ROWB + ((pc ^ k_swz<D>(row)) << 4);
+        vsrc = row * ROWB + ((pc ^ v_swz<D>(row)) << 4);
     }
-    auto fetch = [&](const T* base, int j, unsigned char* dst, const int (&src)[LD]) {
+    // Load i reads through its own resource starting at byte i * LOAD_STRIDE of the tile,
+    // whose range ends at the tile's last valid key (scalar work only; the per-lane offset
+    // `src` is the same for every i, and every range check sees the whole offset).
+    auto fetch = [&](const T* base, int j, unsigned char* dst, int src) {
         const int j0 = min(j * BN, p.Skv);
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (size_t)j0 * D, min(p.Skv - j0, BN) * ROWB);
+        const int valid = min(p.Skv - j0, BN) * ROWB;
+        const unsigned char* tb = (const unsigned char*)(base + (size_t)j0 * D);
 #pragma unroll
         for (int i = 0; i < LD; ++i)
-            buffer_load_lds16(r, dst + (i * C::NW + w) * 1024, src[i]);
+            buffer_load_lds16(make_rsrc(tb + i * LOAD_STRIDE, max(0, valid - i * LOAD_STRIDE)),
+                              dst + (i * C::NW + w) * 1024, src, 0);
     };
 
     // Per-lane LDS offsets.  K operand: row kb*32 + l32, chunk (2dk + h) ^ k_swz(row); the
