@@ -33,10 +33,12 @@
 //    row so that tile writes, K operand reads and V transpose reads are bank-conflict free.
 //  * Register use is held to 256 per lane so that two waves share each SIMD: one wave's
 //    softmax and memory latency overlap the other's MFMAs.
-//  * The running max is rescaled lazily: m is only raised (and acc, l rescaled) when some
-//    row's max grows by more than 2^8 in the exp2 domain; otherwise the stale max is
-//    kept.  softmax is invariant to the shift, p stays <= 2^8, and the normalisation at
-//    the end uses the same m for acc and l, so the result is the same softmax.
+//  * The running max is kept lazily: p = exp2(c s - m) is computed with the current m and
+//    m is only raised (acc and l rescaled, p recomputed) when a lane's partial row sum of
+//    p exceeds 2^15 -- on the first tile and on a large jump of the max.  softmax is
+//    invariant to the shift, p stays <= 2^15 (exact range in bf16 / fp16), and the
+//    normalisation at the end uses the same m for acc and l, so the result is the same
+//    softmax; the common path computes no row max at all.
 //  * A workgroup is HPW heads x WPH position blocks.  HPW > 1 packs query heads of one
 //    GQA group into a workgroup: they share every K/V tile ("Grouped-query attention").
 //  * Workgroups are dispatched round-robin over the 8 XCDs.  The workgroup id is remapped
@@ -213,7 +215,7 @@ void fa_fwd_kernel(Params p) {
     constexpr int TILE = BN * ROWB;      // bytes per K (or V) tile
     constexpr int CPR = D / 8;           // 16-byte chunks per row
     constexpr int LD = BN * CPR / NT;    // 16-byte chunks of each tile per thread
-    constexpr float TAU = 8.0f;          // lazy-rescale threshold (log2 domain)
+    constexpr float P_LIMIT = 32768.0f;  // lazy max: largest partial row sum of p allowed
     constexpr float LN2 = 0.69314718055994530942f;
     static_assert(BN * CPR % NT == 0, "tile chunks per thread");
     static_assert(TILE % (NT * 16) == 0, "each load fills whole 1 KiB wave slots");
@@ -387,52 +389,66 @@ void fa_fwd_kernel(Params p) {
                         }
                 }
             }
-            // Row max of S(j); lazy rescale of the state (rare: the only branch).
-            float m_new[QB];
-            bool grow = false;
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                float t[KB * 16];
-#pragma unroll
-                for (int k2 = 0; k2 < KB; ++k2)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) t[k2 * 16 + i] = s_cur[k2][qb][i];
-                m_new[qb] = fmaxf(m_run[qb], xhalf_max(Tree<KB * 16>::max(t)) * p.c);
-                grow |= m_new[qb] > m_run[qb] + TAU;
-            }
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            // S(j+1) = K(j+1) Q^T: MFMA work independent of the softmax below.
+            qk(kl(std::integral_constant<int, PAR ^ 1>{}), s_nxt);
+
+            // P = exp2(c s - m) with the running max m, packed to the storage type, and the
+            // lane's partial row sums (each 16-key block summed as soon as it is packed).
+            u32x4 pk[KB][QB][2];
+            float ts[QB];
+            auto make_p = [&]() {
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
-                    const float alpha = fast_exp2(m_run[qb] - m_new[qb]);
-                    m_run[qb] = m_new[qb];
+                    const float neg_m = -m_run[qb];
+                    float psum[KB];
+#pragma unroll
+                    for (int k2 = 0; k2 < KB; ++k2) {
+                        float t[16];
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            t[i] = fast_exp2(__builtin_fmaf(s_cur[k2][qb][i], p.c, neg_m));
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf) {
+                            const float* e = t + 8 * hf;
+                            pk[k2][qb][hf] = (u32x4){pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]),
+                                                     pack2<BF16>(e[4], e[5]), pack2<BF16>(e[6], e[7])};
+                        }
+                        psum[k2] = Tree<16>::sum(t);
+                    }
+                    ts[qb] = Tree<KB>::sum(psum);
+                }
+            };
+            make_p();
+            // Lazy max.  Every p is at most its lane's partial sum, so while those sums stay
+            // <= 2^15 the running max m may lag the true row max: p fits the storage type and
+            // the softmax is unchanged, since acc and l share m.  Otherwise (the first tile,
+            // where m = -inf makes the sums inf or NaN, or a jump of the max) raise m to the
+            // row max, rescale acc and l, and recompute P.  No row max on the common path.
+            bool bad = false;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) bad |= !(ts[qb] <= P_LIMIT);
+            if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    float t[KB * 16];
+#pragma unroll
+                    for (int k2 = 0; k2 < KB; ++k2)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) t[k2 * 16 + i] = s_cur[k2][qb][i];
+                    const float m_new = fmaxf(m_run[qb], xhalf_max(Tree<KB * 16>::max(t)) * p.c);
+                    const float alpha = fast_exp2(m_run[qb] - m_new);
+                    m_run[qb] = m_new;
                     l_run[qb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
                 }
+                make_p();
             }
-            // S(j+1) = K(j+1) Q^T: MFMA work independent of the softmax below.
-            qk(kl(std::integral_constant<int, PAR ^ 1>{}), s_nxt);
-            // P = exp2(c s - m) packed to the storage type, its row sum, and O^T += V^T P^T.
-            // Each 16-key block is summed as soon as it is packed, so its fp32 values die early.
+
+            // O^T += V^T P^T.
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                const float neg_m = -m_run[qb];
-                float psum[KB];
-                u32x4 pk[KB][2];
-#pragma unroll
-                for (int k2 = 0; k2 < KB; ++k2) {
-                    float t[16];
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        t[i] = fast_exp2(__builtin_fmaf(s_cur[k2][qb][i], p.c, neg_m));
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const float* e = t + 8 * hf;
-                        pk[k2][hf] = (u32x4){pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]),
-                                             pack2<BF16>(e[4], e[5]), pack2<BF16>(e[6], e[7])};
-                    }
-                    psum[k2] = Tree<16>::sum(t);
-                }
+                l_run[qb] += xhalf_sum(ts[qb]);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -444,11 +460,10 @@ void fa_fwd_kernel(Params p) {
                             const u32x2 x0 = lds_read_tr16(pr);
                             const u32x2 x1 = lds_read_tr16(pr + 8 * ROWB);
                             const u32x4 a = {x0[0], x0[1], x1[0], x1[1]};
-                            acc[db][qb] = mfma32<BF16>(a, pk[k2][hf], acc[db][qb]);
+                            acc[db][qb] = mfma32<BF16>(a, pk[k2][qb][hf], acc[db][qb]);
                         }
                     }
                 }
-                l_run[qb] += xhalf_sum(Tree<KB>::sum(psum));
             }
         }
         __syncthreads();
