@@ -317,17 +317,15 @@ void fa_fwd_kernel(Params p) {
         ksrc = row * ROWB + ((pc ^ k_swz<D>(row)) << 4);
         vsrc = row * ROWB + ((pc ^ v_swz<D>(row)) << 4);
     }
-    // Load i reads through its own resource starting at byte i * LOAD_STRIDE of the tile,
-    // whose range ends at the tile's last valid key (scalar work only; the per-lane offset
-    // `src` is the same for every i, and every range check sees the whole offset).
+    // One buffer resource per tile, ending at the tile's last valid key; load i adds
+    // i * LOAD_STRIDE as the scalar offset (gfx950's range check covers voffset + soffset,
+    // so every load past the end of the range reads zero).
     auto fetch = [&](const T* base, int j, unsigned char* dst, int src) {
         const int j0 = min(j * BN, p.Skv);
-        const int valid = min(p.Skv - j0, BN) * ROWB;
-        const unsigned char* tb = (const unsigned char*)(base + (size_t)j0 * D);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (size_t)j0 * D, min(p.Skv - j0, BN) * ROWB);
 #pragma unroll
         for (int i = 0; i < LD; ++i)
-            buffer_load_lds16(make_rsrc(tb + i * LOAD_STRIDE, max(0, valid - i * LOAD_STRIDE)),
-                              dst + (i * C::NW + w) * 1024, src, 0);
+            buffer_load_lds16(r, dst + (i * C::NW + w) * 1024, src, i * LOAD_STRIDE);
     };
 
     // Per-lane LDS offsets.  K operand: row kb*32 + l32, chunk (2dk + h) ^ k_swz(row); the
@@ -393,7 +391,9 @@ void fa_fwd_kernel(Params p) {
             qk(kl(std::integral_constant<int, PAR ^ 1>{}), s_nxt);
 
             // P = exp2(c s - m) with the running max m, packed to the storage type, and the
-            // lane's partial row sums (each 16-key block summed as soon as it is packed).
+            // lane's partial row sums in fp32 (each 16-key block summed as soon as it is
+            // packed).  Summing the rounded bf16 p instead would move LSE by ~1e-3 on rows
+            // with few visible keys.
             u32x4 pk[KB][QB][2];
             float ts[QB];
             auto make_p = [&]() {
