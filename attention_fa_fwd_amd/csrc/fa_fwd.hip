@@ -54,11 +54,21 @@ hipError_t launch_cfg(const Params& p, hipStream_t s) {
     FA_ENTRY(D, 64, 1, 4, 1, CAUSAL, BF16, CNAME, TNAME),          \
     FA_ENTRY(D, 64, 1, 8, 1, CAUSAL, BF16, CNAME, TNAME)
 
+// 32-key tiles (head dim 128 only: a 32 x 64 tile is too small to split over 512 threads).
+#define FA_TILES_BN32(CAUSAL, BF16, CNAME, TNAME)                  \
+    FA_ENTRY(128, 32, 1, 1, 4, CAUSAL, BF16, CNAME, TNAME),        \
+    FA_ENTRY(128, 32, 1, 2, 4, CAUSAL, BF16, CNAME, TNAME),        \
+    FA_ENTRY(128, 32, 1, 2, 2, CAUSAL, BF16, CNAME, TNAME),        \
+    FA_ENTRY(128, 32, 1, 4, 1, CAUSAL, BF16, CNAME, TNAME),        \
+    FA_ENTRY(128, 32, 1, 8, 1, CAUSAL, BF16, CNAME, TNAME)
+
 const ConfigEntry kConfigs[] = {
     FA_TILES(128, 1, 1, "causal", "bf16"), FA_TILES(128, 0, 1, "full", "bf16"),
     FA_TILES(128, 1, 0, "causal", "fp16"), FA_TILES(128, 0, 0, "full", "fp16"),
     FA_TILES(64, 1, 1, "causal", "bf16"),  FA_TILES(64, 0, 1, "full", "bf16"),
     FA_TILES(64, 1, 0, "causal", "fp16"),  FA_TILES(64, 0, 0, "full", "fp16"),
+    FA_TILES_BN32(1, 1, "causal", "bf16"), FA_TILES_BN32(0, 1, "full", "bf16"),
+    FA_TILES_BN32(1, 0, "causal", "fp16"), FA_TILES_BN32(0, 0, "full", "fp16"),
 };
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 
@@ -115,8 +125,10 @@ int find(int D, int bf16, int causal, int BN, int QB, int WPH, int HPW) {
     return -1;
 }
 
-// The dispatch rule.  Grouped-query problems pack 4 query heads of a group into one
-// workgroup, so each K/V tile is read once for all of them; groups of 2 pack 2 heads;
+// The dispatch rule, from a sweep of every configuration on the named workloads: 32-key
+// tiles for head dim 128 (fewer live registers, so the pipelined loop hides more latency),
+// 64-key tiles for head dim 64.  Grouped-query problems pack 4 query heads of a group into
+// one workgroup, so each K/V tile is read once for all of them; groups of 2 pack 2 heads;
 // the rest use 128 positions of one head.  Two 4-wave workgroups share a CU.
 int select(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal, int input_pos, int dtype) {
     (void)B;
@@ -126,9 +138,10 @@ int select(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal, int input
     const int bf16 = dtype == FA_DTYPE_BF16;
     const int cz = causal != 0;
     const int group = Hq / Hkv;
-    if (group % 4 == 0) return find(D, bf16, cz, 64, 1, 1, 4);
-    if (group % 2 == 0) return find(D, bf16, cz, 64, 1, 2, 2);
-    return find(D, bf16, cz, 64, 1, 4, 1);
+    const int bn = D == 128 ? 32 : 64;
+    if (group % 4 == 0) return find(D, bf16, cz, bn, 1, 1, 4);
+    if (group % 2 == 0) return find(D, bf16, cz, bn, 1, 2, 2);
+    return find(D, bf16, cz, bn, 1, 4, 1);
 }
 
 // Workgroup -> XCD mapping.  The hardware hands workgroup w to XCD w % 8.  Mode 1 gives

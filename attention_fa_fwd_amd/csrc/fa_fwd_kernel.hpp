@@ -27,9 +27,10 @@
 //  * K and V tiles are double-buffered in LDS and move there straight from HBM with
 //    gfx950's 128-bit buffer loads to LDS: no staging registers, no LDS write instructions.
 //    The buffer range ends at key Skv, so a ragged key tail lands as zeros.  The K loop is
-//    software-pipelined: step j issues the MFMAs of S(j+1) in the same block as the
-//    softmax and P V of tile j, so matrix work overlaps the exp2 work; K is loaded two
-//    tiles ahead and V one tile ahead in the same two-buffer LDS footprint.  16-byte chunks are XOR-swizzled per
+//    a three-stage software pipeline: step j issues the MFMAs of S(j+1) in the same block as the
+//    softmax of tile j together with the P V of tile j-1, so all matrix work of a step is
+//    independent of its exp2 work and can overlap it; K is loaded two tiles ahead and V
+//    one tile ahead of its use, in the same two-buffer LDS footprint.  16-byte chunks are XOR-swizzled per
 //    row so that tile writes, K operand reads and V transpose reads are bank-conflict free.
 //  * Register use is held to 256 per lane so that two waves share each SIMD: one wave's
 //    softmax and memory latency overlap the other's MFMAs.
@@ -97,7 +98,7 @@ struct Cfg {
     static constexpr int BMP = 32 * QB * WPH;   // query positions per workgroup
     static constexpr int WAVES_PER_SIMD = QB == 1 ? 2 : 1;  // register budget 256 / 512
     static_assert(D == 64 || D == 128, "head dim");
-    static_assert(BN == 64 || BN == 128, "key tile");
+    static_assert(BN == 32 || BN == 64, "key tile");
     static_assert(QB == 1 || QB == 2, "query blocks per wave");
     static_assert(NW == 4 || NW == 8, "waves per workgroup");
 };
@@ -360,18 +361,52 @@ void fa_fwd_kernel(Params p) {
         }
     };
 
-    // One K-loop step for tile j.  On entry s_cur holds S(j); the step issues S(j+1) into
-    // s_nxt in the same straight-line block as the softmax and P V of tile j, so the MFMAs
-    // of the next scores overlap the exp2 work of this tile.  Loads run two tiles ahead
-    // for K and one for V: the step reads k_lds[(j+1)%2] and v_lds[j%2] and loads K(j+2)
-    // into k_lds[j%2] and V(j+1) into v_lds[(j+1)%2], which nobody reads during step j.
-    auto step = [&](int j, auto par_tag, auto masked_tag, f32x16 (&s_cur)[KB][QB],
-                    f32x16 (&s_nxt)[KB][QB]) {
+    // O^T += V^T P^T for the tile whose V sits in `vb` and whose packed P is `pk`.
+    auto pv = [&](const unsigned char* vb, const u32x4 (&pk)[KB][QB][2]) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int k2 = 0; k2 < KB; ++k2)
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const unsigned char* pr = vb + voff[db] + (k2 * 32 + 16 * hf) * ROWB;
+                        const u32x2 x0 = lds_read_tr16(pr);
+                        const u32x2 x1 = lds_read_tr16(pr + 8 * ROWB);
+                        const u32x4 a = {x0[0], x0[1], x1[0], x1[1]};
+                        acc[db][qb] = mfma32<BF16>(a, pk[k2][qb][hf], acc[db][qb]);
+                    }
+    };
+
+    // Register sets that alternate with the parity of j: S(j) / S(j+1) and P(j-1) / P(j).
+    f32x16 sA[KB][QB], sB[KB][QB];
+    u32x4 pkA[KB][QB][2], pkB[KB][QB][2];
+    auto pick = [](auto par, auto& a, auto& b) -> auto& {
+        if constexpr (decltype(par)::value) return b;
+        else return a;
+    };
+
+    // One K-loop step for tile j, a three-stage software pipeline.  The step issues the
+    // MFMAs of S(j+1) = K(j+1) Q^T and of O^T += V(j-1)^T P(j-1)^T -- neither depends on
+    // this step's softmax -- in the same straight-line block as the softmax of S(j) into
+    // P(j), so all matrix work can overlap the exp2 work.  Loads: K(j+2) into k_lds[j%2]
+    // and V(j) into v_lds[j%2]; the step reads k_lds[(j+1)%2] and v_lds[(j-1)%2], so no
+    // buffer is written while it is read, and one barrier per step suffices.
+    auto step = [&](int j, auto par_tag, auto masked_tag, auto first_tag) {
         constexpr int PAR = decltype(par_tag)::value;      // j % 2
         constexpr bool MASKED = decltype(masked_tag)::value;
+        constexpr bool FIRST = decltype(first_tag)::value; // j == 0: no P(j-1) yet
+        using OTHER = std::integral_constant<int, PAR ^ 1>;
+        auto& s_cur = pick(par_tag, sA, sB);
+        auto& s_nxt = pick(par_tag, sB, sA);
+        auto& pk_cur = pick(par_tag, pkA, pkB);
+        auto& pk_prev = pick(par_tag, pkB, pkA);
         fetch(kp, j + 2, kl(par_tag), ksrc);
-        fetch(vp, j + 1, vl(std::integral_constant<int, PAR ^ 1>{}), vsrc);
-        if (!MASKED || j < wave_tc) {
+        fetch(vp, j, vl(par_tag), vsrc);
+        const bool do_sm = !MASKED || j < wave_tc;          // softmax of tile j
+        const bool do_pv = !FIRST && (!MASKED || j - 1 < wave_tc);   // P V of tile j-1
+        if (do_sm) {
             if constexpr (MASKED) {
                 const int j0 = j * BN;
 #pragma unroll
@@ -387,14 +422,17 @@ void fa_fwd_kernel(Params p) {
                         }
                 }
             }
-            // S(j+1) = K(j+1) Q^T: MFMA work independent of the softmax below.
-            qk(kl(std::integral_constant<int, PAR ^ 1>{}), s_nxt);
-
+        }
+        // Matrix work of this step: S(j+1), and P V of tile j-1.
+        qk(kl(OTHER{}), s_nxt);
+        if constexpr (!FIRST) {
+            if (!MASKED || do_pv) pv(vl(OTHER{}), pk_prev);
+        }
+        if (do_sm) {
             // P = exp2(c s - m) with the running max m, packed to the storage type, and the
             // lane's partial row sums in fp32 (each 16-key block summed as soon as it is
             // packed).  Summing the rounded bf16 p instead would move LSE by ~1e-3 on rows
             // with few visible keys.
-            u32x4 pk[KB][QB][2];
             float ts[QB];
             auto make_p = [&]() {
 #pragma unroll
@@ -410,8 +448,8 @@ void fa_fwd_kernel(Params p) {
 #pragma unroll
                         for (int hf = 0; hf < 2; ++hf) {
                             const float* e = t + 8 * hf;
-                            pk[k2][qb][hf] = (u32x4){pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]),
-                                                     pack2<BF16>(e[4], e[5]), pack2<BF16>(e[6], e[7])};
+                            pk_cur[k2][qb][hf] = (u32x4){pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]),
+                                                         pack2<BF16>(e[4], e[5]), pack2<BF16>(e[6], e[7])};
                         }
                         psum[k2] = Tree<16>::sum(t);
                     }
@@ -423,7 +461,8 @@ void fa_fwd_kernel(Params p) {
             // <= 2^15 the running max m may lag the true row max: p fits the storage type and
             // the softmax is unchanged, since acc and l share m.  Otherwise (the first tile,
             // where m = -inf makes the sums inf or NaN, or a jump of the max) raise m to the
-            // row max, rescale acc and l, and recompute P.  No row max on the common path.
+            // row max, rescale acc (which already holds P V up to tile j-1) and l, and
+            // recompute P.  No row max on the common path.
             bool bad = false;
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) bad |= !(ts[qb] <= P_LIMIT);
@@ -444,64 +483,51 @@ void fa_fwd_kernel(Params p) {
                 }
                 make_p();
             }
-
-            // O^T += V^T P^T.
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                l_run[qb] += xhalf_sum(ts[qb]);
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-#pragma unroll
-                    for (int k2 = 0; k2 < KB; ++k2) {
-#pragma unroll
-                        for (int hf = 0; hf < 2; ++hf) {
-                            const unsigned char* pr =
-                                vl(par_tag) + voff[db] + (k2 * 32 + 16 * hf) * ROWB;
-                            const u32x2 x0 = lds_read_tr16(pr);
-                            const u32x2 x1 = lds_read_tr16(pr + 8 * ROWB);
-                            const u32x4 a = {x0[0], x0[1], x1[0], x1[1]};
-                            acc[db][qb] = mfma32<BF16>(a, pk[k2][qb][hf], acc[db][qb]);
-                        }
-                    }
-                }
-            }
+            for (int qb = 0; qb < QB; ++qb) l_run[qb] += xhalf_sum(ts[qb]);
         }
         __syncthreads();
     };
 
-    // Prologue: K(0), V(0) to LDS; S(0) while K(1) arrives.
+    // Prologue: K(0) to LDS; S(0) while K(1) arrives.
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    f32x16 s0[KB][QB], s1[KB][QB];
+    using F = std::false_type;
+    using TT = std::true_type;
     fetch(kp, 0, k_lds0, ksrc);
-    fetch(vp, 0, v_lds0, vsrc);
     __syncthreads();
     fetch(kp, 1, k_lds1, ksrc);
-    qk(k_lds0, s0);
+    qk(k_lds0, sA);
     __syncthreads();
 
     // The K loop in two parts (K-loop split): tiles needing no mask, then the diagonal /
-    // key-tail tiles.  Unrolled by two so buffer parity and the roles of s0 / s1 are fixed.
-    using F = std::false_type;
-    using TT = std::true_type;
-    int j = 0;
+    // key-tail tiles.  Unrolled by two so the parity of j -- buffers and register roles --
+    // is fixed at compile time in every copy of the step.
+    if (n_free > 0) step(0, P0{}, F{}, TT{});
+    else step(0, P0{}, TT{}, TT{});
+    int j = 1;
     for (; j + 1 < n_free; j += 2) {
-        step(j, P0{}, F{}, s0, s1);
-        step(j + 1, P1{}, F{}, s1, s0);
+        step(j, P1{}, F{}, F{});
+        step(j + 1, P0{}, F{}, F{});
     }
     if (j < n_free) {
-        step(j, P0{}, F{}, s0, s1);
+        step(j, P1{}, F{}, F{});
         ++j;
-        if (j < Tc) {
-            step(j, P1{}, TT{}, s1, s0);
-            ++j;
-        }
+    }
+    if (j < Tc && (j & 1)) {
+        step(j, P1{}, TT{}, F{});
+        ++j;
     }
     for (; j + 1 < Tc; j += 2) {
-        step(j, P0{}, TT{}, s0, s1);
-        step(j + 1, P1{}, TT{}, s1, s0);
+        step(j, P0{}, TT{}, F{});
+        step(j + 1, P1{}, TT{}, F{});
     }
-    if (j < Tc) step(j, P0{}, TT{}, s0, s1);
+    if (j < Tc) step(j, P0{}, TT{}, F{});
+    // Drain: P V of the last tile (its V arrived during the last step).
+    if (Tc - 1 < wave_tc) {
+        if ((Tc - 1) & 1) pv(v_lds1, pkB);
+        else pv(v_lds0, pkA);
+    }
 
     // Epilogue: O = acc / l (v_rcp_f32), rounded to the storage type; LSE = ln2 (m + log2 l).
     T* op = (T*)p.o + (size_t)(b * p.Hq + hq) * p.Sq * D;
