@@ -14,7 +14,8 @@ import math
 import os
 import threading
 
-__all__ = ["fa_fwd", "fa_fwd_into", "select_config", "config_names", "num_configs", "FaError",
+__all__ = ["fa_fwd", "fa_fwd_into", "fa_fwd_splitkv", "fa_fwd_splitkv_into", "splitkv_num_splits",
+           "splitkv_workspace_size", "select_config", "config_names", "num_configs", "FaError",
            "load_library", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_fwd.so")
@@ -43,6 +44,12 @@ def _declare(lib):
     lib.fa_fwd.restype = _c_int
     lib.fa_fwd_config.argtypes = _FWD_ARGS + [_c_int]
     lib.fa_fwd_config.restype = _c_int
+    lib.fa_fwd_splitkv.argtypes = _FWD_ARGS[:-1] + [_c_int, _c_int, _vp, ctypes.c_size_t, _vp]
+    lib.fa_fwd_splitkv.restype = _c_int
+    lib.fa_splitkv_num_splits.argtypes = [_c_int] * 10
+    lib.fa_splitkv_num_splits.restype = _c_int
+    lib.fa_splitkv_workspace_size.argtypes = [_c_int] * 5
+    lib.fa_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.fa_select_config.argtypes = [_c_int] * 9
     lib.fa_select_config.restype = _c_int
     lib.fa_num_configs.argtypes = []
@@ -88,15 +95,10 @@ def _check(rc: int):
         raise FaError(rc, load_library().fa_strerror(rc).decode())
 
 
-def fa_fwd_into(q, k, v, out, lse, scale=None, causal=True, input_pos=0, config=-1, stream=None):
-    """Run the kernel into caller-provided ``out`` [B,Hq,Sq,D] and ``lse`` [B,Hq,Sq] (fp32).
-
-    All tensors must be contiguous and on the same GPU.  ``stream`` is a raw
-    hipStream_t value; by default torch's current stream on q's device.
-    """
+def _check_tensors(q, k, v, out, lse):
+    """Shapes, dtypes, devices and contiguity of one call; returns (B, Hq, Hkv, Sq, Skv, D)."""
     import torch
 
-    lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
@@ -116,6 +118,19 @@ def fa_fwd_into(q, k, v, out, lse, scale=None, causal=True, input_pos=0, config=
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, Sq):
         raise ValueError("out must match q and lse must be [B, Hq, Sq]")
+    return B, Hq, Hkv, Sq, Skv, D
+
+
+def fa_fwd_into(q, k, v, out, lse, scale=None, causal=True, input_pos=0, config=-1, stream=None):
+    """Run the kernel into caller-provided ``out`` [B,Hq,Sq,D] and ``lse`` [B,Hq,Sq] (fp32).
+
+    All tensors must be contiguous and on the same GPU.  ``stream`` is a raw
+    hipStream_t value; by default torch's current stream on q's device.
+    """
+    import torch
+
+    lib = load_library()
+    B, Hq, Hkv, Sq, Skv, D = _check_tensors(q, k, v, out, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if stream is None:
@@ -127,6 +142,70 @@ def fa_fwd_into(q, k, v, out, lse, scale=None, causal=True, input_pos=0, config=
                                stream, int(config))
     _check(rc)
     return out, lse
+
+
+def splitkv_num_splits(B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype, config=-1) -> int:
+    """Split count fa_fwd_splitkv picks for num_splits=0 (dtype: torch dtype or FA code)."""
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    rc = load_library().fa_splitkv_num_splits(B, Hq, Hkv, Sq, Skv, D, 1 if causal else 0,
+                                              input_pos, code, config)
+    _check(rc if rc < 0 else 0)
+    return rc
+
+
+def splitkv_workspace_size(B, Hq, Sq, D, num_splits) -> int:
+    """Workspace bytes fa_fwd_splitkv needs for ``num_splits`` key ranges."""
+    return int(load_library().fa_splitkv_workspace_size(B, Hq, Sq, D, num_splits))
+
+
+def fa_fwd_splitkv_into(q, k, v, out, lse, workspace, num_splits=0, scale=None, causal=True,
+                        input_pos=0, config=-1, stream=None):
+    """Split-KV forward into caller-provided ``out``, ``lse`` and ``workspace``.
+
+    ``workspace`` is a contiguous GPU tensor of at least
+    ``splitkv_workspace_size(B, Hq, Sq, D, splits)`` bytes (None when one split runs).
+    ``num_splits`` = 0 lets the library choose.
+    """
+    import torch
+
+    lib = load_library()
+    B, Hq, Hkv, Sq, Skv, D = _check_tensors(q, k, v, out, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    if workspace is not None:
+        if not workspace.is_cuda or workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on q's device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    else:
+        ws_ptr, ws_bytes = None, 0
+    with torch.cuda.device(q.device):
+        rc = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), B, Hq, Hkv, Sq, Skv, D, float(scale),
+                                1 if causal else 0, int(input_pos), _dtype_code(q.dtype),
+                                int(num_splits), int(config), ws_ptr, ws_bytes, stream)
+    _check(rc)
+    return out, lse
+
+
+def fa_fwd_splitkv(q, k, v, scale=None, causal=True, input_pos=0, num_splits=0, config=-1):
+    """Split-KV attention forward: the same result as ``fa_fwd`` (up to rounding order),
+    computed over ``num_splits`` key ranges (0 = the library's choice) and merged.
+    Allocates the workspace with torch; returns (out, lse)."""
+    import torch
+
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Skv, _ = k.shape
+    if num_splits == 0:
+        num_splits = splitkv_num_splits(B, Hq, Hkv, Sq, Skv, D, causal, input_pos, q.dtype, config)
+    nbytes = splitkv_workspace_size(B, Hq, Sq, D, num_splits)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    return fa_fwd_splitkv_into(q, k, v, out, lse, ws, num_splits=num_splits, scale=scale,
+                               causal=causal, input_pos=input_pos, config=config)
 
 
 def fa_fwd(q, k, v, scale=None, causal=True, input_pos=0, config=-1):

@@ -9,6 +9,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -33,7 +34,7 @@ struct ConfigEntry {
 
 template <class C>
 hipError_t launch_cfg(const Params& p, hipStream_t s) {
-    const long long wgs = (long long)p.n_tiles * p.hsub * p.B * p.Hkv;
+    const long long wgs = (long long)p.n_tiles * p.hsub * p.B * p.Hkv * p.num_splits;
     hipLaunchKernelGGL(fa::fa_fwd_kernel<C>, dim3((unsigned)wgs), dim3(C::NT), 0, s, p);
     return hipGetLastError();
 }
@@ -71,6 +72,26 @@ const ConfigEntry kConfigs[] = {
     FA_TILES_BN32(1, 0, "causal", "fp16"), FA_TILES_BN32(0, 0, "full", "fp16"),
 };
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
+
+// Largest split count: bounds the merge kernel's loop and the workspace.
+constexpr int kMaxSplits = 256;
+// CUs of an MI355X, and the resident workgroups that fill it (two four-wave workgroups
+// per CU).
+constexpr long long kNumCUs = 256;
+constexpr long long kFullGrid = 512;
+
+hipError_t launch_merge(const Params& p, int D, int bf16, hipStream_t s) {
+    const int rows = p.B * p.Hq * p.Sq;
+    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    if (D == 128) {
+        if (bf16) hipLaunchKernelGGL((fa::fa_merge_kernel<128, true>), grid, block, 0, s, p.o_part, p.lse_part, p.o, p.lse, rows, p.num_splits);
+        else hipLaunchKernelGGL((fa::fa_merge_kernel<128, false>), grid, block, 0, s, p.o_part, p.lse_part, p.o, p.lse, rows, p.num_splits);
+    } else {
+        if (bf16) hipLaunchKernelGGL((fa::fa_merge_kernel<64, true>), grid, block, 0, s, p.o_part, p.lse_part, p.o, p.lse, rows, p.num_splits);
+        else hipLaunchKernelGGL((fa::fa_merge_kernel<64, false>), grid, block, 0, s, p.o_part, p.lse_part, p.o, p.lse, rows, p.num_splits);
+    }
+    return hipGetLastError();
+}
 
 bool overlaps(uintptr_t a, size_t na, uintptr_t b, size_t nb) {
     return a < b + nb && b < a + na;
@@ -160,18 +181,56 @@ void xcd_mapping(int ngrp, int items_per_group, int* mode, int* arg) {
     }
 }
 
-int run(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
-        int Hkv, int Sq, int Skv, int D, float scale, int causal, int input_pos, int dtype,
-        void* stream, int config) {
-    int rc = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos, dtype);
-    if (rc != FA_OK) return rc;
+// Bytes of split-KV workspace: the fp32 partial O [S][B*Hq*Sq][D], then the fp32 partial
+// LSE [S][B*Hq*Sq].  Zero for one split.
+size_t workspace_bytes_for(int B, int Hq, int Sq, int D, int num_splits) {
+    if (num_splits <= 1 || B <= 0 || Hq <= 0 || Sq <= 0) return 0;
+    return (size_t)num_splits * B * Hq * Sq * (size_t)(D + 1) * sizeof(float);
+}
+
+// Tiles of the longest key range of any query tile (all keys, or the causal extent).
+int max_key_tiles(const ConfigEntry& c, int Sq, int Skv, int causal, int input_pos) {
+    const long long vis = causal ? std::min<long long>((long long)input_pos + Sq, Skv) : Skv;
+    return (int)((vis + c.BN - 1) / c.BN);
+}
+
+// Split count for num_splits = 0.  Splitting pays only when the plain grid leaves CUs idle
+// (fewer workgroups than CUs): then enough ranges for about kFullGrid workgroups, with at
+// least 8 key tiles per range, and no more ranges than keep the partials' fp32 traffic
+// (written once, read once by the merge) within the K/V bytes the kernel reads.  Chosen
+// from measured sweeps: decoding with 8 to 128 workgroups runs fastest at ~512 after the
+// split; a 256-workgroup prefill loses to the partial traffic.
+int auto_splits(const ConfigEntry& c, long long wgs, int B, int Hq, int Hkv, int Sq, int Skv,
+                int causal, int input_pos) {
+    if (wgs <= 0 || wgs >= kNumCUs) return 1;
+    const long long want = (kFullGrid + wgs - 1) / wgs;
+    const long long by_len = max_key_tiles(c, Sq, Skv, causal, input_pos) / 8;
+    const double kv_bytes = 4.0 * B * Hkv * (double)Skv * c.D;
+    const double part_bytes = 8.0 * B * Hq * (double)Sq * (c.D + 1);   // per range
+    const long long by_traffic = (long long)(kv_bytes / part_bytes);
+    return (int)std::max(1LL, std::min({want, by_len, by_traffic, (long long)kMaxSplits}));
+}
+
+int resolve_config(int config, int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                   int input_pos, int dtype) {
     if (config < -1 || config >= kNumConfigs) return FA_ERR_INVALID_CONFIG;
     if (config == -1) config = select(B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype);
     if (config < 0) return FA_ERR_INVALID_CONFIG;
-    const ConfigEntry& c = kConfigs[config];
-    if (!applicable(c, Hq, Hkv, D, causal, dtype)) return FA_ERR_INVALID_CONFIG;
-    if ((long long)B * Hq * Sq == 0) return FA_OK;
+    if (!applicable(kConfigs[config], Hq, Hkv, D, causal, dtype)) return FA_ERR_INVALID_CONFIG;
+    return config;
+}
 
+long long grid_of(const ConfigEntry& c, int B, int Hq, int Hkv, int Sq) {
+    const int bmp = 32 * c.QB * c.WPH;
+    return (long long)((Sq + bmp - 1) / bmp) * (Hq / Hkv / c.HPW) * B * Hkv;
+}
+
+// num_splits: 1 = the plain forward pass (out / lse written by the attention kernel);
+// > 1 = partials into `workspace`, then the merge kernel.  Arguments already validated.
+int launch(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+           int Hkv, int Sq, int Skv, float scale, int causal, int input_pos, int config,
+           int num_splits, void* workspace, void* stream) {
+    const ConfigEntry& c = kConfigs[config];
     const int bmp = 32 * c.QB * c.WPH;
     Params p;
     p.q = q;
@@ -189,10 +248,64 @@ int run(const void* q, const void* k, const void* v, void* out, float* lse, int 
     p.group = Hq / Hkv;
     p.n_tiles = (Sq + bmp - 1) / bmp;
     p.hsub = p.group / c.HPW;
-    const long long wgs = (long long)p.n_tiles * p.hsub * B * Hkv;
+    p.num_splits = num_splits;
+    p.o_part = nullptr;
+    p.lse_part = nullptr;
+    if (num_splits > 1) {
+        const size_t rows = (size_t)B * Hq * Sq;
+        p.o_part = (float*)workspace;
+        p.lse_part = (float*)workspace + (size_t)num_splits * rows * c.D;
+    }
+    const long long wgs = (long long)p.n_tiles * p.hsub * B * Hkv * num_splits;
     if (wgs > 0x7fffffffLL) return FA_ERR_INVALID_SHAPE;
-    xcd_mapping(B * Hkv, p.n_tiles * p.hsub, &p.map_mode, &p.map_arg);
-    return c.launch(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    xcd_mapping(B * Hkv, p.n_tiles * p.hsub * num_splits, &p.map_mode, &p.map_arg);
+    hipStream_t s = (hipStream_t)stream;
+    if (c.launch(p, s) != hipSuccess) return FA_ERR_LAUNCH;
+    if (num_splits > 1 && launch_merge(p, c.D, c.bf16, s) != hipSuccess) return FA_ERR_LAUNCH;
+    return FA_OK;
+}
+
+int run(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+        int Hkv, int Sq, int Skv, int D, float scale, int causal, int input_pos, int dtype,
+        void* stream, int config) {
+    int rc = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos, dtype);
+    if (rc != FA_OK) return rc;
+    config = resolve_config(config, B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype);
+    if (config < 0) return config;
+    if ((long long)B * Hq * Sq == 0) return FA_OK;
+    return launch(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, scale, causal, input_pos, config, 1,
+                  nullptr, stream);
+}
+
+int run_splitkv(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal, int input_pos,
+                int dtype, int num_splits, int config, void* workspace, size_t workspace_bytes,
+                void* stream) {
+    int rc = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos, dtype);
+    if (rc != FA_OK) return rc;
+    config = resolve_config(config, B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype);
+    if (config < 0) return config;
+    if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_INVALID_SPLITS;
+    const ConfigEntry& c = kConfigs[config];
+    if (num_splits == 0)
+        num_splits = auto_splits(c, grid_of(c, B, Hq, Hkv, Sq), B, Hq, Hkv, Sq, Skv, causal,
+                                 causal ? input_pos : 0);
+    if ((long long)B * Hq * Sq == 0) return FA_OK;
+    if (num_splits > 1) {
+        const size_t need = workspace_bytes_for(B, Hq, Sq, D, num_splits);
+        if (!workspace) return FA_ERR_NULL_POINTER;
+        if ((uintptr_t)workspace & 15u) return FA_ERR_MISALIGNED;
+        if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+        const size_t qb = (size_t)B * Hq * Sq * D * 2, kb = (size_t)B * Hkv * Skv * D * 2;
+        const size_t lb = (size_t)B * Hq * Sq * 4;
+        const uintptr_t w = (uintptr_t)workspace;
+        if (overlaps(w, need, (uintptr_t)q, qb) || overlaps(w, need, (uintptr_t)k, kb) ||
+            overlaps(w, need, (uintptr_t)v, kb) || overlaps(w, need, (uintptr_t)out, qb) ||
+            overlaps(w, need, (uintptr_t)lse, lb))
+            return FA_ERR_ALIAS;
+    }
+    return launch(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, scale, causal, input_pos, config,
+                  num_splits, workspace, stream);
 }
 
 }  // namespace
@@ -211,6 +324,33 @@ int fa_fwd_config(const void* q, const void* k, const void* v, void* out, float*
                   int input_pos, int dtype, void* stream, int config) {
     return run(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos, dtype,
                stream, config);
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                   int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
+                   int input_pos, int dtype, int num_splits, int config, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    return run_splitkv(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos,
+                       dtype, num_splits, config, workspace, workspace_bytes, stream);
+}
+
+int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                          int input_pos, int dtype, int config) {
+    if (B < 0 || Hq < 0 || Sq < 0 || Hkv < 1 || Skv < 1) return FA_ERR_INVALID_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_HEAD_GROUP;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
+    if (input_pos < 0 || (long long)input_pos + Sq > INT_MAX) return FA_ERR_INVALID_INPUT_POS;
+    config = resolve_config(config, B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype);
+    if (config < 0) return config;
+    const ConfigEntry& c = kConfigs[config];
+    return auto_splits(c, grid_of(c, B, Hq, Hkv, Sq), B, Hq, Hkv, Sq, Skv, causal,
+                       causal ? input_pos : 0);
+}
+
+size_t fa_splitkv_workspace_size(int B, int Hq, int Sq, int D, int num_splits) {
+    if (D != 64 && D != 128) return 0;
+    return workspace_bytes_for(B, Hq, Sq, D, num_splits);
 }
 
 int fa_select_config(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal, int input_pos,
@@ -244,6 +384,8 @@ const char* fa_strerror(int code) {
         case FA_ERR_ALIAS: return "out or lse overlaps an input or each other";
         case FA_ERR_INVALID_CONFIG: return "kernel configuration id out of range or not applicable to this call";
         case FA_ERR_LAUNCH: return "kernel launch failed";
+        case FA_ERR_INVALID_SPLITS: return "num_splits must be in 0..256";
+        case FA_ERR_WORKSPACE: return "split-KV workspace smaller than fa_splitkv_workspace_size()";
         default: return "unknown status code";
     }
 }

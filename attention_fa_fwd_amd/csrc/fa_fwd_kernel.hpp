@@ -45,6 +45,12 @@
 //  * Workgroups are dispatched round-robin over the 8 XCDs.  The workgroup id is remapped
 //    so that each XCD works on whole (batch, K/V head) groups, keeping their K/V tiles in
 //    its own L2, and within an XCD the heaviest causal tiles come first.
+//  * Split-KV (for grids too small to fill 256 CUs, e.g. decoding with one query row --
+//    the pages' "too few tiles" case, cuTile post Part 2 "Autotuning", "How I Beat PyTorch's
+//    Flash Attention" Phase 5): each query tile's visible K/V tiles are cut into num_splits
+//    tile-aligned ranges, one workgroup each.  A workgroup stores its range's normalised
+//    partial O (fp32) and LSE; fa_merge_kernel folds the partials with the online-softmax
+//    rescale ("Online softmax update") applied across ranges.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -59,6 +65,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -81,6 +88,9 @@ struct Params {
     int hsub;        // head groups per K/V head: group / HPW
     int map_mode;    // workgroup -> XCD mapping: 0 plain, 1 groups per XCD, 2 XCDs per group
     int map_arg;     // mode 1: groups per XCD; mode 2: XCDs per group
+    int num_splits;  // key ranges per query tile; > 1 writes partials for the merge kernel
+    float* o_part;   // num_splits > 1: normalised partial O, fp32 [num_splits][B*Hq*Sq][D]
+    float* lse_part; // num_splits > 1: partial LSE, fp32 [num_splits][B*Hq*Sq]
 };
 
 // Compile-time configuration of one kernel instance.
@@ -227,8 +237,8 @@ void fa_fwd_kernel(Params p) {
     const int l32 = lane & 31;
     const int h = lane >> 5;
 
-    // Workgroup -> (batch, K/V head, head subgroup, query tile); see the header comment.
-    const int ipg = p.n_tiles * p.hsub;          // work items per (batch, K/V head) group
+    // Workgroup -> (batch, K/V head, query tile, head subgroup, key split); see the header
+    // comment.  The splits of one query tile are adjacent work items.
     const int ngrp = p.B * p.Hkv;
     int grp, item;
     {
@@ -248,10 +258,11 @@ void fa_fwd_kernel(Params p) {
     }
     const int b = grp / p.Hkv;
     const int kvh = grp - b * p.Hkv;
+    const int split = item % p.num_splits;
+    item /= p.num_splits;
     const int trank = item / p.hsub;
     const int hs = item - trank * p.hsub;
     const int tile = CAUSAL ? p.n_tiles - 1 - trank : trank;
-    (void)ipg;
     const int hq = kvh * p.group + hs * HPW + w / WPH;
     const int q0 = tile * C::BMP;
     const int qw0 = q0 + (w % WPH) * (32 * QB);
@@ -283,6 +294,14 @@ void fa_fwd_kernel(Params p) {
     const int wave_tc = qw_last < qw0 ? 0
                         : CAUSAL ? (min(p.input_pos + qw_last + 1, p.Skv) + BN - 1) / BN
                                  : Tc;
+    // This workgroup's key split: tiles [t0, t1) of [0, Tc), tile-aligned, so no mask is
+    // needed at split boundaries.  Loads stop at key kend.  An empty range (more splits than
+    // tiles) leaves the state empty: the partial is O = 0, LSE = -inf.
+    const int t0 = (int)((long long)Tc * split / p.num_splits);
+    const int t1 = (int)((long long)Tc * (split + 1) / p.num_splits);
+    const int nt = t1 - t0;                    // tiles in this range
+    const int nf = max(0, min(n_free - t0, nt));   // leading tiles of it needing no mask
+    const int kend = min(p.Skv, t1 * BN);
 
     // Running state: m (exp2 domain, possibly stale), l, acc (= O^T blocks).
     float m_run[QB], l_run[QB];
@@ -322,8 +341,8 @@ void fa_fwd_kernel(Params p) {
     // i * LOAD_STRIDE as the scalar offset (gfx950's range check covers voffset + soffset,
     // so every load past the end of the range reads zero).
     auto fetch = [&](const T* base, int j, unsigned char* dst, int src) {
-        const int j0 = min(j * BN, p.Skv);
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (size_t)j0 * D, min(p.Skv - j0, BN) * ROWB);
+        const int j0 = min(j * BN, kend);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (size_t)j0 * D, min(kend - j0, BN) * ROWB);
 #pragma unroll
         for (int i = 0; i < LD; ++i)
             buffer_load_lds16(r, dst + (i * C::NW + w) * 1024, src, i * LOAD_STRIDE);
@@ -437,7 +456,9 @@ void fa_fwd_kernel(Params p) {
             auto make_p = [&]() {
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
-                    const float neg_m = -m_run[qb];
+                    // m = -inf until the row's first visible key; meanwhile use 0, so masked
+                    // keys give p = 0, and take the slow path below.
+                    const float neg_m = m_run[qb] == -__builtin_inff() ? 0.0f : -m_run[qb];
                     float psum[KB];
 #pragma unroll
                     for (int k2 = 0; k2 < KB; ++k2) {
@@ -459,13 +480,13 @@ void fa_fwd_kernel(Params p) {
             make_p();
             // Lazy max.  Every p is at most its lane's partial sum, so while those sums stay
             // <= 2^15 the running max m may lag the true row max: p fits the storage type and
-            // the softmax is unchanged, since acc and l share m.  Otherwise (the first tile,
-            // where m = -inf makes the sums inf or NaN, or a jump of the max) raise m to the
-            // row max, rescale acc (which already holds P V up to tile j-1) and l, and
-            // recompute P.  No row max on the common path.
+            // the softmax is unchanged, since acc and l share m.  Otherwise (a jump of the
+            // max, or m still -inf: the row's first tile) raise m to the row max, rescale acc
+            // (which already holds P V up to tile j-1) and l, and recompute P.  No row max on
+            // the common path.
             bool bad = false;
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) bad |= !(ts[qb] <= P_LIMIT);
+            for (int qb = 0; qb < QB; ++qb) bad |= !(ts[qb] <= P_LIMIT) || m_run[qb] == -__builtin_inff();
             if (__builtin_amdgcn_ballot_w64(bad) != 0) {
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
@@ -475,7 +496,8 @@ void fa_fwd_kernel(Params p) {
 #pragma unroll
                         for (int i = 0; i < 16; ++i) t[k2 * 16 + i] = s_cur[k2][qb][i];
                     const float m_new = fmaxf(m_run[qb], xhalf_max(Tree<KB * 16>::max(t)) * p.c);
-                    const float alpha = fast_exp2(m_run[qb] - m_new);
+                    // A row with no visible key yet keeps m = -inf and its (zero) state.
+                    const float alpha = m_new == -__builtin_inff() ? 1.0f : fast_exp2(m_run[qb] - m_new);
                     m_run[qb] = m_new;
                     l_run[qb] *= alpha;
 #pragma unroll
@@ -489,68 +511,125 @@ void fa_fwd_kernel(Params p) {
         __syncthreads();
     };
 
-    // Prologue: K(0) to LDS; S(0) while K(1) arrives.
+    // Prologue: K(t0) to LDS; S(t0) while K(t0+1) arrives.  Local step i handles tile t0+i
+    // and uses buffers / register sets of parity i % 2.
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
     using F = std::false_type;
     using TT = std::true_type;
-    fetch(kp, 0, k_lds0, ksrc);
-    __syncthreads();
-    fetch(kp, 1, k_lds1, ksrc);
-    qk(k_lds0, sA);
-    __syncthreads();
+    if (nt > 0) {
+        fetch(kp, t0, k_lds0, ksrc);
+        __syncthreads();
+        fetch(kp, t0 + 1, k_lds1, ksrc);
+        qk(k_lds0, sA);
+        __syncthreads();
 
-    // The K loop in two parts (K-loop split): tiles needing no mask, then the diagonal /
-    // key-tail tiles.  Unrolled by two so the parity of j -- buffers and register roles --
-    // is fixed at compile time in every copy of the step.
-    if (n_free > 0) step(0, P0{}, F{}, TT{});
-    else step(0, P0{}, TT{}, TT{});
-    int j = 1;
-    for (; j + 1 < n_free; j += 2) {
-        step(j, P1{}, F{}, F{});
-        step(j + 1, P0{}, F{}, F{});
-    }
-    if (j < n_free) {
-        step(j, P1{}, F{}, F{});
-        ++j;
-    }
-    if (j < Tc && (j & 1)) {
-        step(j, P1{}, TT{}, F{});
-        ++j;
-    }
-    for (; j + 1 < Tc; j += 2) {
-        step(j, P0{}, TT{}, F{});
-        step(j + 1, P1{}, TT{}, F{});
-    }
-    if (j < Tc) step(j, P0{}, TT{}, F{});
-    // Drain: P V of the last tile (its V arrived during the last step).
-    if (Tc - 1 < wave_tc) {
-        if ((Tc - 1) & 1) pv(v_lds1, pkB);
-        else pv(v_lds0, pkA);
+        // The K loop in two parts (K-loop split): tiles needing no mask, then the diagonal /
+        // key-tail tiles.  Unrolled by two so the parity of i -- buffers and register roles
+        // -- is fixed at compile time in every copy of the step.
+        if (nf > 0) step(t0, P0{}, F{}, TT{});
+        else step(t0, P0{}, TT{}, TT{});
+        int i = 1;
+        for (; i + 1 < nf; i += 2) {
+            step(t0 + i, P1{}, F{}, F{});
+            step(t0 + i + 1, P0{}, F{}, F{});
+        }
+        if (i < nf) {
+            step(t0 + i, P1{}, F{}, F{});
+            ++i;
+        }
+        if (i < nt && (i & 1)) {
+            step(t0 + i, P1{}, TT{}, F{});
+            ++i;
+        }
+        for (; i + 1 < nt; i += 2) {
+            step(t0 + i, P0{}, TT{}, F{});
+            step(t0 + i + 1, P1{}, TT{}, F{});
+        }
+        if (i < nt) step(t0 + i, P0{}, TT{}, F{});
+        // Drain: P V of the last tile (its V arrived during the last step).
+        if (t1 - 1 < wave_tc) {
+            if ((nt - 1) & 1) pv(v_lds1, pkB);
+            else pv(v_lds0, pkA);
+        }
     }
 
-    // Epilogue: O = acc / l (v_rcp_f32), rounded to the storage type; LSE = ln2 (m + log2 l).
-    T* op = (T*)p.o + (size_t)(b * p.Hq + hq) * p.Sq * D;
-    float* lp = p.lse + (size_t)(b * p.Hq + hq) * p.Sq;
+    // Epilogue: O = acc / l (v_rcp_f32); LSE = ln2 (m + log2 l), -inf for a row with no
+    // visible key (l = 0, O = 0).  One split: O rounded to the storage type.  Several
+    // splits: the normalised partial O in fp32 and its LSE, for the merge kernel.
+    const size_t head_row0 = (size_t)(b * p.Hq + hq) * p.Sq;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int row = qw0 + qb * 32 + l32;
         if (row < p.Sq) {
-            const float inv = __builtin_amdgcn_rcpf(l_run[qb]);
-            T* orow = op + (size_t)row * D;
+            const float l = l_run[qb];
+            const float inv = l > 0.0f ? __builtin_amdgcn_rcpf(l) : 0.0f;
+            const float lse = l > 0.0f ? (m_run[qb] + __builtin_amdgcn_logf(l)) * LN2 : -__builtin_inff();
+            if (p.num_splits == 1) {
+                T* orow = (T*)p.o + (head_row0 + row) * D;
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const f32x16 a = acc[db][qb] * inv;
-                const u32x4 w0 = {pack2<BF16>(a[0], a[1]), pack2<BF16>(a[2], a[3]),
-                                  pack2<BF16>(a[4], a[5]), pack2<BF16>(a[6], a[7])};
-                const u32x4 w1 = {pack2<BF16>(a[8], a[9]), pack2<BF16>(a[10], a[11]),
-                                  pack2<BF16>(a[12], a[13]), pack2<BF16>(a[14], a[15])};
-                *(u32x4*)(orow + db * 32 + 16 * h) = w0;
-                *(u32x4*)(orow + db * 32 + 16 * h + 8) = w1;
+                for (int db = 0; db < DB; ++db) {
+                    const f32x16 a = acc[db][qb] * inv;
+                    const u32x4 w0 = {pack2<BF16>(a[0], a[1]), pack2<BF16>(a[2], a[3]),
+                                      pack2<BF16>(a[4], a[5]), pack2<BF16>(a[6], a[7])};
+                    const u32x4 w1 = {pack2<BF16>(a[8], a[9]), pack2<BF16>(a[10], a[11]),
+                                      pack2<BF16>(a[12], a[13]), pack2<BF16>(a[14], a[15])};
+                    *(u32x4*)(orow + db * 32 + 16 * h) = w0;
+                    *(u32x4*)(orow + db * 32 + 16 * h + 8) = w1;
+                }
+                if (h == 0) p.lse[head_row0 + row] = lse;
+            } else {
+                const size_t rows = (size_t)p.B * p.Hq * p.Sq;
+                float* orow = p.o_part + ((size_t)split * rows + head_row0 + row) * D;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const f32x16 a = acc[db][qb] * inv;
+#pragma unroll
+                    for (int v4 = 0; v4 < 4; ++v4)
+                        *(f32x4*)(orow + db * 32 + 16 * h + 4 * v4) =
+                            (f32x4){a[4 * v4], a[4 * v4 + 1], a[4 * v4 + 2], a[4 * v4 + 3]};
+                }
+                if (h == 0) p.lse_part[(size_t)split * rows + head_row0 + row] = lse;
             }
-            if (h == 0) lp[row] = (m_run[qb] + __builtin_amdgcn_logf(l_run[qb])) * LN2;
         }
     }
+}
+
+// Merge of the key splits (the online-softmax rescale applied across ranges):
+//   LSE = ln sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s,
+// with O_s the normalised partial of split s.  One wave per (batch, head, query) row; lane
+// i handles d = 2i, 2i+1 (head dim 128) or d = i (64).
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void fa_merge_kernel(const float* o_part, const float* lse_part,
+                                                       void* o, float* lse, int rows, int num_splits) {
+    constexpr int PER = D / 64;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    constexpr float LOG2E = 1.44269504088896340736f;
+    float mx = -__builtin_inff();
+    for (int sp = 0; sp < num_splits; ++sp) mx = fmaxf(mx, lse_part[(size_t)sp * rows + row]);
+    float out[PER] = {};
+    float total = 0.0f;
+    if (mx != -__builtin_inff()) {
+        for (int sp = 0; sp < num_splits; ++sp) {
+            const float ls = lse_part[(size_t)sp * rows + row];
+            const float wgt = ls == -__builtin_inff() ? 0.0f : fast_exp2((ls - mx) * LOG2E);
+            total += wgt;
+            const float* src = o_part + ((size_t)sp * rows + row) * D + lane * PER;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) out[e] += wgt * src[e];
+        }
+    }
+    const float inv = total > 0.0f ? __builtin_amdgcn_rcpf(total) : 0.0f;
+    uint16_t* orow = (uint16_t*)o + (size_t)row * D + lane * PER;
+    if constexpr (PER == 2) {
+        *(uint32_t*)orow = pack2<BF16>(out[0] * inv, out[1] * inv);
+    } else {
+        const uint32_t w = pack2<BF16>(out[0] * inv, 0.0f);
+        orow[0] = (uint16_t)(w & 0xffffu);
+    }
+    if (lane == 0) lse[row] = total > 0.0f ? mx + __builtin_logf(total) : -__builtin_inff();
 }
 
 }  // namespace fa

@@ -31,6 +31,10 @@ WORKLOADS = {
                                         dtype="bf16", causal=True, input_pos=0),
     "gqa4_prefill_q1024_kv16384_d128_bf16": dict(B=2, Hq=32, Hkv=8, Sq=1024, Skv=16384, D=128,
                                                   dtype="bf16", causal=True, input_pos=15360),
+    # One new token per sequence against a 16K-token cache: the under-filled grid that
+    # split-KV is for (32 workgroups unsplit).
+    "gqa4_decode_b4_kv16384_d128_bf16": dict(B=4, Hq=32, Hkv=8, Sq=1, Skv=16384, D=128,
+                                              dtype="bf16", causal=True, input_pos=16383),
 }
 
 

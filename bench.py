@@ -9,7 +9,17 @@ FLOPs are counted as 4*B*Hq*Sq*Skv*D, halved when causal.  Inputs are resident i
 before the timed region; each step is one call of the library's fa_fwd on torch's
 current stream, timed with HIP events recorded on that stream.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
+Warm-up: W untimed steps, then more untimed steps until at least MIN_WARMUP_S seconds of
+warm-up have passed.  Coming out of idle the GPU needs some tens of milliseconds to reach
+its working clock (the first ~30 launches of the headline kernel run up to 30% slower),
+so a fixed small W would time the clock ramp rather than the kernel.  The extra steps are
+reported as "warmup_extra_steps".
+
+--splitkv times fa_fwd_splitkv (the library's split count, workspace allocated before the
+timed region) instead; decoding workloads (one query row) are reported in GB/s against
+the HBM roofline, since reading K and V bounds them.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--splitkv] [--all]
 """
 
 from __future__ import annotations
@@ -31,6 +41,8 @@ HEADLINE = "gqa8_causal_s8192_d128_bf16"
 # MI355X dense bf16/fp16 MFMA peak: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU.
 PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.json")
+MIN_WARMUP_S = 0.3
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
 KERNEL_SOURCES = [os.path.join(ROOT, "attention_fa_fwd_amd", "csrc", f)
                   for f in ("fa_fwd_kernel.hpp", "fa_fwd.hip")]
 
@@ -83,7 +95,14 @@ def traffic_bytes(workload):
     return e.get("hbm_bytes_per_launch")
 
 
-def time_gpu(name, steps, warmup, config=-1):
+def algorithmic_bytes(w):
+    """q, k, v read once; out and lse written once."""
+    qo = 2 * w["B"] * w["Hq"] * w["Sq"] * w["D"] * 2
+    kv = 2 * w["B"] * w["Hkv"] * w["Skv"] * w["D"] * 2
+    return qo + kv + w["B"] * w["Hq"] * w["Sq"] * 4
+
+
+def time_gpu(name, steps, warmup, config=-1, splitkv=False):
     import torch
 
     import attention_fa_fwd_amd as fa
@@ -98,14 +117,32 @@ def time_gpu(name, steps, warmup, config=-1):
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
+    splits = 1
+    if splitkv:
+        splits = fa.splitkv_num_splits(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"],
+                                       w["causal"], w["input_pos"], q.dtype, config)
+        nbytes = fa.splitkv_workspace_size(w["B"], w["Hq"], w["Sq"], w["D"], splits)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
 
-    def step():
-        fa.fa_fwd_into(q, k, v, out, lse, scale=kw["scale"], causal=kw["causal"],
-                       input_pos=kw["input_pos"], config=config, stream=sp)
+        def step():
+            fa.fa_fwd_splitkv_into(q, k, v, out, lse, ws, num_splits=splits, scale=kw["scale"],
+                                   causal=kw["causal"], input_pos=kw["input_pos"], config=config,
+                                   stream=sp)
+    else:
+        def step():
+            fa.fa_fwd_into(q, k, v, out, lse, scale=kw["scale"], causal=kw["causal"],
+                           input_pos=kw["input_pos"], config=config, stream=sp)
 
+    t_warm = time.perf_counter()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    extra = 0
+    while time.perf_counter() - t_warm < MIN_WARMUP_S:
+        for _ in range(10):
+            step()
+        extra += 10
+        torch.cuda.synchronize()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -119,7 +156,8 @@ def time_gpu(name, steps, warmup, config=-1):
     total_ms = evs[0].elapsed_time(evs[-1])
     cfg = config if config >= 0 else fa.select_config(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"],
                                                       w["D"], w["causal"], w["input_pos"], q.dtype)
-    return dict(total_ms=total_ms, wall_s=wall, per_ms=per, kernel=fa.config_names()[cfg])
+    return dict(total_ms=total_ms, wall_s=wall, per_ms=per, kernel=fa.config_names()[cfg],
+                warmup_extra=extra, splits=splits)
 
 
 def cpu_baseline(name):
@@ -151,28 +189,43 @@ def cpu_baseline(name):
                 wall_s=round(dt, 3))
 
 
-def bench_line(name, steps, warmup, config=-1, with_cpu=True):
+def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False):
     from attention_fa_fwd_amd.inputs import WORKLOADS
 
     w = WORKLOADS[name]
     log(f"workload {name}: {w}")
-    r = time_gpu(name, steps, warmup, config)
+    r = time_gpu(name, steps, warmup, config, splitkv)
     ms_step = r["total_ms"] / steps
     flops = literal_flops(w)
     value = flops / (ms_step * 1e-3) / 1e12
     mean_kernel_ms = sum(r["per_ms"]) / len(r["per_ms"])
-    achieved = flops / (mean_kernel_ms * 1e-3) / 1e12
     med = r["per_ms"][len(r["per_ms"]) // 2]
     p95 = r["per_ms"][min(len(r["per_ms"]) - 1, int(math.ceil(0.95 * len(r["per_ms"]))) - 1)]
-    log(f"kernel {r['kernel']}: mean {mean_kernel_ms * 1e3:.1f} us, median {med * 1e3:.1f} us, "
-        f"p95 {p95 * 1e3:.1f} us, min {r['per_ms'][0] * 1e3:.1f} us")
+    path = f"fa_fwd_splitkv ({r['splits']} splits)" if splitkv else "fa_fwd"
+    log(f"{path} kernel {r['kernel']}: mean {mean_kernel_ms * 1e3:.1f} us, median {med * 1e3:.1f} us, "
+        f"p95 {p95 * 1e3:.1f} us, min {r['per_ms'][0] * 1e3:.1f} us, "
+        f"{r['warmup_extra']} extra warm-up steps")
+    decode = w["Sq"] <= 16
+    if decode:
+        # Reading K and V bounds a decoding step: GB/s of algorithmic bytes per call.
+        gbs = algorithmic_bytes(w) / (mean_kernel_ms * 1e-3) / 1e9
+        metric, value, unit = "attention decode GB/s of algorithmic HBM bytes", gbs, "GB/s"
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = flops / (mean_kernel_ms * 1e-3) / 1e12
+        metric, unit = METRIC, "TFLOP/s"
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_TFLOPS, 1),
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+                    "traffic": None if splitkv else traffic_bytes(name)}
     line = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 2),
-        "unit": "TFLOP/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
+        "warmup_extra_steps": r["warmup_extra"],
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -181,15 +234,15 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True):
         "data": "synthetic: seeded N(0,1) q, k, v rounded to the storage dtype",
         "config": {"workload": name, "B": w["B"], "Hq": w["Hq"], "Hkv": w["Hkv"], "Sq": w["Sq"],
                    "Skv": w["Skv"], "D": w["D"], "causal": w["causal"],
-                   "input_pos": w["input_pos"], "kernel": r["kernel"], "parallelism": "single GPU"},
-        "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2),
-        "tflops_exact_pairs": round(exact_flops(w) / (ms_step * 1e-3) / 1e12, 2),
+                   "input_pos": w["input_pos"], "kernel": r["kernel"], "path": path,
+                   "parallelism": "single GPU"},
         "kernel_us": {"mean": round(mean_kernel_ms * 1e3, 2), "median": round(med * 1e3, 2),
                       "p95": round(p95 * 1e3, 2), "min": round(r["per_ms"][0] * 1e3, 2)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_TFLOPS, 1),
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
-                     "traffic": traffic_bytes(name)},
+        "roofline": roofline,
     }
+    if not decode:
+        line["pct_of_peak"] = round(100.0 * value / PEAK_TFLOPS, 2)
+        line["tflops_exact_pairs"] = round(exact_flops(w) / (ms_step * 1e-3) / 1e12, 2)
     if with_cpu:
         log("timing the fp64 CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(name)
@@ -216,11 +269,13 @@ def calibrate_copy(reps=3):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--config", type=int, default=-1, help="force a kernel configuration id")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--splitkv", action="store_true",
+                    help="time fa_fwd_splitkv with the library's split count")
     ap.add_argument("--all", action="store_true",
                     help="also time every named workload (extra JSON lines on stderr)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -236,13 +291,17 @@ def main(argv=None):
     if a.steps < 1 or a.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
-    line = bench_line(a.workload, a.steps, a.warmup, a.config, with_cpu=not a.no_cpu_baseline)
+    line = bench_line(a.workload, a.steps, a.warmup, a.config, with_cpu=not a.no_cpu_baseline,
+                      splitkv=a.splitkv)
     if a.all:
         from attention_fa_fwd_amd.inputs import WORKLOADS
 
         for name in WORKLOADS:
-            if name != a.workload:
-                extra = bench_line(name, a.steps, a.warmup, -1, with_cpu=False)
+            runs = [False, True] if WORKLOADS[name]["Sq"] <= 16 else [False]
+            for split in runs:
+                if name == a.workload and split == a.splitkv:
+                    continue
+                extra = bench_line(name, a.steps, a.warmup, -1, with_cpu=False, splitkv=split)
                 print("[bench-extra] " + json.dumps(extra), file=sys.stderr, flush=True)
     print(json.dumps(line), flush=True)
     return 0

@@ -21,18 +21,21 @@
  * move 128-bit vectors); lse must be 4-byte aligned.  out and lse must not overlap the
  * inputs or each other.
  *
- * Ownership: the caller owns every buffer.  The library allocates nothing, keeps no state
- * besides constant tables, and may be called from several host threads at once.
+ * Ownership: the caller owns every buffer (including fa_fwd_splitkv's workspace).  The
+ * library allocates nothing, keeps no state besides constant tables, and may be called
+ * from several host threads at once.
  *
- * Asynchrony: the call validates its arguments on the host (no HIP call), enqueues one
- * kernel on `stream` (a hipStream_t passed as void*; NULL = the null stream) and returns
- * without synchronising.  Faults inside the kernel surface on the next synchronisation.
+ * Asynchrony: the call validates its arguments on the host (no HIP call), enqueues its
+ * kernel (fa_fwd_splitkv: two kernels) on `stream` (a hipStream_t passed as void*; NULL =
+ * the null stream) and returns without synchronising.  Faults inside the kernel surface on the next synchronisation.
  *
  * Errors: a nonzero return leaves out and lse untouched and launches nothing, except
  * FA_ERR_LAUNCH, which reports a failed launch.  Checks run in the order of the codes below.
  */
 #ifndef FA_FWD_H
 #define FA_FWD_H
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -57,7 +60,9 @@ enum fa_status {
     FA_ERR_MISALIGNED = -8,           /* q/k/v/out not 16-byte or lse not 4-byte aligned      */
     FA_ERR_ALIAS = -9,                /* out or lse overlaps an input or each other           */
     FA_ERR_INVALID_CONFIG = -10,      /* fa_fwd_config: config id unknown or not applicable  */
-    FA_ERR_LAUNCH = -11               /* the kernel launch failed (hipGetLastError)           */
+    FA_ERR_LAUNCH = -11,              /* the kernel launch failed (hipGetLastError)           */
+    FA_ERR_INVALID_SPLITS = -12,      /* fa_fwd_splitkv: num_splits outside 0..256            */
+    FA_ERR_WORKSPACE = -13            /* fa_fwd_splitkv: workspace_bytes too small            */
 };
 
 /*
@@ -88,6 +93,52 @@ int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
 int fa_fwd_config(const void* q, const void* k, const void* v, void* out, float* lse,
                   int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
                   int causal, int input_pos, int dtype, void* stream, int config);
+
+/*
+ * Split-KV forward pass, for grids too small to fill the GPU (few heads or short query
+ * blocks; decoding with Sq = 1).  The pages motivate it by launches with too few tiles for
+ * the processors ("Tuning Flash Attention for peak performance in NVIDIA CUDA Tile", Part 2
+ * "Autotuning"; "How I Beat PyTorch's Flash Attention", "Phase 5: Adaptive Tile
+ * Dispatch"); they do not split the key loop, this library does: the visible key tiles of
+ * each query tile are cut into num_splits tile-aligned ranges, each handled by its own
+ * workgroup, which writes the range's normalised partial output O_s (fp32) and LSE_s.  A
+ * second kernel merges them with the online-softmax rescale of the cuTile post ("Online
+ * softmax update") applied across ranges:
+ *     LSE = ln sum_s exp(LSE_s),   out = sum_s exp(LSE_s - LSE) O_s
+ * (a range with no visible key has LSE_s = -inf and weight 0).  The result is the same
+ * attention as fa_fwd up to rounding order; out is rounded to `dtype` once, after the merge.
+ *
+ *   q .. dtype       as for fa_fwd.
+ *   num_splits       0 = choose (fa_splitkv_num_splits), 1 = no split (same kernels as
+ *                    fa_fwd; workspace unused, may be NULL), 2..256 = that many ranges.
+ *                    Ranges beyond the number of key tiles are empty and harmless.
+ *   config           as for fa_fwd_config; -1 = the dispatch table.
+ *   workspace        device memory of >= fa_splitkv_workspace_size(B, Hq, Sq, D, splits)
+ *                    bytes, 16-byte aligned, owned by the caller, overlapping no tensor.
+ *                    Its contents on entry do not matter; on return it holds the partials.
+ *                    Two calls in flight at once need two workspaces.
+ *   workspace_bytes  size of workspace.
+ *   stream           both kernels are enqueued on it, in order; no synchronisation.
+ * Checks: those of fa_fwd_config, then num_splits (FA_ERR_INVALID_SPLITS), then -- only
+ * when more than one split runs and B*Hq*Sq > 0 -- workspace NULL (FA_ERR_NULL_POINTER),
+ * misaligned (FA_ERR_MISALIGNED), too small (FA_ERR_WORKSPACE), overlapping (FA_ERR_ALIAS).
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
+                   int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+                   int causal, int input_pos, int dtype, int num_splits, int config,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Split count fa_fwd_splitkv uses for num_splits = 0: 1 when the plain grid has at least
+ * one workgroup per CU (256); else enough ranges for about 512 workgroups, capped so that
+ * each range has >= 8 key tiles, the fp32 partials' traffic stays within the K/V bytes,
+ * and there are at most 256 ranges.  Negative fa_status on invalid sizes. */
+int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                          int input_pos, int dtype, int config);
+
+/* Workspace bytes fa_fwd_splitkv needs for num_splits ranges:
+ * num_splits * B * Hq * Sq * (D + 1) * 4 (fp32 partial O, then fp32 partial LSE), 0 when
+ * num_splits <= 1, the problem is empty or D is unsupported. */
+size_t fa_splitkv_workspace_size(int B, int Hq, int Sq, int D, int num_splits);
 
 /* Configuration the dispatch table picks for these arguments, or a negative fa_status. */
 int fa_select_config(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,

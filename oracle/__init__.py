@@ -8,6 +8,7 @@ from .attention import (  # noqa: F401
     LN2,
     LOG2E,
     attention_blocked,
+    attention_key_range,
     attention_naive,
     attention_online_tiled,
     attention_probs_naive,
@@ -15,5 +16,6 @@ from .attention import (  # noqa: F401
     classify_tiles,
     kv_head_of,
     key_visibility,
+    merge_partials,
     tile_plan,
 )

@@ -30,7 +30,7 @@ its host code ("Launching the kernel: Host-side code").  The log-sum-exp output
 is on no page; it is read as the natural-log log-sum-exp of the scaled, masked
 scores of each row.
 
-Three forms are provided, written independently of one another:
+Four forms are provided, written independently of one another:
 
 * ``attention_naive``          pure-Python loops over the definition (tiny shapes);
 * ``attention_blocked``        the definition with NumPy matmuls, row block by row
@@ -38,6 +38,9 @@ Three forms are provided, written independently of one another:
 * ``attention_online_tiled``   the tile-by-tile online-softmax algorithm of the
                                [cuTile] kernel, with its loop bound, K-loop split,
                                exp2 domain and rescaling, in float64.
+* ``attention_key_range`` and ``merge_partials``: the definition over one key
+                               range, and the online-softmax fold of several ranges
+                               into one result (split-KV).
 
 Parity status: every function here is pinned by the CPU test suite against
 brute force, an independent library routine (PyTorch's CPU float64
@@ -384,3 +387,78 @@ def attention_online_tiled(q, k, v, scale, causal=False, input_pos=0, tile_m=64,
                 O[b, head, rows[valid]] = out[valid]
                 L[b, head, rows[valid]] = lse[valid]
     return O, L
+
+
+# ----------------------------------------------------------------------------
+# Form (iv): attention over a key range, and the merge of ranges (split-KV)
+# ----------------------------------------------------------------------------
+
+def attention_key_range(q, k, v, scale, causal, input_pos, key_lo, key_hi):
+    """The definition with each row's visible keys cut to key_lo <= j < key_hi.
+
+    The pages split the work over query tiles only; splitting the key loop is
+    the answer here to launches with too few query tiles to fill the GPU
+    ([cuTile] Part 2 "Autotuning", [Journey] "Phase 5: Adaptive Tile
+    Dispatch").  Each range is the module-docstring definition over V(i)
+    intersected with [key_lo, key_hi).  Returns (O_s [B,Hq,Sq,D], LSE_s
+    [B,Hq,Sq]) as float64; a row with no visible key in the range gets
+    O_s = 0 and LSE_s = -inf (the log of an empty sum).
+    """
+    B, Hq, Hkv, Sq, Skv, D = _shapes(q, k, v)
+    if not (math.isfinite(scale) and scale > 0):
+        raise ValueError("scale must be finite and > 0")
+    O = np.zeros((B, Hq, Sq, D))
+    L = np.full((B, Hq, Sq), -np.inf)
+    in_range = (np.arange(Skv) >= key_lo) & (np.arange(Skv) < key_hi)
+    vis = key_visibility(np.arange(Sq), Skv, causal, input_pos) & in_range[None, :]
+    rows = np.nonzero(vis.any(axis=1))[0]
+    if rows.size == 0:
+        return O, L
+    for b in range(B):
+        for hq in range(Hq):
+            g = kv_head_of(hq, Hq, Hkv)
+            kh = np.asarray(k[b, g], np.float64)
+            vh = np.asarray(v[b, g], np.float64)
+            s = scaled_scores(np.asarray(q[b, hq, rows], np.float64), kh, scale)
+            m, e, l = masked_softmax_stats(s, vis[rows])
+            O[b, hq, rows] = normalise(e, l, vh)
+            L[b, hq, rows] = log_sum_exp(m, l)
+    return O, L
+
+
+def merge_partials(o_parts, lse_parts):
+    """Fold per-range results (O_s, LSE_s) into the attention over all the ranges.
+
+    This is the [cuTile] online-softmax update (Part 1 "Online softmax update",
+    "Accumulating the output", "Final normalization and store") with whole key
+    ranges in place of K/V tiles, in natural-log units.  A range enters as the
+    state (m, l, acc) = (LSE_s, 1, O_s): after a range the kernel holds m and l
+    with m + ln l = LSE_s and acc / l = O_s, and scaling l and acc by one
+    common factor changes neither O nor LSE.  For each range in turn:
+
+        m_new = max(m, LSE_s);  alpha = exp(m - m_new);  beta = exp(LSE_s - m_new)
+        l = alpha * l + beta;   acc = alpha * acc + beta * O_s;   m = m_new
+
+    and at the end O = acc / l, LSE = m + ln l.  A range with LSE_s = -inf (no
+    visible key) has weight 0; when every range is empty, O = 0, LSE = -inf.
+
+    o_parts: [S, ..., D]; lse_parts: [S, ...].  Returns (O [..., D], LSE [...]).
+    """
+    o_parts = np.asarray(o_parts, np.float64)
+    lse_parts = np.asarray(lse_parts, np.float64)
+    m = np.full(lse_parts.shape[1:], -np.inf)
+    l = np.zeros(lse_parts.shape[1:])
+    acc = np.zeros(o_parts.shape[1:])
+    for o_s, lse_s in zip(o_parts, lse_parts):
+        m_new = np.maximum(m, lse_s)
+        live = m_new > -np.inf               # some range so far has a visible key
+        safe = np.where(live, m_new, 0.0)
+        alpha = np.where(live, np.exp(m - safe), 1.0)
+        beta = np.where(live, np.exp(lse_s - safe), 0.0)
+        l = alpha * l + beta
+        acc = alpha[..., None] * acc + beta[..., None] * o_s
+        m = m_new
+    nonempty = l > 0
+    O = np.where(nonempty[..., None], acc / np.where(nonempty, l, 1.0)[..., None], 0.0)
+    LSE = np.where(nonempty, m + np.log(np.where(nonempty, l, 1.0)), -np.inf)
+    return O, LSE

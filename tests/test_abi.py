@@ -138,3 +138,66 @@ def test_binding_rejects_cpu_tensors():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         fa.load_library(str(tmp_path / "missing.so"))
+
+
+# --- split-KV entry points -----------------------------------------------------------
+
+W = 6 * P   # fake workspace address, 16-byte aligned, clear of every tensor
+
+
+def call_split(lib, num_splits=2, config=-1, ws=W, ws_bytes=1 << 28, **over):
+    a = dict(GOOD, **over)
+    return lib.fa_fwd_splitkv(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                              a["Sq"], a["Skv"], a["D"], a["scale"], a["causal"], a["input_pos"],
+                              a["dtype"], num_splits, config, ws, ws_bytes, None)
+
+
+def test_splitkv_workspace_size(lib):
+    assert fa.splitkv_workspace_size(1, 32, 1024, 128, 2) == 2 * 32 * 1024 * 129 * 4
+    assert fa.splitkv_workspace_size(2, 3, 5, 64, 7) == 7 * 2 * 3 * 5 * 65 * 4
+    assert fa.splitkv_workspace_size(1, 32, 1024, 128, 1) == 0
+    assert fa.splitkv_workspace_size(1, 32, 1024, 128, 0) == 0
+    assert fa.splitkv_workspace_size(0, 32, 1024, 128, 4) == 0
+    assert fa.splitkv_workspace_size(1, 32, 1024, 96, 4) == 0
+
+
+def test_splitkv_auto_split_count(lib):
+    # A grid with a workgroup per CU is not split (256 workgroups at 1024 tokens, and the
+    # full causal 8K grid); decoding (8 workgroups) is split to ~512 workgroups; ranges
+    # keep >= 8 key tiles; a small prefill (128 workgroups) is not split because its fp32
+    # partials would move more bytes than its K/V.
+    assert fa.splitkv_num_splits(1, 32, 32, 1024, 1024, 128, False, 0, 0) == 1
+    assert fa.splitkv_num_splits(1, 32, 4, 8192, 8192, 128, True, 0, 1) == 1
+    assert fa.splitkv_num_splits(1, 32, 4, 1, 16384, 128, True, 16383, 1) == 64
+    assert fa.splitkv_num_splits(4, 32, 8, 1, 16384, 128, True, 16383, 1) == 16
+    assert fa.splitkv_num_splits(16, 32, 8, 1, 4096, 128, True, 4095, 1) == 4
+    assert fa.splitkv_num_splits(1, 1, 1, 1, 64, 128, True, 63, 1) == 1     # 2 tiles: too short
+    assert fa.splitkv_num_splits(1, 1, 1, 1, 4096, 64, False, 0, 0) == 4096 // 64 // 8
+    assert fa.splitkv_num_splits(1, 8, 8, 2048, 2048, 128, True, 0, 0) == 1
+    with pytest.raises(fa.FaError):
+        fa.splitkv_num_splits(1, 3, 2, 1, 64, 128, True, 0, 1)
+
+
+@pytest.mark.parametrize("over,kw,code", [
+    (dict(Hq=3), {}, -3),                                    # fa_fwd's checks come first
+    ({}, dict(config=10 ** 6), -10),
+    ({}, dict(num_splits=-1), -12), ({}, dict(num_splits=257), -12),
+    ({}, dict(ws=0), -1),
+    ({}, dict(ws=W + 8), -8),
+    ({}, dict(ws_bytes=2 * 4 * 8 * 65 * 4 - 1), -13),
+    ({}, dict(ws=O - 64), -9), ({}, dict(ws=L), -9), ({}, dict(ws=Q + 16), -9),
+])
+def test_splitkv_validation(lib, over, kw, code):
+    assert call_split(lib, **kw, **over) == code
+
+
+def test_splitkv_validation_order_and_noops(lib):
+    assert call_split(lib, num_splits=-1, ws=0, D=96) == -4
+    assert call_split(lib, num_splits=300, ws=0) == -12
+    # empty problems launch nothing and need no workspace
+    assert call_split(lib, Sq=0, ws=0, ws_bytes=0) == 0
+    assert call_split(lib, B=0, ws=0, ws_bytes=0, num_splits=0) == 0
+    # exactly the documented workspace size is enough to pass validation; the call would
+    # then launch, which needs a GPU, so only the size rule is checked here
+    need = fa.splitkv_workspace_size(1, 4, 8, 64, 2)
+    assert call_split(lib, ws_bytes=need - 1) == -13

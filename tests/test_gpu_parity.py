@@ -112,7 +112,7 @@ def test_named_workload(name):
     rng = np.random.default_rng(1)
     B, Hq, Sq = w["B"], w["Hq"], w["Sq"]
     rows = {0, 1, 31, 32, 63, 64, 127, 128, 255, 256, Sq // 2, Sq - 2, Sq - 1}
-    samples = [(int(rng.integers(B)), int(rng.integers(Hq)), i) for i in sorted(rows) if i < Sq]
+    samples = [(int(rng.integers(B)), int(rng.integers(Hq)), i) for i in sorted(rows) if 0 <= i < Sq]
     samples += [(int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(Sq)))
                 for _ in range(48)]
     samples += [(B - 1, Hq - 1, Sq - 1), (0, 0, 0)]
