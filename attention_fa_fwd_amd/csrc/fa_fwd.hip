@@ -60,12 +60,13 @@ hipError_t launch_cfg(const Params& p, hipStream_t s) {
     FA_ENTRY(128, 32, 1, 1, 4, CAUSAL, BF16, CNAME, TNAME),        \
     FA_ENTRY(128, 32, 1, 2, 4, CAUSAL, BF16, CNAME, TNAME),        \
     FA_ENTRY(128, 32, 1, 2, 2, CAUSAL, BF16, CNAME, TNAME),        \
+    FA_ENTRY(128, 32, 1, 4, 2, CAUSAL, BF16, CNAME, TNAME),        \
     FA_ENTRY(128, 32, 1, 4, 1, CAUSAL, BF16, CNAME, TNAME),        \
     FA_ENTRY(128, 32, 1, 8, 1, CAUSAL, BF16, CNAME, TNAME)
 
+// Head dim 128 uses 32-key tiles only: with three LDS buffers and three register sets a
+// 64-key tile no longer fits two waves per SIMD.
 const ConfigEntry kConfigs[] = {
-    FA_TILES(128, 1, 1, "causal", "bf16"), FA_TILES(128, 0, 1, "full", "bf16"),
-    FA_TILES(128, 1, 0, "causal", "fp16"), FA_TILES(128, 0, 0, "full", "fp16"),
     FA_TILES(64, 1, 1, "causal", "bf16"),  FA_TILES(64, 0, 1, "full", "bf16"),
     FA_TILES(64, 1, 0, "causal", "fp16"),  FA_TILES(64, 0, 0, "full", "fp16"),
     FA_TILES_BN32(1, 1, "causal", "bf16"), FA_TILES_BN32(0, 1, "full", "bf16"),
@@ -146,23 +147,39 @@ int find(int D, int bf16, int causal, int BN, int QB, int WPH, int HPW) {
     return -1;
 }
 
-// The dispatch rule, from a sweep of every configuration on the named workloads: 32-key
-// tiles for head dim 128 (fewer live registers, so the pipelined loop hides more latency),
-// 64-key tiles for head dim 64.  Grouped-query problems pack 4 query heads of a group into
-// one workgroup, so each K/V tile is read once for all of them; groups of 2 pack 2 heads;
-// the rest use 128 positions of one head.  Two 4-wave workgroups share a CU.
+// Workgroups of the unsplit grid of configuration c.
+long long grid_of(const ConfigEntry& c, int B, int Hq, int Hkv, int Sq) {
+    const int bmp = 32 * c.QB * c.WPH;
+    return (long long)((Sq + bmp - 1) / bmp) * (Hq / Hkv / c.HPW) * B * Hkv;
+}
+
+// The dispatch rule, from a sweep of every configuration on the named workloads (timed
+// after the GPU has reached its working clock): 32-key tiles for head dim 128 (fewer live
+// registers, so the pipelined loop hides more latency), 64-key tiles for head dim 64.
+// Grouped-query problems pack 4 (or 2) query heads of a group into one workgroup, so each
+// K/V tile is read once for all of them.  An 8-wave workgroup (a whole CU: its K/V tiles
+// shared by twice the waves) beats two 4-wave ones when it still forms at least one
+// workgroup per CU; smaller grids use 4-wave workgroups for more of them.
 int select(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal, int input_pos, int dtype) {
-    (void)B;
-    (void)Sq;
     (void)Skv;
     (void)input_pos;
     const int bf16 = dtype == FA_DTYPE_BF16;
     const int cz = causal != 0;
     const int group = Hq / Hkv;
     const int bn = D == 128 ? 32 : 64;
-    if (group % 4 == 0) return find(D, bf16, cz, bn, 1, 1, 4);
-    if (group % 2 == 0) return find(D, bf16, cz, bn, 1, 2, 2);
-    return find(D, bf16, cz, bn, 1, 4, 1);
+    int big, small;
+    if (group % 4 == 0) {
+        big = find(D, bf16, cz, bn, 1, 2, 4);
+        small = find(D, bf16, cz, bn, 1, 1, 4);
+    } else if (group % 2 == 0) {
+        big = find(D, bf16, cz, bn, 1, 4, 2);
+        small = find(D, bf16, cz, bn, 1, 2, 2);
+    } else {
+        big = find(D, bf16, cz, bn, 1, 8, 1);
+        small = find(D, bf16, cz, bn, 1, 4, 1);
+    }
+    if (big >= 0 && grid_of(kConfigs[big], B, Hq, Hkv, Sq) >= kNumCUs) return big;
+    return small;
 }
 
 // Workgroup -> XCD mapping.  The hardware hands workgroup w to XCD w % 8.  Mode 1 gives
@@ -218,11 +235,6 @@ int resolve_config(int config, int B, int Hq, int Hkv, int Sq, int Skv, int D, i
     if (config < 0) return FA_ERR_INVALID_CONFIG;
     if (!applicable(kConfigs[config], Hq, Hkv, D, causal, dtype)) return FA_ERR_INVALID_CONFIG;
     return config;
-}
-
-long long grid_of(const ConfigEntry& c, int B, int Hq, int Hkv, int Sq) {
-    const int bmp = 32 * c.QB * c.WPH;
-    return (long long)((Sq + bmp - 1) / bmp) * (Hq / Hkv / c.HPW) * B * Hkv;
 }
 
 // num_splits: 1 = the plain forward pass (out / lse written by the attention kernel);

@@ -24,14 +24,16 @@
 //    of 16 lanes, lane i receives element (i mod 4) of the 8-byte rows addressed by lanes
 //    4j + i/4, j = 0..3.  The d-order of the fragments is chosen so that each lane ends
 //    with 16 consecutive d of its query (two 128-bit stores per 32-wide block).
-//  * K and V tiles are double-buffered in LDS and move there straight from HBM with
-//    gfx950's 128-bit buffer loads to LDS: no staging registers, no LDS write instructions.
-//    The buffer range ends at key Skv, so a ragged key tail lands as zeros.  The K loop is
-//    a three-stage software pipeline: step j issues the MFMAs of S(j+1) in the same block as the
-//    softmax of tile j together with the P V of tile j-1, so all matrix work of a step is
-//    independent of its exp2 work and can overlap it; K is loaded two tiles ahead and V
-//    one tile ahead of its use, in the same two-buffer LDS footprint.  16-byte chunks are XOR-swizzled per
-//    row so that tile writes, K operand reads and V transpose reads are bank-conflict free.
+//  * K and V tiles are triple-buffered in LDS and move there straight from HBM with
+//    gfx950's 128-bit buffer loads to LDS: no staging registers, no LDS write instructions
+//    (staging through registers measured 5% slower).  The buffer range ends at key Skv,
+//    so a ragged key tail lands as zeros.  The K loop is a three-stage software pipeline:
+//    step j issues the MFMAs of S(j+1) in the same block as the softmax of tile j together
+//    with the P V of tile j-1, so all matrix work of a step is independent of its exp2 work
+//    and can overlap it.  K is loaded three tiles and V two tiles ahead of their use, so a
+//    load has two steps to land; each step waits only for the previous step's loads.
+//    16-byte chunks are XOR-swizzled per row so that tile writes, K operand reads and V
+//    transpose reads are bank-conflict free.
 //  * Register use is held to 256 per lane so that two waves share each SIMD: one wave's
 //    softmax and memory latency overlap the other's MFMAs.
 //  * The running max is kept lazily: p = exp2(c s - m) is computed with the current m and
@@ -59,6 +61,10 @@
 #include <type_traits>
 
 namespace fa {
+
+// The K-loop lambdas must be inlined: an outlined step is a call with its state on the
+// stack (private memory), several times slower.
+#define FA_INLINE __attribute__((always_inline))
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -314,13 +320,19 @@ void fa_fwd_kernel(Params p) {
         for (int db = 0; db < DB; ++db) acc[db][qb] = (f32x16){};
     }
 
-    // LDS: K(j) lives in k_lds[j%2] and V(j) in v_lds[j%2].  Four separate arrays, so the
-    // compiler can tell a direct-to-LDS load into one from reads of another and does not
-    // wait for the load before those reads; the barrier that ends each step drains it.
-    __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILE], k_lds1[TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TILE], v_lds1[TILE];
-    auto kl = [&](auto par) -> unsigned char* { return decltype(par)::value ? k_lds1 : k_lds0; };
-    auto vl = [&](auto par) -> unsigned char* { return decltype(par)::value ? v_lds1 : v_lds0; };
+    // LDS: K(t0+i) lives in k_lds[i%3] and V(t0+i) in v_lds[i%3].  Six separate arrays, so
+    // the compiler can tell a direct-to-LDS load into one from reads of another and does
+    // not wait for the load before those reads; the step-end barrier publishes it.
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILE], k_lds1[TILE], k_lds2[TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TILE], v_lds1[TILE], v_lds2[TILE];
+    auto kl = [&](auto ph) -> unsigned char* {
+        constexpr int P = decltype(ph)::value;
+        return P == 0 ? k_lds0 : P == 1 ? k_lds1 : k_lds2;
+    };
+    auto vl = [&](auto ph) -> unsigned char* {
+        constexpr int P = decltype(ph)::value;
+        return P == 0 ? v_lds0 : P == 1 ? v_lds1 : v_lds2;
+    };
 
     // Tiles move from HBM straight into LDS (buffer_load_dwordx4 ... lds): in load i, wave
     // w fills the 1 KiB of LDS at chunk slots (i*NW + w)*64 + lane, so each lane fetches
@@ -340,7 +352,7 @@ void fa_fwd_kernel(Params p) {
     // One buffer resource per tile, ending at the tile's last valid key; load i adds
     // i * LOAD_STRIDE as the scalar offset (gfx950's range check covers voffset + soffset,
     // so every load past the end of the range reads zero).
-    auto fetch = [&](const T* base, int j, unsigned char* dst, int src) {
+    auto fetch = [&](const T* base, int j, unsigned char* dst, int src) FA_INLINE {
         const int j0 = min(j * BN, kend);
         const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (size_t)j0 * D, min(kend - j0, BN) * ROWB);
 #pragma unroll
@@ -366,7 +378,7 @@ void fa_fwd_kernel(Params p) {
         voff[db] = v_lane_row * ROWB + (vq >> 1) * 8 + (((4 * db) ^ vu) << 4);
 
     // S^T = K Q^T of the tile in K buffer `kb`.
-    auto qk = [&](const unsigned char* kb, f32x16 (&s)[KB][QB]) {
+    auto qk = [&](const unsigned char* kb, f32x16 (&s)[KB][QB]) FA_INLINE {
 #pragma unroll
         for (int k2 = 0; k2 < KB; ++k2) {
 #pragma unroll
@@ -381,7 +393,7 @@ void fa_fwd_kernel(Params p) {
     };
 
     // O^T += V^T P^T for the tile whose V sits in `vb` and whose packed P is `pk`.
-    auto pv = [&](const unsigned char* vb, const u32x4 (&pk)[KB][QB][2]) {
+    auto pv = [&](const unsigned char* vb, const u32x4 (&pk)[KB][QB][2]) FA_INLINE {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -398,31 +410,45 @@ void fa_fwd_kernel(Params p) {
                     }
     };
 
-    // Register sets that alternate with the parity of j: S(j) / S(j+1) and P(j-1) / P(j).
-    f32x16 sA[KB][QB], sB[KB][QB];
-    u32x4 pkA[KB][QB][2], pkB[KB][QB][2];
-    auto pick = [](auto par, auto& a, auto& b) -> auto& {
-        if constexpr (decltype(par)::value) return b;
-        else return a;
+    // Register sets that rotate with the phase of the step: S and packed P.
+    f32x16 s0[KB][QB], s1[KB][QB], s2[KB][QB];
+    u32x4 pk0[KB][QB][2], pk1[KB][QB][2], pk2[KB][QB][2];
+    auto pick = [](auto ph, auto& a, auto& b, auto& c) -> auto& {
+        constexpr int P = decltype(ph)::value;
+        if constexpr (P == 0) return a;
+        else if constexpr (P == 1) return b;
+        else return c;
+    };
+    // End of a step: wait until this wave's loads issued one step earlier have landed
+    // (the loads of this step, 2*LD of them, may stay in flight), then the workgroup
+    // barrier.  The asm is a compiler memory barrier as well.
+    auto end_step = [&]() FA_INLINE {
+        constexpr int N = 2 * LD;
+        constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+        static_assert(N < 64, "vmcnt range");
+        asm volatile("s_waitcnt %0\n\ts_barrier" ::"n"(imm) : "memory");
     };
 
-    // One K-loop step for tile j, a three-stage software pipeline.  The step issues the
-    // MFMAs of S(j+1) = K(j+1) Q^T and of O^T += V(j-1)^T P(j-1)^T -- neither depends on
-    // this step's softmax -- in the same straight-line block as the softmax of S(j) into
-    // P(j), so all matrix work can overlap the exp2 work.  Loads: K(j+2) into k_lds[j%2]
-    // and V(j) into v_lds[j%2]; the step reads k_lds[(j+1)%2] and v_lds[(j-1)%2], so no
-    // buffer is written while it is read, and one barrier per step suffices.
-    auto step = [&](int j, auto par_tag, auto masked_tag, auto first_tag) {
-        constexpr int PAR = decltype(par_tag)::value;      // j % 2
+    // One K-loop step for tile j (phase PH = (j - t0) % 3), a three-stage software
+    // pipeline.  The step issues the MFMAs of S(j+1) = K(j+1) Q^T and of O^T += V(j-1)^T
+    // P(j-1)^T -- neither depends on this step's softmax -- in the same straight-line
+    // block as the softmax of S(j) into P(j), so all matrix work can overlap the exp2
+    // work.  Loads: K(j+3) into k_lds[PH] (K(j) was used by the previous step) and V(j+1)
+    // into v_lds[PH+1] (V(j-2) was used by the previous step); the step reads
+    // k_lds[PH+1] = K(j+1) and v_lds[PH+2] = V(j-1), so no buffer is written while it is
+    // read, and one barrier per step suffices.
+    auto step = [&](int j, auto ph_tag, auto masked_tag, auto first_tag) FA_INLINE {
+        constexpr int PH = decltype(ph_tag)::value;        // (j - t0) % 3
         constexpr bool MASKED = decltype(masked_tag)::value;
-        constexpr bool FIRST = decltype(first_tag)::value; // j == 0: no P(j-1) yet
-        using OTHER = std::integral_constant<int, PAR ^ 1>;
-        auto& s_cur = pick(par_tag, sA, sB);
-        auto& s_nxt = pick(par_tag, sB, sA);
-        auto& pk_cur = pick(par_tag, pkA, pkB);
-        auto& pk_prev = pick(par_tag, pkB, pkA);
-        fetch(kp, j + 2, kl(par_tag), ksrc);
-        fetch(vp, j, vl(par_tag), vsrc);
+        constexpr bool FIRST = decltype(first_tag)::value; // j == t0: no P(j-1) yet
+        using N1 = std::integral_constant<int, (PH + 1) % 3>;
+        using N2 = std::integral_constant<int, (PH + 2) % 3>;
+        auto& s_cur = pick(ph_tag, s0, s1, s2);
+        auto& s_nxt = pick(N1{}, s0, s1, s2);
+        auto& pk_cur = pick(ph_tag, pk0, pk1, pk2);
+        auto& pk_prev = pick(N2{}, pk0, pk1, pk2);
+        fetch(kp, j + 3, kl(ph_tag), ksrc);
+        fetch(vp, j + 1, vl(N1{}), vsrc);
         const bool do_sm = !MASKED || j < wave_tc;          // softmax of tile j
         const bool do_pv = !FIRST && (!MASKED || j - 1 < wave_tc);   // P V of tile j-1
         if (do_sm) {
@@ -443,9 +469,9 @@ void fa_fwd_kernel(Params p) {
             }
         }
         // Matrix work of this step: S(j+1), and P V of tile j-1.
-        qk(kl(OTHER{}), s_nxt);
+        qk(kl(N1{}), s_nxt);
         if constexpr (!FIRST) {
-            if (!MASKED || do_pv) pv(vl(OTHER{}), pk_prev);
+            if (!MASKED || do_pv) pv(vl(N2{}), pk_prev);
         }
         if (do_sm) {
             // P = exp2(c s - m) with the running max m, packed to the storage type, and the
@@ -453,7 +479,7 @@ void fa_fwd_kernel(Params p) {
             // packed).  Summing the rounded bf16 p instead would move LSE by ~1e-3 on rows
             // with few visible keys.
             float ts[QB];
-            auto make_p = [&]() {
+            auto make_p = [&]() FA_INLINE {
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
                     // m = -inf until the row's first visible key; meanwhile use 0, so masked
@@ -508,49 +534,57 @@ void fa_fwd_kernel(Params p) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) l_run[qb] += xhalf_sum(ts[qb]);
         }
-        __syncthreads();
+        end_step();
     };
 
-    // Prologue: K(t0) to LDS; S(t0) while K(t0+1) arrives.  Local step i handles tile t0+i
-    // and uses buffers / register sets of parity i % 2.
-    using P0 = std::integral_constant<int, 0>;
-    using P1 = std::integral_constant<int, 1>;
+    // Prologue: K(t0), K(t0+1), K(t0+2) and V(t0) to LDS; S(t0) once K(t0) has landed.
+    // Local step i handles tile t0+i with buffers and register sets of phase i % 3.
+    using Q0 = std::integral_constant<int, 0>;
+    using Q1 = std::integral_constant<int, 1>;
+    using Q2 = std::integral_constant<int, 2>;
     using F = std::false_type;
     using TT = std::true_type;
     if (nt > 0) {
         fetch(kp, t0, k_lds0, ksrc);
-        __syncthreads();
         fetch(kp, t0 + 1, k_lds1, ksrc);
-        qk(k_lds0, sA);
-        __syncthreads();
+        fetch(kp, t0 + 2, k_lds2, ksrc);
+        fetch(vp, t0, v_lds0, vsrc);
+        {
+            constexpr int N = 3 * LD;   // K(t0) landed; the other three tiles may be in flight
+            constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+            asm volatile("s_waitcnt %0\n\ts_barrier" ::"n"(imm) : "memory");
+        }
+        qk(k_lds0, s0);
+        end_step();   // K(t0+1) and K(t0+2) landed
 
         // The K loop in two parts (K-loop split): tiles needing no mask, then the diagonal /
-        // key-tail tiles.  Unrolled by two so the parity of i -- buffers and register roles
-        // -- is fixed at compile time in every copy of the step.
-        if (nf > 0) step(t0, P0{}, F{}, TT{});
-        else step(t0, P0{}, TT{}, TT{});
+        // key-tail tiles.  Unrolled by three so the phase of i -- buffers and register
+        // roles -- is fixed at compile time in every copy of the step.
+        if (nf > 0) step(t0, Q0{}, F{}, TT{});
+        else step(t0, Q0{}, TT{}, TT{});
         int i = 1;
-        for (; i + 1 < nf; i += 2) {
-            step(t0 + i, P1{}, F{}, F{});
-            step(t0 + i + 1, P0{}, F{}, F{});
-        }
-        if (i < nf) {
-            step(t0 + i, P1{}, F{}, F{});
-            ++i;
-        }
-        if (i < nt && (i & 1)) {
-            step(t0 + i, P1{}, TT{}, F{});
-            ++i;
-        }
-        for (; i + 1 < nt; i += 2) {
-            step(t0 + i, P0{}, TT{}, F{});
-            step(t0 + i + 1, P1{}, TT{}, F{});
-        }
-        if (i < nt) step(t0 + i, P0{}, TT{}, F{});
-        // Drain: P V of the last tile (its V arrived during the last step).
+        auto run = [&](int end, auto masked) FA_INLINE {
+            if (i < end && i % 3 == 1) { step(t0 + i, Q1{}, masked, F{}); ++i; }
+            if (i < end && i % 3 == 2) { step(t0 + i, Q2{}, masked, F{}); ++i; }
+            for (; i + 2 < end; i += 3) {
+                step(t0 + i, Q0{}, masked, F{});
+                step(t0 + i + 1, Q1{}, masked, F{});
+                step(t0 + i + 2, Q2{}, masked, F{});
+            }
+            if (i < end) { step(t0 + i, Q0{}, masked, F{}); ++i; }
+            if (i < end) { step(t0 + i, Q1{}, masked, F{}); ++i; }
+        };
+        run(nf, F{});
+        run(nt, TT{});
+        // The last steps issued loads past the range (zero-size, landing as zeros): let
+        // them land before the workgroup can end and its LDS be reused.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // Drain: P V of the last tile (its V landed by the end of the last step).
         if (t1 - 1 < wave_tc) {
-            if ((nt - 1) & 1) pv(v_lds1, pkB);
-            else pv(v_lds0, pkA);
+            const int ph = (nt - 1) % 3;
+            if (ph == 0) pv(v_lds0, pk0);
+            else if (ph == 1) pv(v_lds1, pk1);
+            else pv(v_lds2, pk2);
         }
     }
 
