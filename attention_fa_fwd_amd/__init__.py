@@ -44,9 +44,12 @@ def _declare(lib):
     lib.fa_fwd.restype = _c_int
     lib.fa_fwd_config.argtypes = _FWD_ARGS + [_c_int]
     lib.fa_fwd_config.restype = _c_int
-    lib.fa_fwd_splitkv.argtypes = _FWD_ARGS[:-1] + [_c_int, _c_int, _vp, ctypes.c_size_t, _vp]
+    lib.fa_fwd_window.argtypes = _FWD_ARGS[:12] + [_c_int, _c_int, _c_int, _vp, _c_int]
+    lib.fa_fwd_window.restype = _c_int
+    lib.fa_fwd_splitkv.argtypes = _FWD_ARGS[:14] + [_c_int, _c_int, _c_int, _c_int, _vp,
+                                                    ctypes.c_size_t, _vp]
     lib.fa_fwd_splitkv.restype = _c_int
-    lib.fa_splitkv_num_splits.argtypes = [_c_int] * 10
+    lib.fa_splitkv_num_splits.argtypes = [_c_int] * 11
     lib.fa_splitkv_num_splits.restype = _c_int
     lib.fa_splitkv_workspace_size.argtypes = [_c_int] * 5
     lib.fa_splitkv_workspace_size.restype = ctypes.c_size_t
@@ -121,11 +124,19 @@ def _check_tensors(q, k, v, out, lse):
     return B, Hq, Hkv, Sq, Skv, D
 
 
-def fa_fwd_into(q, k, v, out, lse, scale=None, causal=True, input_pos=0, config=-1, stream=None):
+def _check_window(causal, window):
+    if window < 0 or (window > 0 and not causal):
+        raise ValueError("window must be >= 0 and a sliding window needs causal=True")
+
+
+def fa_fwd_into(q, k, v, out, lse, scale=None, causal=True, input_pos=0, config=-1, stream=None,
+                window=0):
     """Run the kernel into caller-provided ``out`` [B,Hq,Sq,D] and ``lse`` [B,Hq,Sq] (fp32).
 
     All tensors must be contiguous and on the same GPU.  ``stream`` is a raw
     hipStream_t value; by default torch's current stream on q's device.
+    ``window`` > 0 restricts causal attention to a sliding window of that many keys
+    (query i sees keys input_pos + i - window + 1 .. input_pos + i; fa_fwd_window).
     """
     import torch
 
@@ -135,20 +146,27 @@ def fa_fwd_into(q, k, v, out, lse, scale=None, causal=True, input_pos=0, config=
         scale = 1.0 / math.sqrt(D)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check_window(causal, window)
     with torch.cuda.device(q.device):
-        rc = lib.fa_fwd_config(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                               lse.data_ptr(), B, Hq, Hkv, Sq, Skv, D, float(scale),
-                               1 if causal else 0, int(input_pos), _dtype_code(q.dtype),
-                               stream, int(config))
+        if window > 0:
+            rc = lib.fa_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), B, Hq, Hkv, Sq, Skv, D, float(scale),
+                                   int(input_pos), int(window), _dtype_code(q.dtype), stream,
+                                   int(config))
+        else:
+            rc = lib.fa_fwd_config(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), B, Hq, Hkv, Sq, Skv, D, float(scale),
+                                   1 if causal else 0, int(input_pos), _dtype_code(q.dtype),
+                                   stream, int(config))
     _check(rc)
     return out, lse
 
 
-def splitkv_num_splits(B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype, config=-1) -> int:
+def splitkv_num_splits(B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype, config=-1, window=0) -> int:
     """Split count fa_fwd_splitkv picks for num_splits=0 (dtype: torch dtype or FA code)."""
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
     rc = load_library().fa_splitkv_num_splits(B, Hq, Hkv, Sq, Skv, D, 1 if causal else 0,
-                                              input_pos, code, config)
+                                              input_pos, window, code, config)
     _check(rc if rc < 0 else 0)
     return rc
 
@@ -159,7 +177,7 @@ def splitkv_workspace_size(B, Hq, Sq, D, num_splits) -> int:
 
 
 def fa_fwd_splitkv_into(q, k, v, out, lse, workspace, num_splits=0, scale=None, causal=True,
-                        input_pos=0, config=-1, stream=None):
+                        input_pos=0, config=-1, stream=None, window=0):
     """Split-KV forward into caller-provided ``out``, ``lse`` and ``workspace``.
 
     ``workspace`` is a contiguous GPU tensor of at least
@@ -183,13 +201,15 @@ def fa_fwd_splitkv_into(q, k, v, out, lse, workspace, num_splits=0, scale=None, 
     with torch.cuda.device(q.device):
         rc = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                 lse.data_ptr(), B, Hq, Hkv, Sq, Skv, D, float(scale),
-                                1 if causal else 0, int(input_pos), _dtype_code(q.dtype),
-                                int(num_splits), int(config), ws_ptr, ws_bytes, stream)
+                                1 if causal else 0, int(input_pos), int(window),
+                                _dtype_code(q.dtype), int(num_splits), int(config), ws_ptr,
+                                ws_bytes, stream)
     _check(rc)
     return out, lse
 
 
-def fa_fwd_splitkv(q, k, v, scale=None, causal=True, input_pos=0, num_splits=0, config=-1):
+def fa_fwd_splitkv(q, k, v, scale=None, causal=True, input_pos=0, num_splits=0, config=-1,
+                   window=0):
     """Split-KV attention forward: the same result as ``fa_fwd`` (up to rounding order),
     computed over ``num_splits`` key ranges (0 = the library's choice) and merged.
     Allocates the workspace with torch; returns (out, lse)."""
@@ -199,16 +219,17 @@ def fa_fwd_splitkv(q, k, v, scale=None, causal=True, input_pos=0, num_splits=0, 
     B, Hq, Sq, D = q.shape
     _, Hkv, Skv, _ = k.shape
     if num_splits == 0:
-        num_splits = splitkv_num_splits(B, Hq, Hkv, Sq, Skv, D, causal, input_pos, q.dtype, config)
+        num_splits = splitkv_num_splits(B, Hq, Hkv, Sq, Skv, D, causal, input_pos, q.dtype, config,
+                                        window)
     nbytes = splitkv_workspace_size(B, Hq, Sq, D, num_splits)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     return fa_fwd_splitkv_into(q, k, v, out, lse, ws, num_splits=num_splits, scale=scale,
-                               causal=causal, input_pos=input_pos, config=config)
+                               causal=causal, input_pos=input_pos, config=config, window=window)
 
 
-def fa_fwd(q, k, v, scale=None, causal=True, input_pos=0, config=-1):
+def fa_fwd(q, k, v, scale=None, causal=True, input_pos=0, config=-1, window=0):
     """Attention forward: returns (out [B,Hq,Sq,D] in q's dtype, lse [B,Hq,Sq] fp32).
 
     q: [B,Hq,Sq,D]; k, v: [B,Hkv,Skv,D]; fp16 or bf16 on one GPU.  ``scale``
@@ -221,7 +242,7 @@ def fa_fwd(q, k, v, scale=None, causal=True, input_pos=0, config=-1):
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     return fa_fwd_into(q, k, v, out, lse, scale=scale, causal=causal, input_pos=input_pos,
-                       config=config)
+                       config=config, window=window)
 
 
 def select_config(B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype) -> int:

@@ -101,7 +101,7 @@ bool overlaps(uintptr_t a, size_t na, uintptr_t b, size_t nb) {
 // Pure host validation: no HIP call.  Returns FA_OK or the first failing check.
 int validate(const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
-             int input_pos, int dtype) {
+             int input_pos, int window, int dtype) {
     // A pointer may be NULL only when its tensor has no elements (an empty problem).
     const bool q_empty = B <= 0 || Hq <= 0 || Sq <= 0;
     const bool kv_empty = B <= 0 || Hkv <= 0 || Skv <= 0;
@@ -117,7 +117,7 @@ int validate(const void* q, const void* k, const void* v, void* out, float* lse,
     if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
     if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_SCALE;
     if (input_pos < 0 || (long long)input_pos + Sq > INT_MAX) return FA_ERR_INVALID_INPUT_POS;
-    (void)causal;
+    if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_WINDOW;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15u) return FA_ERR_MISALIGNED;
     if ((uintptr_t)lse & 3u) return FA_ERR_MISALIGNED;
     const size_t qb = (size_t)B * Hq * Sq * D * 2, kb = (size_t)B * Hkv * Skv * D * 2;
@@ -205,9 +205,11 @@ size_t workspace_bytes_for(int B, int Hq, int Sq, int D, int num_splits) {
     return (size_t)num_splits * B * Hq * Sq * (size_t)(D + 1) * sizeof(float);
 }
 
-// Tiles of the longest key range of any query tile (all keys, or the causal extent).
-int max_key_tiles(const ConfigEntry& c, int Sq, int Skv, int causal, int input_pos) {
-    const long long vis = causal ? std::min<long long>((long long)input_pos + Sq, Skv) : Skv;
+// Tiles of the longest key range of any query tile (all keys, the causal extent, or a
+// sliding window plus the query tile's own positions).
+int max_key_tiles(const ConfigEntry& c, int Sq, int Skv, int causal, int input_pos, int window) {
+    long long vis = causal ? std::min<long long>((long long)input_pos + Sq, Skv) : Skv;
+    if (causal && window > 0) vis = std::min<long long>(vis, (long long)window + 32 * c.QB * c.WPH);
     return (int)((vis + c.BN - 1) / c.BN);
 }
 
@@ -218,11 +220,12 @@ int max_key_tiles(const ConfigEntry& c, int Sq, int Skv, int causal, int input_p
 // from measured sweeps: decoding with 8 to 128 workgroups runs fastest at ~512 after the
 // split; a 256-workgroup prefill loses to the partial traffic.
 int auto_splits(const ConfigEntry& c, long long wgs, int B, int Hq, int Hkv, int Sq, int Skv,
-                int causal, int input_pos) {
+                int causal, int input_pos, int window) {
     if (wgs <= 0 || wgs >= kNumCUs) return 1;
     const long long want = (kFullGrid + wgs - 1) / wgs;
-    const long long by_len = max_key_tiles(c, Sq, Skv, causal, input_pos) / 8;
-    const double kv_bytes = 4.0 * B * Hkv * (double)Skv * c.D;
+    const int tiles = max_key_tiles(c, Sq, Skv, causal, input_pos, window);
+    const long long by_len = tiles / 8;
+    const double kv_bytes = 4.0 * B * Hkv * std::min<double>(Skv, (double)tiles * c.BN) * c.D;
     const double part_bytes = 8.0 * B * Hq * (double)Sq * (c.D + 1);   // per range
     const long long by_traffic = (long long)(kv_bytes / part_bytes);
     return (int)std::max(1LL, std::min({want, by_len, by_traffic, (long long)kMaxSplits}));
@@ -240,8 +243,8 @@ int resolve_config(int config, int B, int Hq, int Hkv, int Sq, int Skv, int D, i
 // num_splits: 1 = the plain forward pass (out / lse written by the attention kernel);
 // > 1 = partials into `workspace`, then the merge kernel.  Arguments already validated.
 int launch(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
-           int Hkv, int Sq, int Skv, float scale, int causal, int input_pos, int config,
-           int num_splits, void* workspace, void* stream) {
+           int Hkv, int Sq, int Skv, float scale, int causal, int input_pos, int window,
+           int config, int num_splits, void* workspace, void* stream) {
     const ConfigEntry& c = kConfigs[config];
     const int bmp = 32 * c.QB * c.WPH;
     Params p;
@@ -256,6 +259,7 @@ int launch(const void* q, const void* k, const void* v, void* out, float* lse, i
     p.Sq = Sq;
     p.Skv = Skv;
     p.input_pos = causal ? input_pos : 0;
+    p.window = causal ? window : 0;
     p.c = (float)((double)scale * 1.4426950408889634073599246810019);  // scale * log2(e)
     p.group = Hq / Hkv;
     p.n_tiles = (Sq + bmp - 1) / bmp;
@@ -278,22 +282,24 @@ int launch(const void* q, const void* k, const void* v, void* out, float* lse, i
 }
 
 int run(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
-        int Hkv, int Sq, int Skv, int D, float scale, int causal, int input_pos, int dtype,
-        void* stream, int config) {
-    int rc = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos, dtype);
+        int Hkv, int Sq, int Skv, int D, float scale, int causal, int input_pos, int window,
+        int dtype, void* stream, int config) {
+    int rc = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos,
+                      window, dtype);
     if (rc != FA_OK) return rc;
     config = resolve_config(config, B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype);
     if (config < 0) return config;
     if ((long long)B * Hq * Sq == 0) return FA_OK;
-    return launch(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, scale, causal, input_pos, config, 1,
-                  nullptr, stream);
+    return launch(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, scale, causal, input_pos, window,
+                  config, 1, nullptr, stream);
 }
 
 int run_splitkv(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                 int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal, int input_pos,
-                int dtype, int num_splits, int config, void* workspace, size_t workspace_bytes,
-                void* stream) {
-    int rc = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos, dtype);
+                int window, int dtype, int num_splits, int config, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    int rc = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos,
+                      window, dtype);
     if (rc != FA_OK) return rc;
     config = resolve_config(config, B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype);
     if (config < 0) return config;
@@ -301,7 +307,7 @@ int run_splitkv(const void* q, const void* k, const void* v, void* out, float* l
     const ConfigEntry& c = kConfigs[config];
     if (num_splits == 0)
         num_splits = auto_splits(c, grid_of(c, B, Hq, Hkv, Sq), B, Hq, Hkv, Sq, Skv, causal,
-                                 causal ? input_pos : 0);
+                                 causal ? input_pos : 0, causal ? window : 0);
     if ((long long)B * Hq * Sq == 0) return FA_OK;
     if (num_splits > 1) {
         const size_t need = workspace_bytes_for(B, Hq, Sq, D, num_splits);
@@ -316,8 +322,8 @@ int run_splitkv(const void* q, const void* k, const void* v, void* out, float* l
             overlaps(w, need, (uintptr_t)lse, lb))
             return FA_ERR_ALIAS;
     }
-    return launch(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, scale, causal, input_pos, config,
-                  num_splits, workspace, stream);
+    return launch(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, scale, causal, input_pos, window,
+                  config, num_splits, workspace, stream);
 }
 
 }  // namespace
@@ -327,37 +333,46 @@ extern "C" {
 int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
            int Hkv, int Sq, int Skv, int D, float scale, int causal, int input_pos, int dtype,
            void* stream) {
-    return run(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos, dtype,
+    return run(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos, 0, dtype,
                stream, -1);
 }
 
 int fa_fwd_config(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                   int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
                   int input_pos, int dtype, void* stream, int config) {
-    return run(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos, dtype,
+    return run(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos, 0, dtype,
                stream, config);
+}
+
+int fa_fwd_window(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                  int Hq, int Hkv, int Sq, int Skv, int D, float scale, int input_pos,
+                  int window, int dtype, void* stream, int config) {
+    // window < 1 is invalid here; -1 lets validate() report it in its documented place.
+    return run(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, 1, input_pos,
+               window < 1 ? -1 : window, dtype, stream, config);
 }
 
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                    int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
-                   int input_pos, int dtype, int num_splits, int config, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+                   int input_pos, int window, int dtype, int num_splits, int config,
+                   void* workspace, size_t workspace_bytes, void* stream) {
     return run_splitkv(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos,
-                       dtype, num_splits, config, workspace, workspace_bytes, stream);
+                       window, dtype, num_splits, config, workspace, workspace_bytes, stream);
 }
 
 int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
-                          int input_pos, int dtype, int config) {
+                          int input_pos, int window, int dtype, int config) {
     if (B < 0 || Hq < 0 || Sq < 0 || Hkv < 1 || Skv < 1) return FA_ERR_INVALID_SHAPE;
     if (Hq % Hkv != 0) return FA_ERR_HEAD_GROUP;
     if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
     if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
     if (input_pos < 0 || (long long)input_pos + Sq > INT_MAX) return FA_ERR_INVALID_INPUT_POS;
+    if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_WINDOW;
     config = resolve_config(config, B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype);
     if (config < 0) return config;
     const ConfigEntry& c = kConfigs[config];
     return auto_splits(c, grid_of(c, B, Hq, Hkv, Sq), B, Hq, Hkv, Sq, Skv, causal,
-                       causal ? input_pos : 0);
+                       causal ? input_pos : 0, causal ? window : 0);
 }
 
 size_t fa_splitkv_workspace_size(int B, int Hq, int Sq, int D, int num_splits) {
@@ -398,6 +413,7 @@ const char* fa_strerror(int code) {
         case FA_ERR_LAUNCH: return "kernel launch failed";
         case FA_ERR_INVALID_SPLITS: return "num_splits must be in 0..256";
         case FA_ERR_WORKSPACE: return "split-KV workspace smaller than fa_splitkv_workspace_size()";
+        case FA_ERR_INVALID_WINDOW: return "window must be >= 0, needs causal masking, and >= 1 for fa_fwd_window";
         default: return "unknown status code";
     }
 }

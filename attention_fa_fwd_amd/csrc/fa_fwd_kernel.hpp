@@ -94,6 +94,7 @@ struct Params {
     int hsub;        // head groups per K/V head: group / HPW
     int map_mode;    // workgroup -> XCD mapping: 0 plain, 1 groups per XCD, 2 XCDs per group
     int map_arg;     // mode 1: groups per XCD; mode 2: XCDs per group
+    int window;      // causal sliding window: keys input_pos + i - window + 1 .. ; 0 = none
     int num_splits;  // key ranges per query tile; > 1 writes partials for the merge kernel
     float* o_part;   // num_splits > 1: normalised partial O, fp32 [num_splits][B*Hq*Sq][D]
     float* lse_part; // num_splits > 1: partial LSE, fp32 [num_splits][B*Hq*Sq]
@@ -290,23 +291,34 @@ void fa_fwd_kernel(Params p) {
         for (int dk = 0; dk < DK; ++dk) qf[qb][dk] = src[dk * 2 + h];
     }
 
-    // Loop bounds.  Workgroup: Tc tiles, of which the first n_free need no mask.  Wave:
-    // tiles >= wave_tc are fully masked for its rows and skipped.
+    // Loop bounds.  Workgroup: tiles [tb, Tc); tiles [f0, f1) need no mask (K-loop split),
+    // those before f0 (sliding-window edge) and from f1 on (diagonal, key tail) do.  Wave:
+    // tiles outside [wave_lo, wave_tc) are fully masked for its rows and skipped.
+    const bool win = CAUSAL && p.window > 0;
     const int q_last = min(q0 + C::BMP, p.Sq) - 1;
     const int Tc = CAUSAL ? (min(p.input_pos + q_last + 1, p.Skv) + BN - 1) / BN
                           : (p.Skv + BN - 1) / BN;
-    const int n_free = min(CAUSAL ? min((p.input_pos + q0) / BN, p.Skv / BN) : p.Skv / BN, Tc);
+    const int tb = win ? min(max(0, p.input_pos + q0 - p.window + 1) / BN, Tc) : 0;
+    const int f1 = min(CAUSAL ? min((p.input_pos + q0) / BN, p.Skv / BN) : p.Skv / BN, Tc);
+    // First tile above every row's window edge.  When masked tiles precede it, it is run
+    // as a masked step too, so that every unmasked step follows an unmasked one (or is the
+    // first step) and P V of its predecessor needs no per-wave check.
+    int f0 = win ? max(tb, (p.input_pos + q_last - p.window + BN) / BN) : tb;
+    if (f0 > tb) ++f0;
     const int qw_last = min(qw0 + 32 * QB, p.Sq) - 1;
     const int wave_tc = qw_last < qw0 ? 0
                         : CAUSAL ? (min(p.input_pos + qw_last + 1, p.Skv) + BN - 1) / BN
                                  : Tc;
-    // This workgroup's key split: tiles [t0, t1) of [0, Tc), tile-aligned, so no mask is
+    const int wave_lo = win ? max(0, p.input_pos + qw0 - p.window + 1) / BN : 0;
+    // This workgroup's key split: tiles [t0, t1) of [tb, Tc), tile-aligned, so no mask is
     // needed at split boundaries.  Loads stop at key kend.  An empty range (more splits than
     // tiles) leaves the state empty: the partial is O = 0, LSE = -inf.
-    const int t0 = (int)((long long)Tc * split / p.num_splits);
-    const int t1 = (int)((long long)Tc * (split + 1) / p.num_splits);
+    const int t0 = tb + (int)((long long)(Tc - tb) * split / p.num_splits);
+    const int t1 = tb + (int)((long long)(Tc - tb) * (split + 1) / p.num_splits);
     const int nt = t1 - t0;                    // tiles in this range
-    const int nf = max(0, min(n_free - t0, nt));   // leading tiles of it needing no mask
+    // Local step bands: [0, ua) masked, [ua, ub) unmasked, [ub, nt) masked.
+    const int ua = min(max(f0 - t0, 0), nt);
+    const int ub = max(ua, min(f1 - t0, nt));
     const int kend = min(p.Skv, t1 * BN);
 
     // Running state: m (exp2 domain, possibly stale), l, acc (= O^T blocks).
@@ -449,8 +461,8 @@ void fa_fwd_kernel(Params p) {
         auto& pk_prev = pick(N2{}, pk0, pk1, pk2);
         fetch(kp, j + 3, kl(ph_tag), ksrc);
         fetch(vp, j + 1, vl(N1{}), vsrc);
-        const bool do_sm = !MASKED || j < wave_tc;          // softmax of tile j
-        const bool do_pv = !FIRST && (!MASKED || j - 1 < wave_tc);   // P V of tile j-1
+        const bool do_sm = !MASKED || (j >= wave_lo && j < wave_tc);   // softmax of tile j
+        const bool do_pv = !FIRST && (!MASKED || (j - 1 >= wave_lo && j - 1 < wave_tc));   // P V of tile j-1
         if (do_sm) {
             if constexpr (MASKED) {
                 const int j0 = j * BN;
@@ -458,12 +470,13 @@ void fa_fwd_kernel(Params p) {
                 for (int qb = 0; qb < QB; ++qb) {
                     const int qpos = p.input_pos + qw0 + qb * 32 + l32;
                     const int lim = CAUSAL ? min(qpos, p.Skv - 1) : p.Skv - 1;   // last visible key
+                    const int lo = win ? qpos - p.window + 1 : 0;                 // first visible key
 #pragma unroll
                     for (int k2 = 0; k2 < KB; ++k2)
 #pragma unroll
                         for (int i = 0; i < 16; ++i) {
                             const int key = j0 + k2 * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-                            if (key > lim) s_cur[k2][qb][i] = -__builtin_inff();
+                            if (key > lim || key < lo) s_cur[k2][qb][i] = -__builtin_inff();
                         }
                 }
             }
@@ -557,10 +570,10 @@ void fa_fwd_kernel(Params p) {
         qk(k_lds0, s0);
         end_step();   // K(t0+1) and K(t0+2) landed
 
-        // The K loop in two parts (K-loop split): tiles needing no mask, then the diagonal /
-        // key-tail tiles.  Unrolled by three so the phase of i -- buffers and register
-        // roles -- is fixed at compile time in every copy of the step.
-        if (nf > 0) step(t0, Q0{}, F{}, TT{});
+        // The K loop in bands (K-loop split): window-edge tiles, tiles needing no mask,
+        // then the diagonal / key-tail tiles.  Unrolled by three so the phase of i --
+        // buffers and register roles -- is fixed at compile time in every copy of the step.
+        if (ua == 0 && ub > 0) step(t0, Q0{}, F{}, TT{});
         else step(t0, Q0{}, TT{}, TT{});
         int i = 1;
         auto run = [&](int end, auto masked) FA_INLINE {
@@ -574,13 +587,14 @@ void fa_fwd_kernel(Params p) {
             if (i < end) { step(t0 + i, Q0{}, masked, F{}); ++i; }
             if (i < end) { step(t0 + i, Q1{}, masked, F{}); ++i; }
         };
-        run(nf, F{});
+        run(ua, TT{});
+        run(ub, F{});
         run(nt, TT{});
         // The last steps issued loads past the range (zero-size, landing as zeros): let
         // them land before the workgroup can end and its LDS be reused.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         // Drain: P V of the last tile (its V landed by the end of the last step).
-        if (t1 - 1 < wave_tc) {
+        if (t1 - 1 >= wave_lo && t1 - 1 < wave_tc) {
             const int ph = (nt - 1) % 3;
             if (ph == 0) pv(v_lds0, pk0);
             else if (ph == 1) pv(v_lds1, pk1);

@@ -31,6 +31,10 @@ WORKLOADS = {
                                         dtype="bf16", causal=True, input_pos=0),
     "gqa4_prefill_q1024_kv16384_d128_bf16": dict(B=2, Hq=32, Hkv=8, Sq=1024, Skv=16384, D=128,
                                                   dtype="bf16", causal=True, input_pos=15360),
+    # Sliding-window causal attention over a 16K sequence, window 4096 keys.
+    "gqa8_swa4096_causal_s16384_d128_bf16": dict(B=1, Hq=32, Hkv=4, Sq=16384, Skv=16384, D=128,
+                                                  dtype="bf16", causal=True, input_pos=0,
+                                                  window=4096),
     # One new token per sequence against a 16K-token cache: the under-filled grid that
     # split-KV is for (32 workgroups unsplit).
     "gqa4_decode_b4_kv16384_d128_bf16": dict(B=4, Hq=32, Hkv=8, Sq=1, Skv=16384, D=128,
@@ -59,5 +63,6 @@ def make_workload(name, seed=0):
     """Inputs and call arguments for a named workload: (q, k, v, kwargs)."""
     w = dict(WORKLOADS[name])
     q, k, v = make_qkv(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"], w["dtype"], seed)
-    kw = dict(scale=default_scale(w["D"]), causal=w["causal"], input_pos=w["input_pos"])
+    kw = dict(scale=default_scale(w["D"]), causal=w["causal"], input_pos=w["input_pos"],
+              window=w.get("window", 0))
     return q, k, v, kw

@@ -52,6 +52,9 @@ def log(*a):
 
 
 def literal_flops(w):
+    """4*B*Hq*Sq*Skv*D, halved when causal; a sliding window counts its visible pairs."""
+    if w.get("window", 0):
+        return exact_flops(w)
     f = 4.0 * w["B"] * w["Hq"] * w["Sq"] * w["Skv"] * w["D"]
     return f / 2 if w["causal"] else f
 
@@ -59,7 +62,15 @@ def literal_flops(w):
 def exact_flops(w):
     """4*D per visible (query, key) pair."""
     Sq, Skv, pos = w["Sq"], w["Skv"], w["input_pos"]
-    if not w["causal"]:
+    W = w.get("window", 0)
+    if W:
+        import numpy as np
+
+        i = np.arange(Sq, dtype=np.int64) + pos
+        hi = np.minimum(i, Skv - 1)
+        lo = np.maximum(i - W + 1, 0)
+        pairs = int(np.maximum(hi - lo + 1, 0).sum())
+    elif not w["causal"]:
         pairs = Sq * Skv
     else:
         pairs = 0
@@ -120,18 +131,20 @@ def time_gpu(name, steps, warmup, config=-1, splitkv=False):
     splits = 1
     if splitkv:
         splits = fa.splitkv_num_splits(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"],
-                                       w["causal"], w["input_pos"], q.dtype, config)
+                                       w["causal"], w["input_pos"], q.dtype, config,
+                                       kw["window"])
         nbytes = fa.splitkv_workspace_size(w["B"], w["Hq"], w["Sq"], w["D"], splits)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
 
         def step():
             fa.fa_fwd_splitkv_into(q, k, v, out, lse, ws, num_splits=splits, scale=kw["scale"],
                                    causal=kw["causal"], input_pos=kw["input_pos"], config=config,
-                                   stream=sp)
+                                   stream=sp, window=kw["window"])
     else:
         def step():
             fa.fa_fwd_into(q, k, v, out, lse, scale=kw["scale"], causal=kw["causal"],
-                           input_pos=kw["input_pos"], config=config, stream=sp)
+                           input_pos=kw["input_pos"], config=config, stream=sp,
+                           window=kw["window"])
 
     t_warm = time.perf_counter()
     for _ in range(warmup):
@@ -179,7 +192,7 @@ def cpu_baseline(name):
     ks = k[:1, :1].double().numpy()
     vs = v[:1, :1].double().numpy()
     t0 = time.perf_counter()
-    oracle.attention_blocked(qs, ks, vs, kw["scale"], kw["causal"], kw["input_pos"])
+    oracle.attention_blocked(qs, ks, vs, kw["scale"], kw["causal"], kw["input_pos"], window=kw["window"])
     dt = time.perf_counter() - t0
     ws = dict(w, B=1, Hq=G, Hkv=1)
     return dict(value=literal_flops(ws) / dt / 1e12, unit="TFLOP/s", cores=int(threads),
@@ -234,7 +247,8 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False):
         "data": "synthetic: seeded N(0,1) q, k, v rounded to the storage dtype",
         "config": {"workload": name, "B": w["B"], "Hq": w["Hq"], "Hkv": w["Hkv"], "Sq": w["Sq"],
                    "Skv": w["Skv"], "D": w["D"], "causal": w["causal"],
-                   "input_pos": w["input_pos"], "kernel": r["kernel"], "path": path,
+                   "input_pos": w["input_pos"], "window": w.get("window", 0),
+                   "kernel": r["kernel"], "path": path,
                    "parallelism": "single GPU"},
         "kernel_us": {"mean": round(mean_kernel_ms * 1e3, 2), "median": round(med * 1e3, 2),
                       "p95": round(p95 * 1e3, 2), "min": round(r["per_ms"][0] * 1e3, 2)},

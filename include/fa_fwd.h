@@ -30,7 +30,8 @@
  * the null stream) and returns without synchronising.  Faults inside the kernel surface on the next synchronisation.
  *
  * Errors: a nonzero return leaves out and lse untouched and launches nothing, except
- * FA_ERR_LAUNCH, which reports a failed launch.  Checks run in the order of the codes below.
+ * FA_ERR_LAUNCH, which reports a failed launch.  Checks run in the order of the codes below,
+ * except that the window check (FA_ERR_INVALID_WINDOW) follows the input_pos check.
  */
 #ifndef FA_FWD_H
 #define FA_FWD_H
@@ -62,7 +63,9 @@ enum fa_status {
     FA_ERR_INVALID_CONFIG = -10,      /* fa_fwd_config: config id unknown or not applicable  */
     FA_ERR_LAUNCH = -11,              /* the kernel launch failed (hipGetLastError)           */
     FA_ERR_INVALID_SPLITS = -12,      /* fa_fwd_splitkv: num_splits outside 0..256            */
-    FA_ERR_WORKSPACE = -13            /* fa_fwd_splitkv: workspace_bytes too small            */
+    FA_ERR_WORKSPACE = -13,           /* fa_fwd_splitkv: workspace_bytes too small            */
+    FA_ERR_INVALID_WINDOW = -14       /* window < 0, window > 0 without causal masking, or    */
+                                      /* fa_fwd_window with window < 1                        */
 };
 
 /*
@@ -95,20 +98,40 @@ int fa_fwd_config(const void* q, const void* k, const void* v, void* out, float*
                   int causal, int input_pos, int dtype, void* stream, int config);
 
 /*
+ * Sliding-window causal attention: query i sees key j iff
+ *     input_pos + i - window + 1 <= j <= input_pos + i,
+ * the `window` most recent keys up to its own position.  The pages only name sliding-window
+ * attention ("How I Beat PyTorch's Flash Attention", "Future work"); this is the usual
+ * causal reading.  A query row whose window holds no key (input_pos + i - window + 1 >= Skv)
+ * gets out = 0 and lse = -inf.  The kernel visits only the key tiles inside some row's window
+ * and masks the window edge like the causal diagonal.
+ *
+ *   window    >= 1 (window >= input_pos + Sq gives plain causal attention).
+ *   config    as for fa_fwd_config; -1 = the dispatch table.
+ *   the rest  as for fa_fwd (causal masking is implied).
+ */
+int fa_fwd_window(const void* q, const void* k, const void* v, void* out, float* lse,
+                  int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+                  int input_pos, int window, int dtype, void* stream, int config);
+
+/*
  * Split-KV forward pass, for grids too small to fill the GPU (few heads or short query
  * blocks; decoding with Sq = 1).  The pages motivate it by launches with too few tiles for
  * the processors ("Tuning Flash Attention for peak performance in NVIDIA CUDA Tile", Part 2
  * "Autotuning"; "How I Beat PyTorch's Flash Attention", "Phase 5: Adaptive Tile
  * Dispatch"); they do not split the key loop, this library does: the visible key tiles of
- * each query tile are cut into num_splits tile-aligned ranges, each handled by its own
- * workgroup, which writes the range's normalised partial output O_s (fp32) and LSE_s.  A
+ * each query tile (inside the window, if any) are cut into num_splits tile-aligned ranges,
+ * each handled by its own workgroup, which writes the range's normalised partial output
+ * O_s (fp32) and LSE_s.  A
  * second kernel merges them with the online-softmax rescale of the cuTile post ("Online
  * softmax update") applied across ranges:
  *     LSE = ln sum_s exp(LSE_s),   out = sum_s exp(LSE_s - LSE) O_s
  * (a range with no visible key has LSE_s = -inf and weight 0).  The result is the same
  * attention as fa_fwd up to rounding order; out is rounded to `dtype` once, after the merge.
  *
- *   q .. dtype       as for fa_fwd.
+ *   q .. input_pos   as for fa_fwd.
+ *   window           0 = none; >= 1 = a sliding window as in fa_fwd_window (needs causal).
+ *   dtype            as for fa_fwd.
  *   num_splits       0 = choose (fa_splitkv_num_splits), 1 = no split (same kernels as
  *                    fa_fwd; workspace unused, may be NULL), 2..256 = that many ranges.
  *                    Ranges beyond the number of key tiles are empty and harmless.
@@ -125,15 +148,15 @@ int fa_fwd_config(const void* q, const void* k, const void* v, void* out, float*
  */
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
                    int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
-                   int causal, int input_pos, int dtype, int num_splits, int config,
-                   void* workspace, size_t workspace_bytes, void* stream);
+                   int causal, int input_pos, int window, int dtype, int num_splits,
+                   int config, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Split count fa_fwd_splitkv uses for num_splits = 0: 1 when the plain grid has at least
  * one workgroup per CU (256); else enough ranges for about 512 workgroups, capped so that
  * each range has >= 8 key tiles, the fp32 partials' traffic stays within the K/V bytes,
  * and there are at most 256 ranges.  Negative fa_status on invalid sizes. */
 int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
-                          int input_pos, int dtype, int config);
+                          int input_pos, int window, int dtype, int config);
 
 /* Workspace bytes fa_fwd_splitkv needs for num_splits ranges:
  * num_splits * B * Hq * Sq * (D + 1) * 4 (fp32 partial O, then fp32 partial LSE), 0 when

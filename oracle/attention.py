@@ -18,6 +18,8 @@ What is computed (every input is converted exactly to float64 first):
     kvh    = hq // (Hq // Hkv)                                  [cuTile] "Grouped-query attention"
     V(i)   = { j < Skv : not causal  or  j <= input_pos + i }   [cuTile] "Causal attention",
                                                                  Part 1 "Applying the causal mask"
+             minus { j < input_pos + i - W + 1 } for a sliding window of W >= 1 keys
+             (causal only; [Journey] "Future work" names sliding-window attention)
     s_j    = scale * <q[b,hq,i,:], k[b,kvh,j,:]>     for j in V(i)
     O      = sum_j exp(s_j - m) v[b,kvh,j,:] / sum_j exp(s_j - m),  m = max_j s_j
     LSE    = m + ln(sum_j exp(s_j - m))
@@ -28,7 +30,11 @@ the one its kernel code (Part 1, "Online softmax update" and "Final
 normalization and store") implements, with the default scale 1/sqrt(D) from
 its host code ("Launching the kernel: Host-side code").  The log-sum-exp output
 is on no page; it is read as the natural-log log-sum-exp of the scaled, masked
-scores of each row.
+scores of each row.  The sliding window is only named on the pages; it is read as
+the common causal form in which query i sees the W most recent keys up to its own
+position.  A row whose V(i) is empty (possible only with a window, when
+input_pos + i - W + 1 >= Skv) is read as O = 0 and LSE = -inf, the values of an
+empty sum.
 
 Four forms are provided, written independently of one another:
 
@@ -80,14 +86,16 @@ def _shapes(q, k, v):
 # Form (i): pure-Python loops over the definition
 # ----------------------------------------------------------------------------
 
-def attention_naive(q, k, v, scale, causal=False, input_pos=0):
+def attention_naive(q, k, v, scale, causal=False, input_pos=0, window=0):
     """Brute-force definition with pure-Python loops; float64; tiny shapes only.
 
     Follows [cuTile] "What is attention?" (textbook softmax(scale Q K^T + M) V),
     "Causal attention" (key n visible to query m iff offs_m >= offs_n, where the
     query position offs_m carries input_pos, Part 1 "Initializing
     accumulators") and "Grouped-query attention" (query heads in contiguous
-    groups of Hq/Hkv share one K/V head).
+    groups of Hq/Hkv share one K/V head).  window > 0 (causal only) also hides
+    keys before input_pos + i - window + 1; a row left with no key gets O = 0,
+    LSE = -inf.
 
     Returns (O [B,Hq,Sq,D], LSE [B,Hq,Sq]) as float64 arrays.
     """
@@ -102,12 +110,17 @@ def attention_naive(q, k, v, scale, causal=False, input_pos=0):
         for hq in range(Hq):
             g = hq // group
             for i in range(Sq):
-                last = Skv - 1
+                first, last = 0, Skv - 1
                 if causal:
                     last = min(last, input_pos + i)
+                    if window > 0:
+                        first = max(0, input_pos + i - window + 1)
+                if first > last:
+                    L[b, hq, i] = -math.inf
+                    continue
                 qi = ql[b][hq][i]
                 s = []
-                for j in range(last + 1):
+                for j in range(first, last + 1):
                     kj = kl[b][g][j]
                     acc = 0.0
                     for d in range(D):
@@ -118,8 +131,8 @@ def attention_naive(q, k, v, scale, causal=False, input_pos=0):
                 den = sum(e)
                 for d in range(D):
                     num = 0.0
-                    for j in range(last + 1):
-                        num += e[j] * vl[b][g][j][d]
+                    for n, j in enumerate(range(first, last + 1)):
+                        num += e[n] * vl[b][g][j][d]
                     O[b, hq, i, d] = num / den
                 L[b, hq, i] = m + math.log(den)
     return O, L
@@ -165,19 +178,24 @@ def kv_head_of(hq, Hq, Hkv):
     return hq // (Hq // Hkv)
 
 
-def key_visibility(rows, Skv, causal, input_pos):
+def key_visibility(rows, Skv, causal, input_pos, window=0):
     """Boolean [len(rows), Skv]: may query row i attend to key j?
 
     [cuTile] "Causal attention" and Part 1 "Applying the causal mask": with
     causal masking key j is visible iff j <= input_pos + i (the query position
     carries input_pos, Part 1 "Initializing accumulators"); without it every
-    key 0..Skv-1 is visible and input_pos plays no part.
+    key 0..Skv-1 is visible and input_pos plays no part.  A sliding window of
+    W = window > 0 keys (causal only) also requires j >= input_pos + i - W + 1.
     """
     rows = np.asarray(rows, dtype=np.int64)
     cols = np.arange(Skv, dtype=np.int64)
     if not causal:
         return np.ones((rows.size, Skv), dtype=bool)
-    return cols[None, :] <= (rows[:, None] + input_pos)
+    pos = rows[:, None] + input_pos
+    vis = cols[None, :] <= pos
+    if window > 0:
+        vis &= cols[None, :] >= pos - window + 1
+    return vis
 
 
 def scaled_scores(q_rows, k_head, scale):
@@ -213,18 +231,20 @@ def log_sum_exp(m, l):
     return m[:, 0] + np.log(l[:, 0])
 
 
-def attention_blocked(q, k, v, scale, causal=False, input_pos=0, rows_per_block=512):
+def attention_blocked(q, k, v, scale, causal=False, input_pos=0, rows_per_block=512, window=0):
     """The definition in float64 with NumPy matmuls, ``rows_per_block`` query rows at a time.
 
     Row blocking only bounds memory: every row is computed from its full set of
-    visible scores in one pass, exactly as defined (module docstring).
+    visible scores in one pass, exactly as defined (module docstring); rows
+    with no visible key (sliding window only) get O = 0 and LSE = -inf.
     Returns (O [B,Hq,Sq,D], LSE [B,Hq,Sq]) as float64 arrays.
     """
     B, Hq, Hkv, Sq, Skv, D = _shapes(q, k, v)
     if not (math.isfinite(scale) and scale > 0):
         raise ValueError("scale must be finite and > 0")
-    O = np.empty((B, Hq, Sq, D))
-    L = np.empty((B, Hq, Sq))
+    _check_window(causal, window)
+    O = np.zeros((B, Hq, Sq, D))
+    L = np.full((B, Hq, Sq), -np.inf)
     for b in range(B):
         for hq in range(Hq):
             g = kv_head_of(hq, Hq, Hkv)
@@ -232,27 +252,40 @@ def attention_blocked(q, k, v, scale, causal=False, input_pos=0, rows_per_block=
             vh = np.asarray(v[b, g], np.float64)
             for i0 in range(0, Sq, rows_per_block):
                 i1 = min(Sq, i0 + rows_per_block)
-                rows = np.arange(i0, i1)
-                s = scaled_scores(np.asarray(q[b, hq, i0:i1], np.float64), kh, scale)
-                m, e, l = masked_softmax_stats(s, key_visibility(rows, Skv, causal, input_pos))
-                O[b, hq, i0:i1] = normalise(e, l, vh)
-                L[b, hq, i0:i1] = log_sum_exp(m, l)
+                vis = key_visibility(np.arange(i0, i1), Skv, causal, input_pos, window)
+                rows = i0 + np.nonzero(vis.any(axis=1))[0]
+                if rows.size == 0:
+                    continue
+                s = scaled_scores(np.asarray(q[b, hq, rows], np.float64), kh, scale)
+                m, e, l = masked_softmax_stats(s, vis[rows - i0])
+                O[b, hq, rows] = normalise(e, l, vh)
+                L[b, hq, rows] = log_sum_exp(m, l)
     return O, L
 
 
-def attention_rows(q, k, v, scale, causal, input_pos, samples):
+def _check_window(causal, window):
+    if window < 0:
+        raise ValueError("window must be >= 0 (0 = no window)")
+    if window > 0 and not causal:
+        raise ValueError("a sliding window needs causal masking")
+
+
+def attention_rows(q, k, v, scale, causal, input_pos, samples, window=0):
     """The blocked definition evaluated only at sampled rows.
 
     ``samples`` is an iterable of (b, hq, i).  Used to check full-size runs
     whose complete oracle would take too long.  Returns (O [n,D], LSE [n]).
     """
     B, Hq, Hkv, Sq, Skv, D = _shapes(q, k, v)
+    _check_window(causal, window)
     samples = list(samples)
-    O = np.empty((len(samples), D))
-    L = np.empty(len(samples))
+    O = np.zeros((len(samples), D))
+    L = np.full(len(samples), -np.inf)
     for n, (b, hq, i) in enumerate(samples):
         g = kv_head_of(hq, Hq, Hkv)
-        vis = key_visibility([i], Skv, causal, input_pos)
+        vis = key_visibility([i], Skv, causal, input_pos, window)
+        if not vis.any():
+            continue
         last = int(np.nonzero(vis[0])[0].max()) + 1  # only rows up to the last visible key are read
         kh = np.asarray(k[b, g, :last], np.float64)
         vh = np.asarray(v[b, g, :last], np.float64)
@@ -393,7 +426,7 @@ def attention_online_tiled(q, k, v, scale, causal=False, input_pos=0, tile_m=64,
 # Form (iv): attention over a key range, and the merge of ranges (split-KV)
 # ----------------------------------------------------------------------------
 
-def attention_key_range(q, k, v, scale, causal, input_pos, key_lo, key_hi):
+def attention_key_range(q, k, v, scale, causal, input_pos, key_lo, key_hi, window=0):
     """The definition with each row's visible keys cut to key_lo <= j < key_hi.
 
     The pages split the work over query tiles only; splitting the key loop is
@@ -409,8 +442,9 @@ def attention_key_range(q, k, v, scale, causal, input_pos, key_lo, key_hi):
         raise ValueError("scale must be finite and > 0")
     O = np.zeros((B, Hq, Sq, D))
     L = np.full((B, Hq, Sq), -np.inf)
+    _check_window(causal, window)
     in_range = (np.arange(Skv) >= key_lo) & (np.arange(Skv) < key_hi)
-    vis = key_visibility(np.arange(Sq), Skv, causal, input_pos) & in_range[None, :]
+    vis = key_visibility(np.arange(Sq), Skv, causal, input_pos, window) & in_range[None, :]
     rows = np.nonzero(vis.any(axis=1))[0]
     if rows.size == 0:
         return O, L

@@ -145,11 +145,18 @@ def test_missing_library_fails_loudly(tmp_path):
 W = 6 * P   # fake workspace address, 16-byte aligned, clear of every tensor
 
 
-def call_split(lib, num_splits=2, config=-1, ws=W, ws_bytes=1 << 28, **over):
+def call_split(lib, num_splits=2, config=-1, ws=W, ws_bytes=1 << 28, window=0, **over):
     a = dict(GOOD, **over)
     return lib.fa_fwd_splitkv(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"],
                               a["Sq"], a["Skv"], a["D"], a["scale"], a["causal"], a["input_pos"],
-                              a["dtype"], num_splits, config, ws, ws_bytes, None)
+                              window, a["dtype"], num_splits, config, ws, ws_bytes, None)
+
+
+def call_window(lib, window=4, config=-1, **over):
+    a = dict(GOOD, **over)
+    return lib.fa_fwd_window(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                             a["Sq"], a["Skv"], a["D"], a["scale"], a["input_pos"], window,
+                             a["dtype"], None, config)
 
 
 def test_splitkv_workspace_size(lib):
@@ -201,3 +208,31 @@ def test_splitkv_validation_order_and_noops(lib):
     # then launch, which needs a GPU, so only the size rule is checked here
     need = fa.splitkv_workspace_size(1, 4, 8, 64, 2)
     assert call_split(lib, ws_bytes=need - 1) == -13
+
+
+# --- sliding window ------------------------------------------------------------------
+
+def test_window_validation(lib):
+    assert call_window(lib, window=0) == -14
+    assert call_window(lib, window=-3) == -14
+    assert call_split(lib, window=-1) == -14
+    assert call_split(lib, window=5, causal=0) == -14
+    # order: input_pos before window, window before alignment
+    assert call_window(lib, window=0, input_pos=-1) == -7
+    assert call_window(lib, window=0, q=Q + 8) == -14
+    assert call_split(lib, window=3, causal=0, out=O + 4) == -14
+    # the window entry point checks everything fa_fwd checks
+    assert call_window(lib, Hq=3) == -3
+    assert call_window(lib, D=96) == -4
+    assert call_window(lib, config=10 ** 6) == -10
+    # empty problems launch nothing
+    assert call_window(lib, Sq=0, q=0, out=0, lse=0) == 0
+
+
+def test_window_split_count(lib):
+    # decoding against a 16K cache with a 4K (1K) window: the window bounds the key tiles,
+    # so the ranges keep >= 8 of them
+    assert fa.splitkv_num_splits(4, 32, 8, 1, 16384, 128, True, 16383, 1, window=4096) == 16
+    assert fa.splitkv_num_splits(4, 32, 8, 1, 16384, 128, True, 16383, 1, window=1024) == 4
+    with pytest.raises(fa.FaError):
+        fa.splitkv_num_splits(4, 32, 8, 1, 16384, 128, False, 0, 1, window=1024)

@@ -113,17 +113,17 @@ def test_golden_tile_counts():
 
 MUTANTS = {
     "gqa_strided": ("kv_head_of", lambda hq, Hq, Hkv: hq % Hkv),
-    "mask_strict_lt": ("key_visibility", lambda rows, Skv, causal, pos: (
+    "mask_strict_lt": ("key_visibility", lambda rows, Skv, causal, pos, window=0: (
         np.ones((len(rows), Skv), bool) if not causal else
         np.maximum(np.arange(Skv)[None, :] < np.asarray(rows)[:, None] + pos,
                    np.arange(Skv)[None, :] == 0))),
-    "mask_ignores_input_pos": ("key_visibility", lambda rows, Skv, causal, pos: (
+    "mask_ignores_input_pos": ("key_visibility", lambda rows, Skv, causal, pos, window=0: (
         np.ones((len(rows), Skv), bool) if not causal else
         np.arange(Skv)[None, :] <= np.asarray(rows)[:, None])),
-    "mask_transposed": ("key_visibility", lambda rows, Skv, causal, pos: (
+    "mask_transposed": ("key_visibility", lambda rows, Skv, causal, pos, window=0: (
         np.ones((len(rows), Skv), bool) if not causal else
         np.arange(Skv)[None, :] >= np.asarray(rows)[:, None] + pos)),
-    "mask_dropped": ("key_visibility", lambda rows, Skv, causal, pos: np.ones((len(rows), Skv), bool)),
+    "mask_dropped": ("key_visibility", lambda rows, Skv, causal, pos, window=0: np.ones((len(rows), Skv), bool)),
     "scale_dropped": ("scaled_scores", lambda qr, kh, scale: qr @ kh.T),
     "scale_inverted": ("scaled_scores", lambda qr, kh, scale: (qr @ kh.T) / scale),
     "scores_sign": ("scaled_scores", lambda qr, kh, scale: -scale * (qr @ kh.T)),
