@@ -17,6 +17,7 @@
 
 #include "fa_fwd.h"
 #include "fa_fwd_kernel.hpp"
+#include "fa_merge_kernel.hpp"
 
 namespace {
 
@@ -75,7 +76,7 @@ const ConfigEntry kConfigs[] = {
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 
 // Largest split count: bounds the merge kernel's loop and the workspace.
-constexpr int kMaxSplits = 256;
+constexpr int kMaxSplits = fa::kMergeMaxSplits;
 // CUs of an MI355X, and the resident workgroups that fill it (two four-wave workgroups
 // per CU).
 constexpr long long kNumCUs = 256;

@@ -51,8 +51,8 @@
 //    the pages' "too few tiles" case, cuTile post Part 2 "Autotuning", "How I Beat PyTorch's
 //    Flash Attention" Phase 5): each query tile's visible K/V tiles are cut into num_splits
 //    tile-aligned ranges, one workgroup each.  A workgroup stores its range's normalised
-//    partial O (fp32) and LSE; fa_merge_kernel folds the partials with the online-softmax
-//    rescale ("Online softmax update") applied across ranges.
+//    partial O (fp32) and LSE; fa_merge_kernel (fa_merge_kernel.hpp) folds the partials
+//    with the online-softmax rescale ("Online softmax update") applied across ranges.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -641,43 +641,6 @@ void fa_fwd_kernel(Params p) {
             }
         }
     }
-}
-
-// Merge of the key splits (the online-softmax rescale applied across ranges):
-//   LSE = ln sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s,
-// with O_s the normalised partial of split s.  One wave per (batch, head, query) row; lane
-// i handles d = 2i, 2i+1 (head dim 128) or d = i (64).
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void fa_merge_kernel(const float* o_part, const float* lse_part,
-                                                       void* o, float* lse, int rows, int num_splits) {
-    constexpr int PER = D / 64;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (row >= rows) return;
-    constexpr float LOG2E = 1.44269504088896340736f;
-    float mx = -__builtin_inff();
-    for (int sp = 0; sp < num_splits; ++sp) mx = fmaxf(mx, lse_part[(size_t)sp * rows + row]);
-    float out[PER] = {};
-    float total = 0.0f;
-    if (mx != -__builtin_inff()) {
-        for (int sp = 0; sp < num_splits; ++sp) {
-            const float ls = lse_part[(size_t)sp * rows + row];
-            const float wgt = ls == -__builtin_inff() ? 0.0f : fast_exp2((ls - mx) * LOG2E);
-            total += wgt;
-            const float* src = o_part + ((size_t)sp * rows + row) * D + lane * PER;
-#pragma unroll
-            for (int e = 0; e < PER; ++e) out[e] += wgt * src[e];
-        }
-    }
-    const float inv = total > 0.0f ? __builtin_amdgcn_rcpf(total) : 0.0f;
-    uint16_t* orow = (uint16_t*)o + (size_t)row * D + lane * PER;
-    if constexpr (PER == 2) {
-        *(uint32_t*)orow = pack2<BF16>(out[0] * inv, out[1] * inv);
-    } else {
-        const uint32_t w = pack2<BF16>(out[0] * inv, 0.0f);
-        orow[0] = (uint16_t)(w & 0xffffu);
-    }
-    if (lane == 0) lse[row] = total > 0.0f ? mx + __builtin_logf(total) : -__builtin_inff();
 }
 
 }  // namespace fa
