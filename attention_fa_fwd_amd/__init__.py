@@ -14,7 +14,7 @@ import math
 import os
 import threading
 
-__all__ = ["fa_fwd", "fa_fwd_into", "fa_fwd_splitkv", "fa_fwd_splitkv_into", "splitkv_num_splits",
+__all__ = ["fa_fwd", "fa_fwd_into", "fa_fwd_fp8", "fa_fwd_fp8_into", "select_config_fp8", "fa_fwd_splitkv", "fa_fwd_splitkv_into", "splitkv_num_splits",
            "splitkv_workspace_size", "select_config", "config_names", "num_configs", "FaError",
            "load_library", "LIB_PATH"]
 
@@ -44,6 +44,11 @@ def _declare(lib):
     lib.fa_fwd.restype = _c_int
     lib.fa_fwd_config.argtypes = _FWD_ARGS + [_c_int]
     lib.fa_fwd_config.restype = _c_int
+    lib.fa_fwd_fp8.argtypes = _FWD_ARGS[:12] + [_c_float, _c_float, _c_int, _c_int, _c_int, _c_int,
+                                                _vp, _c_int]
+    lib.fa_fwd_fp8.restype = _c_int
+    lib.fa_select_config_fp8.argtypes = [_c_int] * 7
+    lib.fa_select_config_fp8.restype = _c_int
     lib.fa_fwd_window.argtypes = _FWD_ARGS[:12] + [_c_int, _c_int, _c_int, _vp, _c_int]
     lib.fa_fwd_window.restype = _c_int
     lib.fa_fwd_splitkv.argtypes = _FWD_ARGS[:14] + [_c_int, _c_int, _c_int, _c_int, _vp,
@@ -260,3 +265,65 @@ def num_configs() -> int:
 def config_names():
     lib = load_library()
     return [lib.fa_config_name(i).decode() for i in range(lib.fa_num_configs())]
+
+
+def fa_fwd_fp8_into(q8, k8, v, out, lse, q_descale, k_descale, scale=None, causal=True,
+                    input_pos=0, window=0, config=-1, stream=None):
+    """fp8 E4M3 q8 [B,Hq,Sq,D], k8 [B,Hkv,Skv,D] (torch.float8_e4m3fn) with per-tensor
+    descale factors; v [B,Hkv,Skv,D] and out in fp16 / bf16; lse fp32 (fa_fwd_fp8)."""
+    import torch
+
+    lib = load_library()
+    for name, t in (("q8", q8), ("k8", k8), ("v", v), ("out", out), ("lse", lse)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != q8.device:
+            raise ValueError(f"{name} is on {t.device}, q8 on {q8.device}")
+    if q8.dtype != torch.float8_e4m3fn or k8.dtype != torch.float8_e4m3fn:
+        raise TypeError("q8 and k8 must be torch.float8_e4m3fn")
+    if out.dtype != v.dtype:
+        raise TypeError("out must have v's dtype")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    B, Hq, Sq, D = q8.shape
+    Bk, Hkv, Skv, Dk = k8.shape
+    if tuple(v.shape) != tuple(k8.shape) or Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch q{tuple(q8.shape)} k{tuple(k8.shape)} v{tuple(v.shape)}")
+    if tuple(out.shape) != tuple(q8.shape) or tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("out must be [B, Hq, Sq, D] and lse [B, Hq, Sq]")
+    _check_window(causal, window)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q8.device).cuda_stream
+    with torch.cuda.device(q8.device):
+        rc = lib.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), B, Hq, Hkv, Sq, Skv, D, float(scale),
+                            float(q_descale), float(k_descale), 1 if causal else 0,
+                            int(input_pos), int(window), _dtype_code(v.dtype), stream,
+                            int(config))
+    _check(rc)
+    return out, lse
+
+
+def fa_fwd_fp8(q8, k8, v, q_descale, k_descale, scale=None, causal=True, input_pos=0, window=0,
+               config=-1):
+    """Attention with fp8 E4M3 queries and keys (real values q_descale * q8, k_descale * k8)
+    and fp16 / bf16 values: returns (out in v's dtype, lse fp32)."""
+    import torch
+
+    q8, k8, v = q8.contiguous(), k8.contiguous(), v.contiguous()
+    out = torch.empty(q8.shape, dtype=v.dtype, device=q8.device)
+    lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=q8.device)
+    return fa_fwd_fp8_into(q8, k8, v, out, lse, q_descale, k_descale, scale=scale, causal=causal,
+                           input_pos=input_pos, window=window, config=config)
+
+
+def select_config_fp8(B, Hq, Hkv, Sq, D, causal, v_dtype) -> int:
+    """Configuration fa_fwd_fp8 picks (v_dtype: torch dtype or FA code)."""
+    code = v_dtype if isinstance(v_dtype, int) else _dtype_code(v_dtype)
+    rc = load_library().fa_select_config_fp8(B, Hq, Hkv, Sq, D, 1 if causal else 0, code)
+    _check(rc if rc < 0 else 0)
+    return rc

@@ -28,7 +28,7 @@ typedef hipError_t (*LaunchFn)(const Params&, hipStream_t);
 
 struct ConfigEntry {
     const char* name;
-    int D, bf16, causal;
+    int D, bf16, causal, qk8;
     int BN, QB, WPH, HPW;
     LaunchFn launch;
 };
@@ -42,11 +42,13 @@ hipError_t launch_cfg(const Params& p, hipStream_t s) {
 
 #define FA_STR2(x) #x
 #define FA_STR(x) FA_STR2(x)
-#define FA_ENTRY(D, BN, QB, WPH, HPW, CAUSAL, BF16, CNAME, TNAME)                             \
+#define FA_ENTRY_Q(D, BN, QB, WPH, HPW, CAUSAL, BF16, QK8, CNAME, TNAME)                     \
     ConfigEntry{"D" FA_STR(D) "_BN" FA_STR(BN) "_Mw" FA_STR(QB) "x32_WPH" FA_STR(WPH)        \
                 "_HPW" FA_STR(HPW) "_" CNAME "_" TNAME,                                        \
-                D, BF16, CAUSAL, BN, QB, WPH, HPW,                                              \
-                &launch_cfg<Cfg<D, BN, QB, WPH, HPW, CAUSAL, BF16>>}
+                D, BF16, CAUSAL, QK8, BN, QB, WPH, HPW,                                         \
+                &launch_cfg<Cfg<D, BN, QB, WPH, HPW, CAUSAL, BF16, QK8>>}
+#define FA_ENTRY(D, BN, QB, WPH, HPW, CAUSAL, BF16, CNAME, TNAME) \
+    FA_ENTRY_Q(D, BN, QB, WPH, HPW, CAUSAL, BF16, false, CNAME, TNAME)
 
 #define FA_TILES(D, CAUSAL, BF16, CNAME, TNAME)                    \
     FA_ENTRY(D, 64, 1, 1, 4, CAUSAL, BF16, CNAME, TNAME),          \
@@ -57,21 +59,23 @@ hipError_t launch_cfg(const Params& p, hipStream_t s) {
     FA_ENTRY(D, 64, 1, 8, 1, CAUSAL, BF16, CNAME, TNAME)
 
 // 32-key tiles (head dim 128 only: a 32 x 64 tile is too small to split over 512 threads).
-#define FA_TILES_BN32(CAUSAL, BF16, CNAME, TNAME)                  \
-    FA_ENTRY(128, 32, 1, 1, 4, CAUSAL, BF16, CNAME, TNAME),        \
-    FA_ENTRY(128, 32, 1, 2, 4, CAUSAL, BF16, CNAME, TNAME),        \
-    FA_ENTRY(128, 32, 1, 2, 2, CAUSAL, BF16, CNAME, TNAME),        \
-    FA_ENTRY(128, 32, 1, 4, 2, CAUSAL, BF16, CNAME, TNAME),        \
-    FA_ENTRY(128, 32, 1, 4, 1, CAUSAL, BF16, CNAME, TNAME),        \
-    FA_ENTRY(128, 32, 1, 8, 1, CAUSAL, BF16, CNAME, TNAME)
+#define FA_TILES_BN32(CAUSAL, BF16, QK8, CNAME, TNAME)                   \
+    FA_ENTRY_Q(128, 32, 1, 1, 4, CAUSAL, BF16, QK8, CNAME, TNAME),       \
+    FA_ENTRY_Q(128, 32, 1, 2, 4, CAUSAL, BF16, QK8, CNAME, TNAME),       \
+    FA_ENTRY_Q(128, 32, 1, 2, 2, CAUSAL, BF16, QK8, CNAME, TNAME),       \
+    FA_ENTRY_Q(128, 32, 1, 4, 2, CAUSAL, BF16, QK8, CNAME, TNAME),       \
+    FA_ENTRY_Q(128, 32, 1, 4, 1, CAUSAL, BF16, QK8, CNAME, TNAME),       \
+    FA_ENTRY_Q(128, 32, 1, 8, 1, CAUSAL, BF16, QK8, CNAME, TNAME)
 
 // Head dim 128 uses 32-key tiles only: with three LDS buffers and three register sets a
-// 64-key tile no longer fits two waves per SIMD.
+// 64-key tile no longer fits two waves per SIMD.  "fp8qk" entries take Q and K in fp8 e4m3.
 const ConfigEntry kConfigs[] = {
     FA_TILES(64, 1, 1, "causal", "bf16"),  FA_TILES(64, 0, 1, "full", "bf16"),
     FA_TILES(64, 1, 0, "causal", "fp16"),  FA_TILES(64, 0, 0, "full", "fp16"),
-    FA_TILES_BN32(1, 1, "causal", "bf16"), FA_TILES_BN32(0, 1, "full", "bf16"),
-    FA_TILES_BN32(1, 0, "causal", "fp16"), FA_TILES_BN32(0, 0, "full", "fp16"),
+    FA_TILES_BN32(1, 1, false, "causal", "bf16"), FA_TILES_BN32(0, 1, false, "full", "bf16"),
+    FA_TILES_BN32(1, 0, false, "causal", "fp16"), FA_TILES_BN32(0, 0, false, "full", "fp16"),
+    FA_TILES_BN32(1, 1, true, "causal", "fp8qk_bf16"), FA_TILES_BN32(0, 1, true, "full", "fp8qk_bf16"),
+    FA_TILES_BN32(1, 0, true, "causal", "fp8qk_fp16"), FA_TILES_BN32(0, 0, true, "full", "fp8qk_fp16"),
 };
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 
@@ -99,14 +103,31 @@ bool overlaps(uintptr_t a, size_t na, uintptr_t b, size_t nb) {
     return a < b + nb && b < a + na;
 }
 
+// One call's arguments.  dtype is the element type of v and out (and of q, k unless
+// qk8); qk8: q and k are fp8 e4m3 with per-tensor dequantisation factors.
+struct Call {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* lse;
+    int B, Hq, Hkv, Sq, Skv, D;
+    float scale;
+    int causal, input_pos, window, dtype;
+    int qk8;
+    float q_descale, k_descale;
+};
+
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
+
 // Pure host validation: no HIP call.  Returns FA_OK or the first failing check.
-int validate(const void* q, const void* k, const void* v, void* out, float* lse,
-             int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
-             int input_pos, int window, int dtype) {
+int validate(const Call& a) {
+    const int B = a.B, Hq = a.Hq, Hkv = a.Hkv, Sq = a.Sq, Skv = a.Skv, D = a.D;
     // A pointer may be NULL only when its tensor has no elements (an empty problem).
     const bool q_empty = B <= 0 || Hq <= 0 || Sq <= 0;
     const bool kv_empty = B <= 0 || Hkv <= 0 || Skv <= 0;
-    if ((!q_empty && (!q || !out || !lse)) || (!kv_empty && (!k || !v))) return FA_ERR_NULL_POINTER;
+    if ((!q_empty && (!a.q || !a.out || !a.lse)) || (!kv_empty && (!a.k || !a.v)))
+        return FA_ERR_NULL_POINTER;
     if (B < 0 || Hq < 0 || Sq < 0 || Hkv < 1 || Skv < 1) return FA_ERR_INVALID_SHAPE;
     // Head indices b*H + h are 32-bit in the kernel; byte sizes stay below 2^50.
     if ((long long)B * Hq > INT_MAX || (long long)B * Hkv > INT_MAX) return FA_ERR_INVALID_SHAPE;
@@ -115,34 +136,40 @@ int validate(const void* q, const void* k, const void* v, void* out, float* lse,
     if (qe > 1125899906842624.0 || ke > 1125899906842624.0) return FA_ERR_INVALID_SHAPE;
     if (Hq % Hkv != 0) return FA_ERR_HEAD_GROUP;
     if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
-    if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
-    if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_SCALE;
-    if (input_pos < 0 || (long long)input_pos + Sq > INT_MAX) return FA_ERR_INVALID_INPUT_POS;
-    if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_WINDOW;
-    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15u) return FA_ERR_MISALIGNED;
-    if ((uintptr_t)lse & 3u) return FA_ERR_MISALIGNED;
-    const size_t qb = (size_t)B * Hq * Sq * D * 2, kb = (size_t)B * Hkv * Skv * D * 2;
+    if (a.qk8 && D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (a.dtype != FA_DTYPE_FP16 && a.dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
+    if (!finite_pos(a.scale)) return FA_ERR_INVALID_SCALE;
+    if (a.qk8 && (!finite_pos(a.q_descale) || !finite_pos(a.k_descale))) return FA_ERR_INVALID_SCALE;
+    if (a.qk8 && !finite_pos(a.scale * a.q_descale * a.k_descale)) return FA_ERR_INVALID_SCALE;
+    if (a.input_pos < 0 || (long long)a.input_pos + Sq > INT_MAX) return FA_ERR_INVALID_INPUT_POS;
+    if (a.window < 0 || (a.window > 0 && !a.causal)) return FA_ERR_INVALID_WINDOW;
+    if (((uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.out) & 15u)
+        return FA_ERR_MISALIGNED;
+    if ((uintptr_t)a.lse & 3u) return FA_ERR_MISALIGNED;
+    const size_t qke = a.qk8 ? 1 : 2;
+    const size_t qb = (size_t)B * Hq * Sq * D * qke, kb = (size_t)B * Hkv * Skv * D * qke;
+    const size_t ob = (size_t)B * Hq * Sq * D * 2, vb = (size_t)B * Hkv * Skv * D * 2;
     const size_t lb = (size_t)B * Hq * Sq * 4;
-    const uintptr_t o = (uintptr_t)out, l = (uintptr_t)lse;
-    if (qb > 0 && (overlaps(o, qb, (uintptr_t)q, qb) || overlaps(o, qb, (uintptr_t)k, kb) ||
-                   overlaps(o, qb, (uintptr_t)v, kb) || overlaps(o, qb, l, lb) ||
-                   overlaps(l, lb, (uintptr_t)q, qb) || overlaps(l, lb, (uintptr_t)k, kb) ||
-                   overlaps(l, lb, (uintptr_t)v, kb)))
+    const uintptr_t o = (uintptr_t)a.out, l = (uintptr_t)a.lse;
+    const uintptr_t q = (uintptr_t)a.q, k = (uintptr_t)a.k, v = (uintptr_t)a.v;
+    if (ob > 0 && (overlaps(o, ob, q, qb) || overlaps(o, ob, k, kb) || overlaps(o, ob, v, vb) ||
+                   overlaps(o, ob, l, lb) || overlaps(l, lb, q, qb) || overlaps(l, lb, k, kb) ||
+                   overlaps(l, lb, v, vb)))
         return FA_ERR_ALIAS;
     return FA_OK;
 }
 
-bool applicable(const ConfigEntry& c, int Hq, int Hkv, int D, int causal, int dtype) {
+bool applicable(const ConfigEntry& c, int Hq, int Hkv, int D, int causal, int dtype, int qk8) {
     const int group = Hq / Hkv;
     return c.D == D && c.bf16 == (dtype == FA_DTYPE_BF16) && c.causal == (causal != 0) &&
-           group % c.HPW == 0;
+           c.qk8 == (qk8 != 0) && group % c.HPW == 0;
 }
 
-int find(int D, int bf16, int causal, int BN, int QB, int WPH, int HPW) {
+int find(int D, int bf16, int causal, int qk8, int BN, int QB, int WPH, int HPW) {
     for (int i = 0; i < kNumConfigs; ++i) {
         const ConfigEntry& c = kConfigs[i];
-        if (c.D == D && c.bf16 == bf16 && c.causal == causal && c.BN == BN && c.QB == QB &&
-            c.WPH == WPH && c.HPW == HPW)
+        if (c.D == D && c.bf16 == bf16 && c.causal == causal && c.qk8 == qk8 && c.BN == BN &&
+            c.QB == QB && c.WPH == WPH && c.HPW == HPW)
             return i;
     }
     return -1;
@@ -161,23 +188,22 @@ long long grid_of(const ConfigEntry& c, int B, int Hq, int Hkv, int Sq) {
 // K/V tile is read once for all of them.  An 8-wave workgroup (a whole CU: its K/V tiles
 // shared by twice the waves) beats two 4-wave ones when it still forms at least one
 // workgroup per CU; smaller grids use 4-wave workgroups for more of them.
-int select(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal, int input_pos, int dtype) {
-    (void)Skv;
-    (void)input_pos;
+int select(int B, int Hq, int Hkv, int Sq, int D, int causal, int dtype, int qk8) {
     const int bf16 = dtype == FA_DTYPE_BF16;
     const int cz = causal != 0;
+    const int q8 = qk8 != 0;
     const int group = Hq / Hkv;
     const int bn = D == 128 ? 32 : 64;
     int big, small;
     if (group % 4 == 0) {
-        big = find(D, bf16, cz, bn, 1, 2, 4);
-        small = find(D, bf16, cz, bn, 1, 1, 4);
+        big = find(D, bf16, cz, q8, bn, 1, 2, 4);
+        small = find(D, bf16, cz, q8, bn, 1, 1, 4);
     } else if (group % 2 == 0) {
-        big = find(D, bf16, cz, bn, 1, 4, 2);
-        small = find(D, bf16, cz, bn, 1, 2, 2);
+        big = find(D, bf16, cz, q8, bn, 1, 4, 2);
+        small = find(D, bf16, cz, q8, bn, 1, 2, 2);
     } else {
-        big = find(D, bf16, cz, bn, 1, 8, 1);
-        small = find(D, bf16, cz, bn, 1, 4, 1);
+        big = find(D, bf16, cz, q8, bn, 1, 8, 1);
+        small = find(D, bf16, cz, q8, bn, 1, 4, 1);
     }
     if (big >= 0 && grid_of(kConfigs[big], B, Hq, Hkv, Sq) >= kNumCUs) return big;
     return small;
@@ -220,111 +246,133 @@ int max_key_tiles(const ConfigEntry& c, int Sq, int Skv, int causal, int input_p
 // (written once, read once by the merge) within the K/V bytes the kernel reads.  Chosen
 // from measured sweeps: decoding with 8 to 128 workgroups runs fastest at ~512 after the
 // split; a 256-workgroup prefill loses to the partial traffic.
-int auto_splits(const ConfigEntry& c, long long wgs, int B, int Hq, int Hkv, int Sq, int Skv,
-                int causal, int input_pos, int window) {
+int auto_splits(const ConfigEntry& c, const Call& a) {
+    const long long wgs = grid_of(c, a.B, a.Hq, a.Hkv, a.Sq);
     if (wgs <= 0 || wgs >= kNumCUs) return 1;
     const long long want = (kFullGrid + wgs - 1) / wgs;
-    const int tiles = max_key_tiles(c, Sq, Skv, causal, input_pos, window);
+    const int tiles = max_key_tiles(c, a.Sq, a.Skv, a.causal, a.causal ? a.input_pos : 0,
+                                    a.causal ? a.window : 0);
     const long long by_len = tiles / 8;
-    const double kv_bytes = 4.0 * B * Hkv * std::min<double>(Skv, (double)tiles * c.BN) * c.D;
-    const double part_bytes = 8.0 * B * Hq * (double)Sq * (c.D + 1);   // per range
+    const double kv_bytes = 4.0 * a.B * a.Hkv * std::min<double>(a.Skv, (double)tiles * c.BN) * c.D;
+    const double part_bytes = 8.0 * a.B * a.Hq * (double)a.Sq * (c.D + 1);   // per range
     const long long by_traffic = (long long)(kv_bytes / part_bytes);
     return (int)std::max(1LL, std::min({want, by_len, by_traffic, (long long)kMaxSplits}));
 }
 
-int resolve_config(int config, int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
-                   int input_pos, int dtype) {
+int resolve_config(int config, const Call& a) {
     if (config < -1 || config >= kNumConfigs) return FA_ERR_INVALID_CONFIG;
-    if (config == -1) config = select(B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype);
+    if (config == -1) config = select(a.B, a.Hq, a.Hkv, a.Sq, a.D, a.causal, a.dtype, a.qk8);
     if (config < 0) return FA_ERR_INVALID_CONFIG;
-    if (!applicable(kConfigs[config], Hq, Hkv, D, causal, dtype)) return FA_ERR_INVALID_CONFIG;
+    if (!applicable(kConfigs[config], a.Hq, a.Hkv, a.D, a.causal, a.dtype, a.qk8))
+        return FA_ERR_INVALID_CONFIG;
     return config;
 }
 
 // num_splits: 1 = the plain forward pass (out / lse written by the attention kernel);
 // > 1 = partials into `workspace`, then the merge kernel.  Arguments already validated.
-int launch(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
-           int Hkv, int Sq, int Skv, float scale, int causal, int input_pos, int window,
-           int config, int num_splits, void* workspace, void* stream) {
+int launch(const Call& a, int config, int num_splits, void* workspace, void* stream) {
     const ConfigEntry& c = kConfigs[config];
     const int bmp = 32 * c.QB * c.WPH;
     Params p;
-    p.q = q;
-    p.k = k;
-    p.v = v;
-    p.o = out;
-    p.lse = lse;
-    p.B = B;
-    p.Hq = Hq;
-    p.Hkv = Hkv;
-    p.Sq = Sq;
-    p.Skv = Skv;
-    p.input_pos = causal ? input_pos : 0;
-    p.window = causal ? window : 0;
-    p.c = (float)((double)scale * 1.4426950408889634073599246810019);  // scale * log2(e)
-    p.group = Hq / Hkv;
-    p.n_tiles = (Sq + bmp - 1) / bmp;
+    p.q = a.q;
+    p.k = a.k;
+    p.v = a.v;
+    p.o = a.out;
+    p.lse = a.lse;
+    p.B = a.B;
+    p.Hq = a.Hq;
+    p.Hkv = a.Hkv;
+    p.Sq = a.Sq;
+    p.Skv = a.Skv;
+    p.input_pos = a.causal ? a.input_pos : 0;
+    p.window = a.causal ? a.window : 0;
+    // scale * log2(e), with the fp8 dequantisation factors of q and k folded in.
+    double c2 = (double)a.scale * 1.4426950408889634073599246810019;
+    if (a.qk8) c2 *= (double)a.q_descale * (double)a.k_descale;
+    p.c = (float)c2;
+    p.group = a.Hq / a.Hkv;
+    p.n_tiles = (a.Sq + bmp - 1) / bmp;
     p.hsub = p.group / c.HPW;
     p.num_splits = num_splits;
     p.o_part = nullptr;
     p.lse_part = nullptr;
     if (num_splits > 1) {
-        const size_t rows = (size_t)B * Hq * Sq;
+        const size_t rows = (size_t)a.B * a.Hq * a.Sq;
         p.o_part = (float*)workspace;
         p.lse_part = (float*)workspace + (size_t)num_splits * rows * c.D;
     }
-    const long long wgs = (long long)p.n_tiles * p.hsub * B * Hkv * num_splits;
+    const long long wgs = (long long)p.n_tiles * p.hsub * a.B * a.Hkv * num_splits;
     if (wgs > 0x7fffffffLL) return FA_ERR_INVALID_SHAPE;
-    xcd_mapping(B * Hkv, p.n_tiles * p.hsub * num_splits, &p.map_mode, &p.map_arg);
+    xcd_mapping(a.B * a.Hkv, p.n_tiles * p.hsub * num_splits, &p.map_mode, &p.map_arg);
     hipStream_t s = (hipStream_t)stream;
     if (c.launch(p, s) != hipSuccess) return FA_ERR_LAUNCH;
     if (num_splits > 1 && launch_merge(p, c.D, c.bf16, s) != hipSuccess) return FA_ERR_LAUNCH;
     return FA_OK;
 }
 
-int run(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
-        int Hkv, int Sq, int Skv, int D, float scale, int causal, int input_pos, int window,
-        int dtype, void* stream, int config) {
-    int rc = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos,
-                      window, dtype);
+int run(const Call& a, void* stream, int config) {
+    int rc = validate(a);
     if (rc != FA_OK) return rc;
-    config = resolve_config(config, B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype);
+    config = resolve_config(config, a);
     if (config < 0) return config;
-    if ((long long)B * Hq * Sq == 0) return FA_OK;
-    return launch(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, scale, causal, input_pos, window,
-                  config, 1, nullptr, stream);
+    if ((long long)a.B * a.Hq * a.Sq == 0) return FA_OK;
+    return launch(a, config, 1, nullptr, stream);
 }
 
-int run_splitkv(const void* q, const void* k, const void* v, void* out, float* lse, int B,
-                int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal, int input_pos,
-                int window, int dtype, int num_splits, int config, void* workspace,
+int run_splitkv(const Call& a, int num_splits, int config, void* workspace,
                 size_t workspace_bytes, void* stream) {
-    int rc = validate(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos,
-                      window, dtype);
+    int rc = validate(a);
     if (rc != FA_OK) return rc;
-    config = resolve_config(config, B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype);
+    config = resolve_config(config, a);
     if (config < 0) return config;
     if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_INVALID_SPLITS;
     const ConfigEntry& c = kConfigs[config];
-    if (num_splits == 0)
-        num_splits = auto_splits(c, grid_of(c, B, Hq, Hkv, Sq), B, Hq, Hkv, Sq, Skv, causal,
-                                 causal ? input_pos : 0, causal ? window : 0);
-    if ((long long)B * Hq * Sq == 0) return FA_OK;
+    if (num_splits == 0) num_splits = auto_splits(c, a);
+    if ((long long)a.B * a.Hq * a.Sq == 0) return FA_OK;
     if (num_splits > 1) {
-        const size_t need = workspace_bytes_for(B, Hq, Sq, D, num_splits);
+        const size_t need = workspace_bytes_for(a.B, a.Hq, a.Sq, a.D, num_splits);
         if (!workspace) return FA_ERR_NULL_POINTER;
         if ((uintptr_t)workspace & 15u) return FA_ERR_MISALIGNED;
         if (workspace_bytes < need) return FA_ERR_WORKSPACE;
-        const size_t qb = (size_t)B * Hq * Sq * D * 2, kb = (size_t)B * Hkv * Skv * D * 2;
-        const size_t lb = (size_t)B * Hq * Sq * 4;
+        const size_t qke = a.qk8 ? 1 : 2;
+        const size_t qb = (size_t)a.B * a.Hq * a.Sq * a.D * qke;
+        const size_t kb = (size_t)a.B * a.Hkv * a.Skv * a.D * qke;
+        const size_t ob = (size_t)a.B * a.Hq * a.Sq * a.D * 2;
+        const size_t vb = (size_t)a.B * a.Hkv * a.Skv * a.D * 2;
+        const size_t lb = (size_t)a.B * a.Hq * a.Sq * 4;
         const uintptr_t w = (uintptr_t)workspace;
-        if (overlaps(w, need, (uintptr_t)q, qb) || overlaps(w, need, (uintptr_t)k, kb) ||
-            overlaps(w, need, (uintptr_t)v, kb) || overlaps(w, need, (uintptr_t)out, qb) ||
-            overlaps(w, need, (uintptr_t)lse, lb))
+        if (overlaps(w, need, (uintptr_t)a.q, qb) || overlaps(w, need, (uintptr_t)a.k, kb) ||
+            overlaps(w, need, (uintptr_t)a.v, vb) || overlaps(w, need, (uintptr_t)a.out, ob) ||
+            overlaps(w, need, (uintptr_t)a.lse, lb))
             return FA_ERR_ALIAS;
     }
-    return launch(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, scale, causal, input_pos, window,
-                  config, num_splits, workspace, stream);
+    return launch(a, config, num_splits, workspace, stream);
+}
+
+Call make_call(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+               int Hkv, int Sq, int Skv, int D, float scale, int causal, int input_pos,
+               int window, int dtype) {
+    Call a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.lse = lse;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Sq = Sq;
+    a.Skv = Skv;
+    a.D = D;
+    a.scale = scale;
+    a.causal = causal;
+    a.input_pos = input_pos;
+    a.window = window;
+    a.dtype = dtype;
+    a.qk8 = 0;
+    a.q_descale = 1.0f;
+    a.k_descale = 1.0f;
+    return a;
 }
 
 }  // namespace
@@ -334,14 +382,16 @@ extern "C" {
 int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
            int Hkv, int Sq, int Skv, int D, float scale, int causal, int input_pos, int dtype,
            void* stream) {
-    return run(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos, 0, dtype,
+    return run(make_call(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos, 0,
+                         dtype),
                stream, -1);
 }
 
 int fa_fwd_config(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                   int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
                   int input_pos, int dtype, void* stream, int config) {
-    return run(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos, 0, dtype,
+    return run(make_call(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos, 0,
+                         dtype),
                stream, config);
 }
 
@@ -349,16 +399,30 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* out, float*
                   int Hq, int Hkv, int Sq, int Skv, int D, float scale, int input_pos,
                   int window, int dtype, void* stream, int config) {
     // window < 1 is invalid here; -1 lets validate() report it in its documented place.
-    return run(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, 1, input_pos,
-               window < 1 ? -1 : window, dtype, stream, config);
+    return run(make_call(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, 1, input_pos,
+                         window < 1 ? -1 : window, dtype),
+               stream, config);
+}
+
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+               int Hq, int Hkv, int Sq, int Skv, int D, float scale, float q_descale,
+               float k_descale, int causal, int input_pos, int window, int v_dtype,
+               void* stream, int config) {
+    Call a = make_call(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos,
+                       window, v_dtype);
+    a.qk8 = 1;
+    a.q_descale = q_descale;
+    a.k_descale = k_descale;
+    return run(a, stream, config);
 }
 
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                    int Hq, int Hkv, int Sq, int Skv, int D, float scale, int causal,
                    int input_pos, int window, int dtype, int num_splits, int config,
                    void* workspace, size_t workspace_bytes, void* stream) {
-    return run_splitkv(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos,
-                       window, dtype, num_splits, config, workspace, workspace_bytes, stream);
+    return run_splitkv(make_call(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal,
+                                 input_pos, window, dtype),
+                       num_splits, config, workspace, workspace_bytes, stream);
 }
 
 int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
@@ -369,11 +433,11 @@ int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Sq, int Skv, int D, int ca
     if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
     if (input_pos < 0 || (long long)input_pos + Sq > INT_MAX) return FA_ERR_INVALID_INPUT_POS;
     if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_WINDOW;
-    config = resolve_config(config, B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype);
+    const Call a = make_call(nullptr, nullptr, nullptr, nullptr, nullptr, B, Hq, Hkv, Sq, Skv, D,
+                             1.0f, causal, input_pos, window, dtype);
+    config = resolve_config(config, a);
     if (config < 0) return config;
-    const ConfigEntry& c = kConfigs[config];
-    return auto_splits(c, grid_of(c, B, Hq, Hkv, Sq), B, Hq, Hkv, Sq, Skv, causal,
-                       causal ? input_pos : 0, causal ? window : 0);
+    return auto_splits(kConfigs[config], a);
 }
 
 size_t fa_splitkv_workspace_size(int B, int Hq, int Sq, int D, int num_splits) {
@@ -388,7 +452,17 @@ int fa_select_config(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
     if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
     if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
     if (input_pos < 0) return FA_ERR_INVALID_INPUT_POS;
-    const int c = select(B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype);
+    (void)Skv;
+    const int c = select(B, Hq, Hkv, Sq, D, causal, dtype, 0);
+    return c < 0 ? FA_ERR_INVALID_CONFIG : c;
+}
+
+int fa_select_config_fp8(int B, int Hq, int Hkv, int Sq, int D, int causal, int v_dtype) {
+    if (B < 0 || Hq < 0 || Sq < 0 || Hkv < 1) return FA_ERR_INVALID_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_HEAD_GROUP;
+    if (D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (v_dtype != FA_DTYPE_FP16 && v_dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
+    const int c = select(B, Hq, Hkv, Sq, D, causal, v_dtype, 1);
     return c < 0 ? FA_ERR_INVALID_CONFIG : c;
 }
 

@@ -72,6 +72,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -101,7 +102,7 @@ struct Params {
 };
 
 // Compile-time configuration of one kernel instance.
-template <int D_, int BN_, int QB_, int WPH_, int HPW_, bool CAUSAL_, bool BF16_>
+template <int D_, int BN_, int QB_, int WPH_, int HPW_, bool CAUSAL_, bool BF16_, bool QK8_ = false>
 struct Cfg {
     static constexpr int D = D_;        // head dim
     static constexpr int BN = BN_;      // keys per K/V tile
@@ -109,7 +110,8 @@ struct Cfg {
     static constexpr int WPH = WPH_;    // waves per head (along positions)
     static constexpr int HPW = HPW_;    // heads per workgroup
     static constexpr bool CAUSAL = CAUSAL_;
-    static constexpr bool BF16 = BF16_;
+    static constexpr bool BF16 = BF16_;    // V / O element type: bf16, else fp16
+    static constexpr bool QK8 = QK8_;      // Q and K in fp8 e4m3 (S = K Q^T on the fp8 MFMA)
     static constexpr int NW = WPH * HPW;
     static constexpr int NT = 64 * NW;
     static constexpr int BMP = 32 * QB * WPH;   // query positions per workgroup
@@ -118,6 +120,7 @@ struct Cfg {
     static_assert(BN == 32 || BN == 64, "key tile");
     static_assert(QB == 1 || QB == 2, "query blocks per wave");
     static_assert(NW == 4 || NW == 8, "waves per workgroup");
+    static_assert(!QK8 || (D == 128 && BN == 32 && QB == 1), "fp8 Q/K: head dim 128, 32-key tiles");
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -154,6 +157,13 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
     }
+}
+
+// D(32x32, fp32) += A(32x64) * B(64x32) with fp8 e4m3 A and B (unit block scales).  Lane l
+// holds row / column l mod 32 and the 32 k-elements 32*(l/32) .. +31 of the 64, in order, in
+// its 8 registers; any ordering of k works as long as A and B share it (probe-checked).
+__device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0x7f, 0, 0x7f);
 }
 
 // 8 bytes (4 x 16 bit) of a transposed LDS read; see the header comment for the lanes.
@@ -229,10 +239,18 @@ void fa_fwd_kernel(Params p) {
     constexpr int KB = BN / 32;          // 32-key blocks per tile
     constexpr int DK = D / 16;           // k-steps of Q K^T
     constexpr int DB = D / 32;           // 32-wide d blocks of O
-    constexpr int ROWB = D * 2;          // bytes per K/V row
-    constexpr int TILE = BN * ROWB;      // bytes per K (or V) tile
-    constexpr int CPR = D / 8;           // 16-byte chunks per row
-    constexpr int LD = BN * CPR / NT;    // 16-byte chunks of each tile per thread
+    constexpr bool QK8 = C::QK8;
+    constexpr int ROWB = D * 2;          // bytes per V row (and K row unless fp8)
+    constexpr int TILE = BN * ROWB;      // bytes per V tile
+    constexpr int CPR = D / 8;           // 16-byte chunks per V row
+    constexpr int LD = BN * CPR / NT;    // 16-byte chunks of each V tile per thread
+    constexpr int ROWK = QK8 ? D : ROWB; // bytes per K row
+    constexpr int TILEK = BN * ROWK;     // bytes per K tile
+    constexpr int CPRK = ROWK / 16;      // 16-byte chunks per K row
+    constexpr int NLK = BN * CPRK / 64;  // 64-lane loads per K tile
+    constexpr int NWK = NLK < C::NW ? NLK : C::NW;   // waves that load K
+    constexpr int LDK = NLK / NWK;       // K loads per loading thread
+    static_assert(NLK % NWK == 0, "K tile loads per wave");
     constexpr float P_LIMIT = 32768.0f;  // lazy max: largest partial row sum of p allowed
     constexpr float LN2 = 0.69314718055994530942f;
     static_assert(BN * CPR % NT == 0, "tile chunks per thread");
@@ -275,20 +293,33 @@ void fa_fwd_kernel(Params p) {
     const int qw0 = q0 + (w % WPH) * (32 * QB);
 
     typedef uint16_t T;
-    const T* qp = (const T*)p.q + (size_t)(b * p.Hq + hq) * p.Sq * D;
-    const T* kp = (const T*)p.k + (size_t)(b * p.Hkv + kvh) * p.Skv * D;
+    constexpr int QE = QK8 ? 1 : 2;   // bytes per Q / K element
+    const unsigned char* qp = (const unsigned char*)p.q + (size_t)(b * p.Hq + hq) * p.Sq * D * QE;
+    const unsigned char* kp = (const unsigned char*)p.k + (size_t)(b * p.Hkv + kvh) * p.Skv * D * QE;
     const T* vp = (const T*)p.v + (size_t)(b * p.Hkv + kvh) * p.Skv * D;
 
     // Queries of this wave, as the B operand of S^T = K Q^T: lane l holds row l%32 of
     // query block qb, elements dk*16 + 8*(l/32) .. +8.  Rows past Sq read row Sq-1; their
     // results are never stored.
-    u32x4 qf[QB][DK];
+    // fp8: lane l holds bytes 64*dk + 32*(l/32) .. +31 of its row for the fp8 MFMA's k-range.
+    constexpr int DK8 = D / 64;
+    u32x4 qf[QK8 ? 1 : QB][QK8 ? 1 : DK];
+    i32x8 qf8[QK8 ? QB : 1][DK8];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int row = min(qw0 + qb * 32 + l32, p.Sq - 1);
-        const u32x4* src = (const u32x4*)(qp + (size_t)row * D);
+        const u32x4* src = (const u32x4*)(qp + (size_t)row * D * QE);
+        if constexpr (QK8) {
 #pragma unroll
-        for (int dk = 0; dk < DK; ++dk) qf[qb][dk] = src[dk * 2 + h];
+            for (int dk = 0; dk < DK8; ++dk) {
+                const u32x4 lo = src[dk * 4 + 2 * h], hi = src[dk * 4 + 2 * h + 1];
+                qf8[qb][dk] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            }
+        } else {
+#pragma unroll
+            for (int dk = 0; dk < DK; ++dk) qf[qb][dk] = src[dk * 2 + h];
+        }
     }
 
     // Loop bounds.  Workgroup: tiles [tb, Tc); tiles [f0, f1) need no mask (K-loop split),
@@ -335,7 +366,7 @@ void fa_fwd_kernel(Params p) {
     // LDS: K(t0+i) lives in k_lds[i%3] and V(t0+i) in v_lds[i%3].  Six separate arrays, so
     // the compiler can tell a direct-to-LDS load into one from reads of another and does
     // not wait for the load before those reads; the step-end barrier publishes it.
-    __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILE], k_lds1[TILE], k_lds2[TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILEK], k_lds1[TILEK], k_lds2[TILEK];
     __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TILE], v_lds1[TILE], v_lds2[TILE];
     auto kl = [&](auto ph) -> unsigned char* {
         constexpr int P = decltype(ph)::value;
@@ -353,13 +384,19 @@ void fa_fwd_kernel(Params p) {
     // The row of a slot advances by 64*NW/CPR rows per load i; that is a multiple of 16, so
     // the swizzles (row mod 16) do not depend on i: one per-lane offset plus i * stride.
     static_assert((64 * C::NW / CPR) % 16 == 0, "load stride keeps the swizzle");
-    constexpr int LOAD_STRIDE = 64 * C::NW * 16;   // bytes of tile per load i
+    static_assert((64 * NWK / CPRK) % 16 == 0, "K load stride keeps the swizzle");
+    constexpr int LOAD_STRIDE = 64 * C::NW * 16;   // bytes of V tile per load i
+    constexpr int LOAD_STRIDE_K = 64 * NWK * 16;   // bytes of K tile per load i
+    // K rows of 128 bytes (fp8) use the 8-chunk swizzle of the head-dim-64 bf16 layout.
+    constexpr int KSWZ_D = QK8 ? 64 : D;
+    auto kswz = [&](int row) { return k_swz<KSWZ_D>(row); };
     int ksrc, vsrc;
     {
         const int slot = w * 64 + lane;
         const int row = slot / CPR, pc = slot % CPR;
-        ksrc = row * ROWB + ((pc ^ k_swz<D>(row)) << 4);
         vsrc = row * ROWB + ((pc ^ v_swz<D>(row)) << 4);
+        const int rowk = slot / CPRK, pck = slot % CPRK;
+        ksrc = rowk * ROWK + ((pck ^ kswz(rowk)) << 4);
     }
     // One buffer resource per tile, ending at the tile's last valid key; load i adds
     // i * LOAD_STRIDE as the scalar offset (gfx950's range check covers voffset + soffset,
@@ -371,13 +408,27 @@ void fa_fwd_kernel(Params p) {
         for (int i = 0; i < LD; ++i)
             buffer_load_lds16(r, dst + (i * C::NW + w) * 1024, src, i * LOAD_STRIDE);
     };
+    // K tiles: waves w < NWK load LDK chunks per lane (all waves unless fp8).
+    auto fetch_k = [&](int j, unsigned char* dst) FA_INLINE {
+        const int j0 = min(j * BN, kend);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(kp + (size_t)j0 * ROWK, min(kend - j0, BN) * ROWK);
+        if (NWK == C::NW || w < NWK) {
+#pragma unroll
+            for (int i = 0; i < LDK; ++i)
+                buffer_load_lds16(r, dst + (i * NWK + w) * 1024, ksrc, i * LOAD_STRIDE_K);
+        }
+    };
 
     // Per-lane LDS offsets.  K operand: row kb*32 + l32, chunk (2dk + h) ^ k_swz(row); the
     // swizzle depends only on l32, so chunk = (2dk) ^ ku with ku = h ^ k_swz(l32).
+    // fp8: chunks 4dk + 2h and 4dk + 2h + 1 of row l32 (physical chunks c and c ^ 1, since
+    // 4dk + 2h is even) hold the lane's 32 k-bytes.
     const int ku = h ^ k_swz<D>(l32);
-    int koff[DK];
+    int koff[QK8 ? DK8 : DK];
 #pragma unroll
-    for (int dk = 0; dk < DK; ++dk) koff[dk] = l32 * ROWB + (((2 * dk) ^ ku) << 4);
+    for (int dk = 0; dk < (QK8 ? DK8 : DK); ++dk)
+        koff[dk] = QK8 ? l32 * ROWK + (((4 * dk + 2 * h) ^ kswz(l32)) << 4)
+                       : l32 * ROWB + (((2 * dk) ^ ku) << 4);
     // V^T operand (two transpose reads per MFMA): this lane addresses key
     // 4*h + jj (+ kb*32 + 16*hf + 8*r) and the 8-byte piece of d = db*32 + 16*(qq&1) +
     // 8*(g&1) + 4*(qq>>1), with jj, qq from the lane's index in its 16-lane group g.
@@ -395,11 +446,23 @@ void fa_fwd_kernel(Params p) {
         for (int k2 = 0; k2 < KB; ++k2) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) s[k2][qb] = (f32x16){};
+            if constexpr (QK8) {
 #pragma unroll
-            for (int dk = 0; dk < DK; ++dk) {
-                const u32x4 a = *(const u32x4*)(kb + k2 * 32 * ROWB + koff[dk]);
+                for (int dk = 0; dk < DK8; ++dk) {
+                    const u32x4 lo = *(const u32x4*)(kb + k2 * 32 * ROWK + koff[dk]);
+                    const u32x4 hi = *(const u32x4*)(kb + k2 * 32 * ROWK + (koff[dk] ^ 16));
+                    const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) s[k2][qb] = mfma32<BF16>(a, qf[qb][dk], s[k2][qb]);
+                    for (int qb = 0; qb < QB; ++qb) s[k2][qb] = mfma32_fp8(a, qf8[qb][dk], s[k2][qb]);
+                }
+            } else {
+#pragma unroll
+                for (int dk = 0; dk < DK; ++dk) {
+                    const u32x4 a = *(const u32x4*)(kb + k2 * 32 * ROWB + koff[dk]);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) s[k2][qb] = mfma32<BF16>(a, qf[qb][dk], s[k2][qb]);
+                }
             }
         }
     };
@@ -434,11 +497,18 @@ void fa_fwd_kernel(Params p) {
     // End of a step: wait until this wave's loads issued one step earlier have landed
     // (the loads of this step, 2*LD of them, may stay in flight), then the workgroup
     // barrier.  The asm is a compiler memory barrier as well.
-    auto end_step = [&]() FA_INLINE {
-        constexpr int N = 2 * LD;
-        constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+    // s_waitcnt vmcnt(N) then s_barrier, as one asm statement (also a compiler memory
+    // barrier).
+    auto wait_barrier = [&](auto n_tag) FA_INLINE {
+        constexpr int N = decltype(n_tag)::value;
         static_assert(N < 64, "vmcnt range");
+        constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
         asm volatile("s_waitcnt %0\n\ts_barrier" ::"n"(imm) : "memory");
+    };
+    // A wave issues LDK K loads (if it loads K) and LD V loads per step.
+    auto end_step = [&]() FA_INLINE {
+        if (NWK == C::NW || w < NWK) wait_barrier(std::integral_constant<int, LDK + LD>{});
+        else wait_barrier(std::integral_constant<int, LD>{});
     };
 
     // One K-loop step for tile j (phase PH = (j - t0) % 3), a three-stage software
@@ -459,7 +529,7 @@ void fa_fwd_kernel(Params p) {
         auto& s_nxt = pick(N1{}, s0, s1, s2);
         auto& pk_cur = pick(ph_tag, pk0, pk1, pk2);
         auto& pk_prev = pick(N2{}, pk0, pk1, pk2);
-        fetch(kp, j + 3, kl(ph_tag), ksrc);
+        fetch_k(j + 3, kl(ph_tag));
         fetch(vp, j + 1, vl(N1{}), vsrc);
         const bool do_sm = !MASKED || (j >= wave_lo && j < wave_tc);   // softmax of tile j
         const bool do_pv = !FIRST && (!MASKED || (j - 1 >= wave_lo && j - 1 < wave_tc));   // P V of tile j-1
@@ -558,15 +628,13 @@ void fa_fwd_kernel(Params p) {
     using F = std::false_type;
     using TT = std::true_type;
     if (nt > 0) {
-        fetch(kp, t0, k_lds0, ksrc);
-        fetch(kp, t0 + 1, k_lds1, ksrc);
-        fetch(kp, t0 + 2, k_lds2, ksrc);
+        fetch_k(t0, k_lds0);
+        fetch_k(t0 + 1, k_lds1);
+        fetch_k(t0 + 2, k_lds2);
         fetch(vp, t0, v_lds0, vsrc);
-        {
-            constexpr int N = 3 * LD;   // K(t0) landed; the other three tiles may be in flight
-            constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
-            asm volatile("s_waitcnt %0\n\ts_barrier" ::"n"(imm) : "memory");
-        }
+        // K(t0) landed; K(t0+1), K(t0+2) and V(t0) may be in flight.
+        if (NWK == C::NW || w < NWK) wait_barrier(std::integral_constant<int, 2 * LDK + LD>{});
+        else wait_barrier(std::integral_constant<int, LD>{});
         qk(k_lds0, s0);
         end_step();   // K(t0+1) and K(t0+2) landed
 

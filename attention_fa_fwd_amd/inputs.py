@@ -42,21 +42,59 @@ WORKLOADS = {
 }
 
 
+# Workloads with fp8 E4M3 queries and keys (per-tensor descale factors) and fp16 / bf16
+# values: the headline and the causal multi-head shapes.
+FP8_WORKLOADS = {
+    "gqa8_causal_s8192_d128_fp8qk_bf16": dict(B=1, Hq=32, Hkv=4, Sq=8192, Skv=8192, D=128,
+                                              dtype="bf16", causal=True, input_pos=0),
+    "mha_causal_s4096_d128_fp8qk_fp16": dict(B=1, Hq=32, Hkv=32, Sq=4096, Skv=4096, D=128,
+                                             dtype="fp16", causal=True, input_pos=0),
+}
+
+
 def default_scale(D: int) -> float:
     """1/sqrt(D), the default softmax scale."""
     return 1.0 / math.sqrt(D)
+
+
+def _randn_qkv(B, Hq, Hkv, Sq, Skv, D, seed):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = torch.randn((B, Hq, Sq, D), generator=g, dtype=torch.float32)
+    k = torch.randn((B, Hkv, Skv, D), generator=g, dtype=torch.float32)
+    v = torch.randn((B, Hkv, Skv, D), generator=g, dtype=torch.float32)
+    return q, k, v
 
 
 def make_qkv(B, Hq, Hkv, Sq, Skv, D, dtype, seed=0):
     """Seeded q [B,Hq,Sq,D], k and v [B,Hkv,Skv,D] on the CPU, rounded to ``dtype``."""
     if isinstance(dtype, str):
         dtype = DTYPES[dtype]
-    g = torch.Generator(device="cpu")
-    g.manual_seed(int(seed))
-    q = torch.randn((B, Hq, Sq, D), generator=g, dtype=torch.float32).to(dtype)
-    k = torch.randn((B, Hkv, Skv, D), generator=g, dtype=torch.float32).to(dtype)
-    v = torch.randn((B, Hkv, Skv, D), generator=g, dtype=torch.float32).to(dtype)
-    return q.contiguous(), k.contiguous(), v.contiguous()
+    q, k, v = _randn_qkv(B, Hq, Hkv, Sq, Skv, D, seed)
+    return q.to(dtype).contiguous(), k.to(dtype).contiguous(), v.to(dtype).contiguous()
+
+
+FP8_MAX = 448.0   # largest finite fp8 E4M3 (OCP "E4M3FN") value
+
+
+def quantize_fp8(x):
+    """Per-tensor fp8 E4M3 quantisation of a float32 tensor: descale = amax / 448 and
+    codes = round-to-nearest-even(x / descale) (torch's conversion), so that
+    descale * codes approximates x.  Returns (codes as torch.float8_e4m3fn, descale)."""
+    amax = float(x.abs().max()) if x.numel() else 1.0
+    descale = (amax / FP8_MAX) if amax > 0 else 1.0
+    return (x / descale).to(torch.float8_e4m3fn).contiguous(), descale
+
+
+def make_qkv_fp8(B, Hq, Hkv, Sq, Skv, D, v_dtype, seed=0):
+    """The same seeded draws as ``make_qkv``, with q and k quantised to fp8 E4M3 per
+    tensor and v rounded to ``v_dtype``.  Returns (q8, k8, v, q_descale, k_descale)."""
+    if isinstance(v_dtype, str):
+        v_dtype = DTYPES[v_dtype]
+    q, k, v = _randn_qkv(B, Hq, Hkv, Sq, Skv, D, seed)
+    q8, qd = quantize_fp8(q)
+    k8, kd = quantize_fp8(k)
+    return q8, k8, v.to(v_dtype).contiguous(), qd, kd
 
 
 def make_workload(name, seed=0):
@@ -66,3 +104,13 @@ def make_workload(name, seed=0):
     kw = dict(scale=default_scale(w["D"]), causal=w["causal"], input_pos=w["input_pos"],
               window=w.get("window", 0))
     return q, k, v, kw
+
+
+def make_fp8_workload(name, seed=0):
+    """Inputs and call arguments for a named fp8 workload: (q8, k8, v, kwargs)."""
+    w = dict(FP8_WORKLOADS[name])
+    q8, k8, v, qd, kd = make_qkv_fp8(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"],
+                                     w["dtype"], seed)
+    kw = dict(scale=default_scale(w["D"]), causal=w["causal"], input_pos=w["input_pos"],
+              window=w.get("window", 0), q_descale=qd, k_descale=kd)
+    return q8, k8, v, kw

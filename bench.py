@@ -38,8 +38,12 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd TFLOP/s and % of MI355X dense bf16 MFMA peak (causal, D=128)"
 HEADLINE = "gqa8_causal_s8192_d128_bf16"
-# MI355X dense bf16/fp16 MFMA peak: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU.
+# MI355X dense bf16/fp16 MFMA peak: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU; fp8 twice that.
 PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+PEAK_FP8_TFLOPS = 2 * PEAK_TFLOPS
+# fp8 Q/K workloads: half the FLOPs (Q K^T) at the fp8 peak, half (P V) at the bf16 one.
+PEAK_FP8QK_TFLOPS = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_TFLOPS)
+METRIC_FP8 = "attention fwd TFLOP/s, fp8 E4M3 Q/K (Q K^T on the fp8 MFMA), fp16/bf16 P V"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.json")
 MIN_WARMUP_S = 0.3
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
@@ -113,23 +117,40 @@ def algorithmic_bytes(w):
     return qo + kv + w["B"] * w["Hq"] * w["Sq"] * 4
 
 
+def workload(name):
+    """(shape dict, is fp8) of a named workload."""
+    from attention_fa_fwd_amd.inputs import FP8_WORKLOADS, WORKLOADS
+
+    if name in FP8_WORKLOADS:
+        return FP8_WORKLOADS[name], True
+    return WORKLOADS[name], False
+
+
 def time_gpu(name, steps, warmup, config=-1, splitkv=False):
     import torch
 
     import attention_fa_fwd_amd as fa
-    from attention_fa_fwd_amd.inputs import WORKLOADS, make_workload
+    from attention_fa_fwd_amd.inputs import make_fp8_workload, make_workload
 
-    w = WORKLOADS[name]
+    w, fp8 = workload(name)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    q, k, v, kw = make_workload(name, seed=0)
+    if fp8:
+        q, k, v, kw = make_fp8_workload(name, seed=0)
+    else:
+        q, k, v, kw = make_workload(name, seed=0)
     q, k, v = q.to(dev), k.to(dev), v.to(dev)
-    out = torch.empty_like(q)
+    out = torch.empty(q.shape, dtype=v.dtype, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     splits = 1
-    if splitkv:
+    if fp8:
+        def step():
+            fa.fa_fwd_fp8_into(q, k, v, out, lse, kw["q_descale"], kw["k_descale"],
+                               scale=kw["scale"], causal=kw["causal"], input_pos=kw["input_pos"],
+                               window=kw["window"], config=config, stream=sp)
+    elif splitkv:
         splits = fa.splitkv_num_splits(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"],
                                        w["causal"], w["input_pos"], q.dtype, config,
                                        kw["window"])
@@ -167,8 +188,13 @@ def time_gpu(name, steps, warmup, config=-1, splitkv=False):
     wall = time.perf_counter() - t0
     per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))  # ms per launch
     total_ms = evs[0].elapsed_time(evs[-1])
-    cfg = config if config >= 0 else fa.select_config(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"],
-                                                      w["D"], w["causal"], w["input_pos"], q.dtype)
+    if config >= 0:
+        cfg = config
+    elif fp8:
+        cfg = fa.select_config_fp8(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["D"], w["causal"], v.dtype)
+    else:
+        cfg = fa.select_config(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"], w["causal"],
+                               w["input_pos"], q.dtype)
     return dict(total_ms=total_ms, wall_s=wall, per_ms=per, kernel=fa.config_names()[cfg],
                 warmup_extra=extra, splits=splits)
 
@@ -203,9 +229,7 @@ def cpu_baseline(name):
 
 
 def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False):
-    from attention_fa_fwd_amd.inputs import WORKLOADS
-
-    w = WORKLOADS[name]
+    w, fp8 = workload(name)
     log(f"workload {name}: {w}")
     r = time_gpu(name, steps, warmup, config, splitkv)
     ms_step = r["total_ms"] / steps
@@ -214,7 +238,7 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False):
     mean_kernel_ms = sum(r["per_ms"]) / len(r["per_ms"])
     med = r["per_ms"][len(r["per_ms"]) // 2]
     p95 = r["per_ms"][min(len(r["per_ms"]) - 1, int(math.ceil(0.95 * len(r["per_ms"]))) - 1)]
-    path = f"fa_fwd_splitkv ({r['splits']} splits)" if splitkv else "fa_fwd"
+    path = "fa_fwd_fp8" if fp8 else f"fa_fwd_splitkv ({r['splits']} splits)" if splitkv else "fa_fwd"
     log(f"{path} kernel {r['kernel']}: mean {mean_kernel_ms * 1e3:.1f} us, median {med * 1e3:.1f} us, "
         f"p95 {p95 * 1e3:.1f} us, min {r['per_ms'][0] * 1e3:.1f} us, "
         f"{r['warmup_extra']} extra warm-up steps")
@@ -227,9 +251,10 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False):
                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
     else:
         achieved = flops / (mean_kernel_ms * 1e-3) / 1e12
-        metric, unit = METRIC, "TFLOP/s"
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_TFLOPS, 1),
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+        metric, unit = (METRIC_FP8 if fp8 else METRIC), "TFLOP/s"
+        peak = PEAK_FP8QK_TFLOPS if fp8 else PEAK_TFLOPS
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                     "traffic": None if splitkv else traffic_bytes(name)}
     line = {
         "metric": metric,
@@ -243,7 +268,7 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w["dtype"],
+        "dtype": f"fp8e4m3 q/k, {w['dtype']} v" if fp8 else w["dtype"],
         "data": "synthetic: seeded N(0,1) q, k, v rounded to the storage dtype",
         "config": {"workload": name, "B": w["B"], "Hq": w["Hq"], "Hkv": w["Hkv"], "Sq": w["Sq"],
                    "Skv": w["Skv"], "D": w["D"], "causal": w["causal"],
@@ -255,9 +280,9 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False):
         "roofline": roofline,
     }
     if not decode:
-        line["pct_of_peak"] = round(100.0 * value / PEAK_TFLOPS, 2)
+        line["pct_of_peak"] = round(100.0 * value / (PEAK_FP8QK_TFLOPS if fp8 else PEAK_TFLOPS), 2)
         line["tflops_exact_pairs"] = round(exact_flops(w) / (ms_step * 1e-3) / 1e12, 2)
-    if with_cpu:
+    if with_cpu and not fp8:
         log("timing the fp64 CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(name)
     return line
@@ -308,10 +333,10 @@ def main(argv=None):
     line = bench_line(a.workload, a.steps, a.warmup, a.config, with_cpu=not a.no_cpu_baseline,
                       splitkv=a.splitkv)
     if a.all:
-        from attention_fa_fwd_amd.inputs import WORKLOADS
+        from attention_fa_fwd_amd.inputs import FP8_WORKLOADS, WORKLOADS
 
-        for name in WORKLOADS:
-            runs = [False, True] if WORKLOADS[name]["Sq"] <= 16 else [False]
+        for name in list(WORKLOADS) + list(FP8_WORKLOADS):
+            runs = [False, True] if name in WORKLOADS and WORKLOADS[name]["Sq"] <= 16 else [False]
             for split in runs:
                 if name == a.workload and split == a.splitkv:
                     continue

@@ -115,6 +115,34 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* out, float*
                   int input_pos, int window, int dtype, void* stream, int config);
 
 /*
+ * Attention with fp8 queries and keys: q [B,Hq,Sq,D] and k [B,Hkv,Skv,D] hold fp8 E4M3
+ * codes (the OCP "E4M3FN" format gfx950's MFMA reads: 1 sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, no infinities, largest finite value 448); v and out are fp16 / bf16
+ * (v_dtype); lse fp32.  The real inputs are q_descale * q and k_descale * k (one factor per
+ * tensor), so
+ *     S = (scale * q_descale * k_descale) * (q_codes . k_codes)
+ * and the rest is fa_fwd's (masking, window, softmax, P in v_dtype, O, LSE).  The pages give
+ * no low-precision scaling rule; per-tensor dequantisation factors are the plainest one.
+ * S = K Q^T runs on gfx950's fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4, unit block scales)
+ * with fp32 accumulation, so the scores are the exact products of the fp8 values up to
+ * fp32 rounding; P V stays on the fp16 / bf16 MFMA.
+ *
+ *   D          128 only (FA_ERR_UNSUPPORTED_HEAD_DIM otherwise).
+ *   q_descale, k_descale   finite and > 0 (FA_ERR_INVALID_SCALE), checked after scale.
+ *   window     0 = none, >= 1 = sliding window (needs causal), as for fa_fwd_splitkv.
+ *   config     -1 = the dispatch table (fa_select_config_fp8), else an fp8 configuration.
+ *   the rest   as for fa_fwd; q and k need 16-byte alignment like the other tensors.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse,
+               int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+               float q_descale, float k_descale, int causal, int input_pos, int window,
+               int v_dtype, void* stream, int config);
+
+/* Configuration fa_fwd_fp8 picks for these sizes (v_dtype: an fa_dtype), or a negative
+ * fa_status. */
+int fa_select_config_fp8(int B, int Hq, int Hkv, int Sq, int D, int causal, int v_dtype);
+
+/*
  * Split-KV forward pass, for grids too small to fill the GPU (few heads or short query
  * blocks; decoding with Sq = 1).  The pages motivate it by launches with too few tiles for
  * the processors ("Tuning Flash Attention for peak performance in NVIDIA CUDA Tile", Part 2

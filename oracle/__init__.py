@@ -8,12 +8,14 @@ from .attention import (  # noqa: F401
     LN2,
     LOG2E,
     attention_blocked,
+    attention_fp8_blocked,
     attention_key_range,
     attention_naive,
     attention_online_tiled,
     attention_probs_naive,
     attention_rows,
     classify_tiles,
+    fp8_e4m3_decode,
     kv_head_of,
     key_visibility,
     merge_partials,

@@ -47,6 +47,9 @@ Four forms are provided, written independently of one another:
 * ``attention_key_range`` and ``merge_partials``: the definition over one key
                                range, and the online-softmax fold of several ranges
                                into one result (split-KV).
+* ``fp8_e4m3_decode`` and ``attention_fp8_blocked``: fp8 E4M3 codes decoded
+                               from the format's definition, and the definition over
+                               dequantised fp8 queries and keys.
 
 Parity status: every function here is pinned by the CPU test suite against
 brute force, an independent library routine (PyTorch's CPU float64
@@ -496,3 +499,38 @@ def merge_partials(o_parts, lse_parts):
     O = np.where(nonempty[..., None], acc / np.where(nonempty, l, 1.0)[..., None], 0.0)
     LSE = np.where(nonempty, m + np.log(np.where(nonempty, l, 1.0)), -np.inf)
     return O, LSE
+
+
+# ----------------------------------------------------------------------------
+# fp8 inputs: decoding E4M3 codes, and attention over dequantised q and k
+# ----------------------------------------------------------------------------
+
+def fp8_e4m3_decode(codes):
+    """Values of fp8 E4M3 codes (the OCP "E4M3FN" variant): float64 array.
+
+    Bit layout, sign-exponent-mantissa = 1-4-3, exponent bias 7.  Exponent field 0
+    encodes subnormals m * 2^-9 (and zero); exponent 1..15 encodes (1 + m/8) *
+    2^(e-7), except that exponent 15 with mantissa 7 is NaN -- the format has no
+    infinities, so its largest finite value is 1.75 * 2^8 = 448.  The pages give
+    no low-precision format; this is the one gfx950's fp8 matrix instructions read.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def attention_fp8_blocked(q_codes, k_codes, v, scale, q_descale, k_descale, causal=False,
+                          input_pos=0, window=0):
+    """Attention of fp8-coded queries and keys: the module-docstring definition applied
+    to q = q_descale * decode(q_codes), k = k_descale * decode(k_codes) and v, in
+    float64 (``attention_blocked``).  Returns (O, LSE)."""
+    if not (math.isfinite(q_descale) and q_descale > 0 and math.isfinite(k_descale) and k_descale > 0):
+        raise ValueError("descale factors must be finite and > 0")
+    q = q_descale * fp8_e4m3_decode(q_codes)
+    k = k_descale * fp8_e4m3_decode(k_codes)
+    return attention_blocked(q, k, np.asarray(v, np.float64), scale, causal, input_pos,
+                             window=window)

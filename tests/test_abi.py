@@ -236,3 +236,46 @@ def test_window_split_count(lib):
     assert fa.splitkv_num_splits(4, 32, 8, 1, 16384, 128, True, 16383, 1, window=1024) == 4
     with pytest.raises(fa.FaError):
         fa.splitkv_num_splits(4, 32, 8, 1, 16384, 128, False, 0, 1, window=1024)
+
+
+# --- fp8 queries and keys ------------------------------------------------------------
+
+def call_fp8(lib, qd=0.01, kd=0.02, window=0, config=-1, **over):
+    a = dict(GOOD, **dict(dict(D=128), **over))
+    return lib.fa_fwd_fp8(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                          a["Sq"], a["Skv"], a["D"], a["scale"], qd, kd, a["causal"], a["input_pos"],
+                          window, a["dtype"], None, config)
+
+
+def test_fp8_validation(lib):
+    assert call_fp8(lib, D=64) == -4                      # head dim 128 only
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert call_fp8(lib, qd=bad) == -6
+        assert call_fp8(lib, kd=bad) == -6
+    assert call_fp8(lib, scale=0.0, qd=0.0) == -6
+    assert call_fp8(lib, window=3, causal=0) == -14
+    assert call_fp8(lib, dtype=2) == -5
+    assert call_fp8(lib, Sq=0, q=0, out=0, lse=0) == 0   # empty: no launch
+    # q and k are 1 byte per element: out placed right after q (B*Hq*Sq*D bytes) is legal,
+    # one byte earlier overlaps
+    qbytes = 1 * 4 * 8 * 128
+    assert call_fp8(lib, out=Q + qbytes, Sq=0) == 0
+    assert call_fp8(lib, out=Q + qbytes - 16) == -9
+
+
+def test_fp8_configs(lib):
+    names = fa.config_names()
+    fp8 = [i for i, nm in enumerate(names) if "_fp8qk_" in nm]
+    assert len(fp8) == 24 and all(names[i].startswith("D128_BN32_") for i in fp8)
+    c = fa.select_config_fp8(1, 32, 4, 8192, 128, True, 1)
+    assert names[c] == "D128_BN32_Mw1x32_WPH2_HPW4_causal_fp8qk_bf16"
+    c = fa.select_config_fp8(1, 32, 32, 4096, 128, True, 0)
+    assert names[c] == "D128_BN32_Mw1x32_WPH8_HPW1_causal_fp8qk_fp16"
+    # a bf16 configuration is not applicable to an fp8 call, nor the reverse
+    bf16 = names.index("D128_BN32_Mw1x32_WPH2_HPW4_causal_bf16")
+    assert call_fp8(lib, config=bf16, dtype=1) == -10
+    args = [GOOD[x] for x in ("q", "k", "v", "out", "lse", "B", "Hq", "Hkv", "Sq", "Skv")] + \
+        [128, GOOD["scale"], 1, 0, 1, None]
+    assert lib.fa_fwd_config(*args, fp8[0]) == -10
+    with pytest.raises(fa.FaError):
+        fa.select_config_fp8(1, 32, 4, 8192, 64, True, 1)

@@ -1,0 +1,132 @@
+"""GPU parity of fa_fwd_fp8 (fp8 E4M3 queries and keys, fp16 / bf16 values) against the
+fp64 oracle over the dequantised inputs.
+
+The scores come from exact products of fp8 values accumulated in fp32, so the output
+error has the same sources as the fp16 / bf16 path (P and O rounded to the value type) and
+the same tolerances apply: max |O - O_oracle| <= 4e-3 (fp16) or 1.6e-2 (bf16), max |LSE -
+LSE_oracle| <= 1e-3.
+"""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_fa_fwd_amd as fa
+import oracle
+from attention_fa_fwd_amd.inputs import FP8_WORKLOADS, make_fp8_workload, make_qkv_fp8
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {torch.float16: 4e-3, torch.bfloat16: 1.6e-2}
+TOL_LSE = 1e-3
+DEV = torch.device("cuda:0")
+
+
+def _say(*a):
+    print("[fp8]", *a, file=sys.stderr, flush=True)
+
+
+def _codes(t):
+    return t.view(torch.uint8).numpy()
+
+
+def oracle_fp8(q8, k8, v, scale, qd, kd, causal, pos, window=0):
+    return oracle.attention_fp8_blocked(_codes(q8), _codes(k8), v.double().numpy(), scale, qd, kd,
+                                        causal, pos, window=window)
+
+
+def run(q8, k8, v, qd, kd, scale, causal, pos, window=0, config=-1):
+    out, lse = fa.fa_fwd_fp8(q8.to(DEV), k8.to(DEV), v.to(DEV), qd, kd, scale=scale, causal=causal,
+                             input_pos=pos, window=window, config=config)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def check(O, L, out, lse, dtype, what):
+    o, l = out.double().numpy(), lse.double().numpy()
+    empty = ~np.isfinite(L)
+    assert np.all(l[empty] == -np.inf) and np.all(o[empty] == 0.0), what
+    assert np.isfinite(o).all() and np.isfinite(l[~empty]).all(), f"non-finite {what}"
+    eo = float(np.max(np.abs(o - O))) if o.size else 0.0
+    el = float(np.max(np.abs(l[~empty] - L[~empty]))) if (~empty).any() else 0.0
+    assert eo <= TOL_O[dtype], f"O max abs err {eo:.3e} {what}"
+    assert el <= TOL_LSE, f"LSE max abs err {el:.3e} {what}"
+
+
+FP8_CASES = [
+    # B, Hq, Hkv, Sq, Skv, causal, pos, window
+    (1, 2, 2, 128, 128, False, 0, 0),
+    (2, 4, 4, 300, 300, True, 0, 0),          # several tiles + ragged tail
+    (1, 8, 2, 257, 391, True, 134, 0),        # ragged both, GQA 4, offset
+    (1, 8, 1, 65, 129, False, 0, 0),          # MQA
+    (1, 8, 8, 1, 1, True, 0, 0),              # one query, one key
+    (1, 4, 4, 1, 700, True, 699, 0),          # decode-like row
+    (1, 8, 2, 300, 300, True, 0, 45),         # sliding window
+    (1, 32, 4, 256, 256, True, 0, 0),
+]
+
+
+@pytest.mark.parametrize("vdt", ["fp16", "bf16"])
+@pytest.mark.parametrize("case", FP8_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_fp8_shapes(case, vdt):
+    B, Hq, Hkv, Sq, Skv, causal, pos, W = case
+    _say(case, vdt)
+    q8, k8, v, qd, kd = make_qkv_fp8(B, Hq, Hkv, Sq, Skv, 128, vdt, seed=sum(case) + 7)
+    scale = 1.0 / math.sqrt(128)
+    out, lse = run(q8, k8, v, qd, kd, scale, causal, pos, W)
+    O, L = oracle_fp8(q8, k8, v, scale, qd, kd, causal, pos, W)
+    check(O, L, out, lse, v.dtype, f"{case} {vdt}")
+
+
+@pytest.mark.parametrize("vdt", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_every_config(vdt, causal):
+    q8, k8, v, qd, kd = make_qkv_fp8(1, 8, 2, 333, 333, 128, vdt, seed=21)
+    pos = 7 if causal else 0
+    O, L = oracle_fp8(q8, k8, v, 0.09, qd, kd, causal, pos)
+    tested = 0
+    for cid, name in enumerate(fa.config_names()):
+        if "_fp8qk_" not in name or (("_causal_" in name) != causal) or not name.endswith(vdt):
+            continue
+        _say("config", name)
+        out, lse = run(q8, k8, v, qd, kd, 0.09, causal, pos, config=cid)
+        check(O, L, out, lse, v.dtype, name)
+        tested += 1
+    assert tested == 6
+
+
+def test_fp8_descale_invariance():
+    """Moving a factor of 2 from scale into q_descale gives bit-identical results (the
+    kernel folds both into one fp32 constant computed in double)."""
+    q8, k8, v, qd, kd = make_qkv_fp8(1, 8, 2, 200, 200, 128, "bf16", seed=22)
+    a = run(q8, k8, v, qd, kd, 0.1, True, 0)
+    b = run(q8, k8, v, qd * 2, kd, 0.05, True, 0)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("name", sorted(FP8_WORKLOADS))
+def test_fp8_named_workload(name):
+    w = FP8_WORKLOADS[name]
+    _say("workload", name)
+    q8, k8, v, kw = make_fp8_workload(name, seed=0)
+    out, lse = run(q8, k8, v, kw["q_descale"], kw["k_descale"], kw["scale"], kw["causal"],
+                   kw["input_pos"], kw["window"])
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    rng = np.random.default_rng(3)
+    B, Hq, Sq = w["B"], w["Hq"], w["Sq"]
+    rows = [0, 1, 31, 32, 63, 64, 127, 128, Sq // 2, Sq - 1]
+    samples = [(0, int(rng.integers(Hq)), i) for i in rows]
+    samples += [(0, int(rng.integers(Hq)), int(rng.integers(Sq))) for _ in range(40)]
+    qf = oracle.fp8_e4m3_decode(_codes(q8)) * kw["q_descale"]
+    kf = oracle.fp8_e4m3_decode(_codes(k8)) * kw["k_descale"]
+    O, L = oracle.attention_rows(qf, kf, v.double().numpy(), kw["scale"], kw["causal"],
+                                 kw["input_pos"], samples)
+    o = np.stack([out[b, h, i].double().numpy() for b, h, i in samples])
+    l = np.array([float(lse[b, h, i]) for b, h, i in samples])
+    assert float(np.max(np.abs(o - O))) <= TOL_O[v.dtype]
+    assert float(np.max(np.abs(l - L))) <= TOL_LSE

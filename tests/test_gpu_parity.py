@@ -90,7 +90,7 @@ def test_every_config_on_same_input(dtype, causal):
     names = fa.config_names()
     tested = 0
     for cid, name in enumerate(names):
-        if not name.startswith("D128_") or (("_causal_" in name) != causal) or \
+        if not name.startswith("D128_") or "_fp8qk_" in name or (("_causal_" in name) != causal) or \
                 (("_bf16" in name) != (dtype == "bf16")):
             continue
         _say("config", name)
