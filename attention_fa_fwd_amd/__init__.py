@@ -14,7 +14,7 @@ import math
 import os
 import threading
 
-__all__ = ["fa_fwd", "fa_fwd_into", "fa_fwd_fp8", "fa_fwd_fp8_into", "select_config_fp8", "fa_fwd_splitkv", "fa_fwd_splitkv_into", "splitkv_num_splits",
+__all__ = ["fa_fwd", "fa_fwd_into", "fa_bwd", "fa_bwd_into", "fa_fwd_fp8", "fa_fwd_fp8_into", "select_config_fp8", "fa_fwd_splitkv", "fa_fwd_splitkv_into", "splitkv_num_splits",
            "splitkv_workspace_size", "select_config", "config_names", "num_configs", "FaError",
            "load_library", "LIB_PATH"]
 
@@ -44,6 +44,11 @@ def _declare(lib):
     lib.fa_fwd.restype = _c_int
     lib.fa_fwd_config.argtypes = _FWD_ARGS + [_c_int]
     lib.fa_fwd_config.restype = _c_int
+    lib.fa_bwd.argtypes = [_vp] * 9 + [_c_int] * 6 + [_c_float] + [_c_int] * 4 + [_vp, ctypes.c_size_t,
+                                                                              _vp]
+    lib.fa_bwd.restype = _c_int
+    lib.fa_bwd_workspace_size.argtypes = [_c_int] * 3
+    lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.fa_fwd_fp8.argtypes = _FWD_ARGS[:12] + [_c_float, _c_float, _c_int, _c_int, _c_int, _c_int,
                                                 _vp, _c_int]
     lib.fa_fwd_fp8.restype = _c_int
@@ -327,3 +332,51 @@ def select_config_fp8(B, Hq, Hkv, Sq, D, causal, v_dtype) -> int:
     rc = load_library().fa_select_config_fp8(B, Hq, Hkv, Sq, D, 1 if causal else 0, code)
     _check(rc if rc < 0 else 0)
     return rc
+
+
+def fa_bwd_into(q, k, v, out, lse, dout, dq, dk, dv, workspace, scale=None, causal=True,
+                input_pos=0, window=0, stream=None):
+    """Backward pass into caller-provided dq [B,Hq,Sq,D], dk, dv [B,Hkv,Skv,D] (q's dtype).
+
+    ``out`` and ``lse`` are the forward pass's results for the same arguments;
+    ``workspace`` holds at least ``B*Hq*Sq*4`` bytes (fa_bwd_workspace_size).
+    """
+    import torch
+
+    lib = load_library()
+    B, Hq, Hkv, Sq, Skv, D = _check_tensors(q, k, v, out, lse)
+    for name, t, ref in (("dout", dout, q), ("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
+        if not t.is_cuda or t.device != q.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor on q's device")
+        if tuple(t.shape) != tuple(ref.shape) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must have shape {tuple(ref.shape)} and dtype {q.dtype}")
+    _check_window(causal, window)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    else:
+        ws_ptr, ws_bytes = None, 0
+    with torch.cuda.device(q.device):
+        rc = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv,
+                        Sq, Skv, D, float(scale), 1 if causal else 0, int(input_pos), int(window),
+                        _dtype_code(q.dtype), ws_ptr, ws_bytes, stream)
+    _check(rc)
+    return dq, dk, dv
+
+
+def fa_bwd(q, k, v, out, lse, dout, scale=None, causal=True, input_pos=0, window=0):
+    """Gradients (dq, dk, dv) of the forward pass for upstream gradient ``dout``;
+    allocates the outputs and the workspace with torch."""
+    import torch
+
+    q, k, v, out, dout = (t.contiguous() for t in (q, k, v, out, dout))
+    B, Hq, Sq, D = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = int(load_library().fa_bwd_workspace_size(B, Hq, Sq))
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    return fa_bwd_into(q, k, v, out, lse.contiguous(), dout, dq, dk, dv, ws, scale=scale,
+                       causal=causal, input_pos=input_pos, window=window)

@@ -1,7 +1,8 @@
 """Build the HIP attention library in-tree for gfx950.
 
-``python -m attention_fa_fwd_amd.build`` (or ``build_library()``) compiles
-``csrc/fa_fwd.hip`` with hipcc into ``attention_fa_fwd_amd/libfa_fwd.so``.
+``python -m attention_fa_fwd_amd.build`` (or ``build_library()``) compiles every
+``csrc/*.hip`` with hipcc (one process per file, in parallel) and links them into
+``attention_fa_fwd_amd/libfa_fwd.so``.
 """
 
 from __future__ import annotations
@@ -38,15 +39,38 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def build_library(verbose: bool = True, extra_flags=None) -> str:
-    """Compile the library; returns its path.  Raises CalledProcessError on failure."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", f"-I{CSRC}",
-           os.path.join(CSRC, "fa_fwd.hip"), "-o", tmp]
-    if verbose:
-        print("[build]", " ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
+def sources():
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def build_library(verbose: bool = True, extra_flags=None, jobs=None) -> str:
+    """Compile every ``csrc/*.hip`` to an object (in parallel) and link the shared
+    library; returns its path.  Raises CalledProcessError on failure."""
+    import concurrent.futures as cf
+    import tempfile
+
+    cc = hipcc()
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"] + list(extra_flags or [])
+    with tempfile.TemporaryDirectory(prefix="fa_build_") as tmpdir:
+        objs, cmds = [], []
+        for src in sources():
+            obj = os.path.join(tmpdir, os.path.basename(src)[:-4] + ".o")
+            objs.append(obj)
+            cmds.append([cc, *flags, f"-I{INCLUDE}", f"-I{CSRC}", "-c", src, "-o", obj])
+        n = jobs or min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
+
+        def run(cmd):
+            if verbose:
+                print("[build]", " ".join(cmd), flush=True)
+            subprocess.run(cmd, check=True)
+
+        with cf.ThreadPoolExecutor(max_workers=n) as ex:
+            for fut in [ex.submit(run, c) for c in cmds]:
+                fut.result()
+        tmp = LIB_PATH + ".tmp"
+        link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        run(link)
+        os.replace(tmp, LIB_PATH)
     return LIB_PATH
 
 

@@ -16,7 +16,9 @@
 #include <cstdio>
 
 #include "fa_fwd.h"
+#include "fa_configs.h"
 #include "fa_fwd_kernel.hpp"
+#include "fa_launch.hpp"
 #include "fa_merge_kernel.hpp"
 
 namespace {
@@ -33,50 +35,16 @@ struct ConfigEntry {
     LaunchFn launch;
 };
 
-template <class C>
-hipError_t launch_cfg(const Params& p, hipStream_t s) {
-    const long long wgs = (long long)p.n_tiles * p.hsub * p.B * p.Hkv * p.num_splits;
-    hipLaunchKernelGGL(fa::fa_fwd_kernel<C>, dim3((unsigned)wgs), dim3(C::NT), 0, s, p);
-    return hipGetLastError();
-}
-
-#define FA_STR2(x) #x
-#define FA_STR(x) FA_STR2(x)
-#define FA_ENTRY_Q(D, BN, QB, WPH, HPW, CAUSAL, BF16, QK8, CNAME, TNAME)                     \
+#define FA_TABLE_ENTRY(D, BN, QB, WPH, HPW, C, B, Q, CNAME, TNAME)                            \
     ConfigEntry{"D" FA_STR(D) "_BN" FA_STR(BN) "_Mw" FA_STR(QB) "x32_WPH" FA_STR(WPH)        \
                 "_HPW" FA_STR(HPW) "_" CNAME "_" TNAME,                                        \
-                D, BF16, CAUSAL, QK8, BN, QB, WPH, HPW,                                         \
-                &launch_cfg<Cfg<D, BN, QB, WPH, HPW, CAUSAL, BF16, QK8>>}
-#define FA_ENTRY(D, BN, QB, WPH, HPW, CAUSAL, BF16, CNAME, TNAME) \
-    FA_ENTRY_Q(D, BN, QB, WPH, HPW, CAUSAL, BF16, false, CNAME, TNAME)
+                D, B, C, Q, BN, QB, WPH, HPW,                                                   \
+                &fa_host::launch_cfg<Cfg<D, BN, QB, WPH, HPW, C, B, Q>>},
+#define FA_STR2(x) #x
+#define FA_STR(x) FA_STR2(x)
 
-#define FA_TILES(D, CAUSAL, BF16, CNAME, TNAME)                    \
-    FA_ENTRY(D, 64, 1, 1, 4, CAUSAL, BF16, CNAME, TNAME),          \
-    FA_ENTRY(D, 64, 1, 2, 4, CAUSAL, BF16, CNAME, TNAME),          \
-    FA_ENTRY(D, 64, 1, 2, 2, CAUSAL, BF16, CNAME, TNAME),          \
-    FA_ENTRY(D, 64, 1, 4, 2, CAUSAL, BF16, CNAME, TNAME),          \
-    FA_ENTRY(D, 64, 1, 4, 1, CAUSAL, BF16, CNAME, TNAME),          \
-    FA_ENTRY(D, 64, 1, 8, 1, CAUSAL, BF16, CNAME, TNAME)
-
-// 32-key tiles (head dim 128 only: a 32 x 64 tile is too small to split over 512 threads).
-#define FA_TILES_BN32(CAUSAL, BF16, QK8, CNAME, TNAME)                   \
-    FA_ENTRY_Q(128, 32, 1, 1, 4, CAUSAL, BF16, QK8, CNAME, TNAME),       \
-    FA_ENTRY_Q(128, 32, 1, 2, 4, CAUSAL, BF16, QK8, CNAME, TNAME),       \
-    FA_ENTRY_Q(128, 32, 1, 2, 2, CAUSAL, BF16, QK8, CNAME, TNAME),       \
-    FA_ENTRY_Q(128, 32, 1, 4, 2, CAUSAL, BF16, QK8, CNAME, TNAME),       \
-    FA_ENTRY_Q(128, 32, 1, 4, 1, CAUSAL, BF16, QK8, CNAME, TNAME),       \
-    FA_ENTRY_Q(128, 32, 1, 8, 1, CAUSAL, BF16, QK8, CNAME, TNAME)
-
-// Head dim 128 uses 32-key tiles only: with three LDS buffers and three register sets a
-// 64-key tile no longer fits two waves per SIMD.  "fp8qk" entries take Q and K in fp8 e4m3.
-const ConfigEntry kConfigs[] = {
-    FA_TILES(64, 1, 1, "causal", "bf16"),  FA_TILES(64, 0, 1, "full", "bf16"),
-    FA_TILES(64, 1, 0, "causal", "fp16"),  FA_TILES(64, 0, 0, "full", "fp16"),
-    FA_TILES_BN32(1, 1, false, "causal", "bf16"), FA_TILES_BN32(0, 1, false, "full", "bf16"),
-    FA_TILES_BN32(1, 0, false, "causal", "fp16"), FA_TILES_BN32(0, 0, false, "full", "fp16"),
-    FA_TILES_BN32(1, 1, true, "causal", "fp8qk_bf16"), FA_TILES_BN32(0, 1, true, "full", "fp8qk_bf16"),
-    FA_TILES_BN32(1, 0, true, "causal", "fp8qk_fp16"), FA_TILES_BN32(0, 0, true, "full", "fp8qk_fp16"),
-};
+// Every compiled configuration (fa_configs.h), in table order.
+const ConfigEntry kConfigs[] = {FA_LIST_ALL(FA_TABLE_ENTRY)};
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 
 // Largest split count: bounds the merge kernel's loop and the workspace.

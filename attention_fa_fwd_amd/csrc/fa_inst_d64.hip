@@ -1,0 +1,7 @@
+// fa_inst_d64.hip -- compiles the forward-kernel configurations of FA_LIST_D64
+// (fa_configs.h); the dispatch table in fa_fwd.hip refers to them.
+#define FA_LAUNCH_DEFINE
+#include "fa_launch.hpp"
+#include "fa_configs.h"
+
+FA_LIST_D64(FA_INSTANTIATE)

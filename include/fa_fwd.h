@@ -26,7 +26,7 @@
  * from several host threads at once.
  *
  * Asynchrony: the call validates its arguments on the host (no HIP call), enqueues its
- * kernel (fa_fwd_splitkv: two kernels) on `stream` (a hipStream_t passed as void*; NULL =
+ * kernel (fa_fwd_splitkv: two kernels; fa_bwd: three) on `stream` (a hipStream_t passed as void*; NULL =
  * the null stream) and returns without synchronising.  Faults inside the kernel surface on the next synchronisation.
  *
  * Errors: a nonzero return leaves out and lse untouched and launches nothing, except
@@ -190,6 +190,38 @@ int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Sq, int Skv, int D, int ca
  * num_splits * B * Hq * Sq * (D + 1) * 4 (fp32 partial O, then fp32 partial LSE), 0 when
  * num_splits <= 1, the problem is empty or D is unsupported. */
 size_t fa_splitkv_workspace_size(int B, int Hq, int Sq, int D, int num_splits);
+
+/*
+ * Backward pass: the gradients dq, dk, dv of out = attention(q, k, v) (as computed by fa_fwd
+ * / fa_fwd_window with the same arguments) for an upstream gradient dout.  The pages name the
+ * backward pass only as future work ("How I Beat PyTorch's Flash Attention", "Future work");
+ * the formulas are the softmax derivative, with P recomputed from the forward's lse:
+ *     P = exp(scale q k^T - lse) (0 where masked),  dv = P^T dout,  dP = dout v^T,
+ *     D = rowsum(dout * out),  dS = P * (dP - D),  dq = scale dS k,  dk = scale dS^T q;
+ * under grouped-query attention dk and dv of a K/V head sum over its query heads.  Rows
+ * with lse = -inf (no visible key) contribute nothing.
+ *
+ *   q, k, v, out, lse   the forward pass's inputs and outputs (layouts as for fa_fwd).
+ *   dout                [B, Hq, Sq, D] in `dtype`.
+ *   dq / dk, dv         outputs, [B, Hq, Sq, D] / [B, Hkv, Skv, D] in `dtype`; they must not
+ *                       overlap any input, each other or the workspace.
+ *   scale .. window     as for fa_fwd_splitkv (window needs causal).
+ *   workspace           >= fa_bwd_workspace_size(B, Hq, Sq) bytes of device memory, 16-byte
+ *                       aligned, owned by the caller (it receives D, fp32 [B*Hq*Sq]).
+ *   stream              the kernels (D, then dk/dv, then dq) are enqueued on it in order.
+ * Checks: as for fa_fwd (pointers, sizes, head group, head dim, dtype, scale, input_pos,
+ * window, alignment, aliasing), then the workspace (NULL, misaligned, too small,
+ * overlapping).  B*Hq*Sq == 0 with K/V rows present writes zero dk and dv.
+ * Deterministic: no atomics; every gradient element is summed in a fixed order.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv,
+           int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+           int causal, int input_pos, int window, int dtype,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_bwd needs: B * Hq * Sq * 4 (0 for an empty problem). */
+size_t fa_bwd_workspace_size(int B, int Hq, int Sq);
 
 /* Configuration the dispatch table picks for these arguments, or a negative fa_status. */
 int fa_select_config(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,

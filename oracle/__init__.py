@@ -7,6 +7,7 @@ import this package.  It shares no code with the HIP library.
 from .attention import (  # noqa: F401
     LN2,
     LOG2E,
+    attention_backward_blocked,
     attention_blocked,
     attention_fp8_blocked,
     attention_key_range,

@@ -50,6 +50,8 @@ Four forms are provided, written independently of one another:
 * ``fp8_e4m3_decode`` and ``attention_fp8_blocked``: fp8 E4M3 codes decoded
                                from the format's definition, and the definition over
                                dequantised fp8 queries and keys.
+* ``attention_backward_blocked``: the gradients dQ, dK, dV from the softmax
+                               derivative (the backward pass).
 
 Parity status: every function here is pinned by the CPU test suite against
 brute force, an independent library routine (PyTorch's CPU float64
@@ -534,3 +536,60 @@ def attention_fp8_blocked(q_codes, k_codes, v, scale, q_descale, k_descale, caus
     k = k_descale * fp8_e4m3_decode(k_codes)
     return attention_blocked(q, k, np.asarray(v, np.float64), scale, causal, input_pos,
                              window=window)
+
+
+# ----------------------------------------------------------------------------
+# Form (v): the backward pass (gradients of O with respect to q, k, v)
+# ----------------------------------------------------------------------------
+
+def attention_backward_blocked(q, k, v, do, scale, causal=False, input_pos=0, window=0,
+                               rows_per_block=512):
+    """Gradients of the forward pass, written out from the softmax derivative, float64.
+
+    With S = scale * Q K^T (masked), P = softmax(S) row-wise, O = P V and an upstream
+    gradient dO ([Journey] "Future work" names the backward pass; the pages give no
+    formulas for it, so these are the textbook derivatives):
+
+        dV = P^T dO
+        dP = dO V^T
+        D_i = sum_j P_ij dP_ij  (= dO_i . O_i)
+        dS = P * (dP - D)       (elementwise; zero where masked)
+        dQ = scale * dS K,      dK = scale * dS^T Q
+
+    Under grouped-query attention dK and dV of a K/V head sum the contributions of every
+    query head in its group.  Rows with no visible key contribute nothing.  Returns
+    (dQ, dK, dV) as float64 arrays of q's and k's shapes.
+    """
+    B, Hq, Hkv, Sq, Skv, D = _shapes(q, k, v)
+    if not (math.isfinite(scale) and scale > 0):
+        raise ValueError("scale must be finite and > 0")
+    _check_window(causal, window)
+    do = np.asarray(do, np.float64)
+    if do.shape != (B, Hq, Sq, D):
+        raise ValueError("do must have q's shape")
+    dQ = np.zeros((B, Hq, Sq, D))
+    dK = np.zeros((B, Hkv, Skv, D))
+    dV = np.zeros((B, Hkv, Skv, D))
+    for b in range(B):
+        for hq in range(Hq):
+            g = kv_head_of(hq, Hq, Hkv)
+            kh = np.asarray(k[b, g], np.float64)
+            vh = np.asarray(v[b, g], np.float64)
+            for i0 in range(0, Sq, rows_per_block):
+                i1 = min(Sq, i0 + rows_per_block)
+                vis = key_visibility(np.arange(i0, i1), Skv, causal, input_pos, window)
+                rows = i0 + np.nonzero(vis.any(axis=1))[0]
+                if rows.size == 0:
+                    continue
+                qr = np.asarray(q[b, hq, rows], np.float64)
+                s = scaled_scores(qr, kh, scale)
+                m, e, l = masked_softmax_stats(s, vis[rows - i0])
+                P = e / l
+                dOr = do[b, hq, rows]
+                dV[b, g] += P.T @ dOr
+                dP = dOr @ vh.T
+                Dr = (P * dP).sum(axis=1, keepdims=True)
+                dS = P * (dP - Dr)
+                dQ[b, hq, rows] = scale * (dS @ kh)
+                dK[b, g] += scale * (dS.T @ qr)
+    return dQ, dK, dV

@@ -1,0 +1,121 @@
+"""GPU parity of the backward pass (fa_bwd) against the fp64 oracle's gradients.
+
+Tolerance (no page or target fixes one): per gradient tensor, max |g - g_oracle| <=
+TOL_REL * max(max |g_oracle|, 0.05 * the largest of the three gradients' maxima), with
+TOL_REL = 4e-3 (fp16) and 1.6e-2 (bf16).  A CPU simulation
+of the kernels' arithmetic (P and dS rounded to the input type before their products, fp32
+accumulation, outputs rounded, D from the rounded forward output) stays below 40% of that
+(tests/test_tolerance_backward.py).  The forward pass that provides out and lse is the
+library's own fa_fwd on the same inputs.
+"""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_fa_fwd_amd as fa
+import oracle
+from attention_fa_fwd_amd.inputs import DTYPES, make_qkv
+
+pytestmark = pytest.mark.gpu
+
+TOL_REL = {torch.float16: 4e-3, torch.bfloat16: 1.6e-2}
+DEV = torch.device("cuda:0")
+
+
+def _say(*a):
+    print("[bwd]", *a, file=sys.stderr, flush=True)
+
+
+def make_dout(shape, dtype, seed):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(1000 + int(seed))
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(dtype)
+
+
+def run_bwd(q, k, v, do, scale, causal, pos, window=0):
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    out, lse = fa.fa_fwd(qd, kd, vd, scale=scale, causal=causal, input_pos=pos, window=window)
+    dq, dk, dv = fa.fa_bwd(qd, kd, vd, out, lse, dod, scale=scale, causal=causal, input_pos=pos,
+                           window=window)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def check(q, k, v, do, scale, causal, pos, window, got, what):
+    ref = oracle.attention_backward_blocked(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                            do.double().numpy(), scale, causal, pos, window)
+    # A gradient that is exactly zero (one key per row, say) is compared at the scale of the
+    # largest of the three, since its rounding noise comes from products of that size.
+    scale_all = max(float(np.max(np.abs(r))) if r.size else 0.0 for r in ref)
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        g = g.double().numpy()
+        assert np.isfinite(g).all(), f"{name} non-finite {what}"
+        m = float(np.max(np.abs(r))) if r.size else 0.0
+        err = float(np.max(np.abs(g - r))) if r.size else 0.0
+        bound = TOL_REL[q.dtype] * max(m, 0.05 * scale_all, 1e-6)
+        assert err <= bound, f"{name} err {err:.3e} vs max {m:.3e} {what}"
+
+
+BWD_CASES = [
+    # B, Hq, Hkv, Sq, Skv, D, causal, pos, window
+    (1, 2, 2, 128, 128, 128, False, 0, 0),
+    (1, 2, 2, 128, 128, 64, True, 0, 0),
+    (2, 4, 4, 300, 300, 128, True, 0, 0),      # ragged, several blocks
+    (1, 8, 2, 257, 391, 128, True, 134, 0),    # ragged both, GQA 4, offset
+    (1, 8, 1, 65, 129, 64, False, 0, 0),       # MQA
+    (1, 8, 8, 1, 1, 128, True, 0, 0),          # one query, one key
+    (1, 4, 4, 1, 700, 128, True, 699, 0),      # decode-like row
+    (3, 6, 3, 129, 64, 64, True, 0, 0),        # Sq > Skv
+    (1, 8, 2, 300, 300, 128, True, 0, 45),     # sliding window
+    (1, 8, 8, 129, 64, 128, True, 0, 9),       # window with empty rows
+    (1, 32, 4, 256, 256, 128, True, 0, 0),
+]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_backward_shapes(case, dtype):
+    B, Hq, Hkv, Sq, Skv, D, causal, pos, W = case
+    _say(case, dtype)
+    q, k, v = make_qkv(B, Hq, Hkv, Sq, Skv, D, dtype, seed=sum(case) + 3)
+    do = make_dout(q.shape, DTYPES[dtype], sum(case))
+    scale = 1.0 / math.sqrt(D)
+    got = run_bwd(q, k, v, do, scale, causal, pos, W)
+    check(q, k, v, do, scale, causal, pos, W, got, f"{case} {dtype}")
+
+
+def test_backward_medium_gqa_causal():
+    """A 2048-token causal GQA problem, every element of every gradient."""
+    q, k, v = make_qkv(1, 8, 2, 2048, 2048, 128, "bf16", seed=31)
+    do = make_dout(q.shape, torch.bfloat16, 31)
+    got = run_bwd(q, k, v, do, 1 / math.sqrt(128), True, 0)
+    check(q, k, v, do, 1 / math.sqrt(128), True, 0, 0, got, "2048 gqa causal")
+
+
+def test_backward_deterministic():
+    q, k, v = make_qkv(1, 8, 2, 300, 500, 128, "bf16", seed=32)
+    do = make_dout(q.shape, torch.bfloat16, 32)
+    a = run_bwd(q, k, v, do, 0.1, True, 200)
+    b = run_bwd(q, k, v, do, 0.1, True, 200)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+def test_backward_errors():
+    q, k, v = make_qkv(1, 4, 2, 64, 64, 128, "bf16", seed=33)
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    out, lse = fa.fa_fwd(q, k, v)
+    do = torch.ones_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    small = torch.empty(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_bwd_into(q, k, v, out, lse, do, dq, dk, dv, small)
+    assert e.value.code == -13
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_bwd_into(q, k, v, out, lse, do, dq, dk, dk, torch.empty(4096, dtype=torch.uint8, device=DEV))
+    assert e.value.code == -9
