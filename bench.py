@@ -19,7 +19,8 @@ reported as "warmup_extra_steps".
 timed region) instead; decoding workloads (one query row) are reported in GB/s against
 the HBM roofline, since reading K and V bounds them.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--splitkv] [--all]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--splitkv]
+                       [--backward] [--all]
 """
 
 from __future__ import annotations
@@ -43,6 +44,7 @@ PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
 PEAK_FP8_TFLOPS = 2 * PEAK_TFLOPS
 # fp8 Q/K workloads: half the FLOPs (Q K^T) at the fp8 peak, half (P V) at the bf16 one.
 PEAK_FP8QK_TFLOPS = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_TFLOPS)
+METRIC_BWD = "attention bwd TFLOP/s (2.5x the forward FLOPs: five matrix products), bf16/fp16"
 METRIC_FP8 = "attention fwd TFLOP/s, fp8 E4M3 Q/K (Q K^T on the fp8 MFMA), fp16/bf16 P V"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.json")
 MIN_WARMUP_S = 0.3
@@ -126,7 +128,7 @@ def workload(name):
     return WORKLOADS[name], False
 
 
-def time_gpu(name, steps, warmup, config=-1, splitkv=False):
+def time_gpu(name, steps, warmup, config=-1, splitkv=False, backward=False):
     import torch
 
     import attention_fa_fwd_amd as fa
@@ -145,7 +147,20 @@ def time_gpu(name, steps, warmup, config=-1, splitkv=False):
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     splits = 1
-    if fp8:
+    if backward:
+        fa.fa_fwd_into(q, k, v, out, lse, scale=kw["scale"], causal=kw["causal"],
+                       input_pos=kw["input_pos"], window=kw["window"], stream=sp)
+        g = torch.Generator(device="cpu")
+        g.manual_seed(1)
+        dout = torch.randn(q.shape, generator=g, dtype=torch.float32).to(q.dtype).to(dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(max(16, w["B"] * w["Hq"] * w["Sq"] * 4), dtype=torch.uint8, device=dev)
+
+        def step():
+            fa.fa_bwd_into(q, k, v, out, lse, dout, dq, dk, dv, ws, scale=kw["scale"],
+                           causal=kw["causal"], input_pos=kw["input_pos"], window=kw["window"],
+                           stream=sp)
+    elif fp8:
         def step():
             fa.fa_fwd_fp8_into(q, k, v, out, lse, kw["q_descale"], kw["k_descale"],
                                scale=kw["scale"], causal=kw["causal"], input_pos=kw["input_pos"],
@@ -195,7 +210,8 @@ def time_gpu(name, steps, warmup, config=-1, splitkv=False):
     else:
         cfg = fa.select_config(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"], w["causal"],
                                w["input_pos"], q.dtype)
-    return dict(total_ms=total_ms, wall_s=wall, per_ms=per, kernel=fa.config_names()[cfg],
+    kernel = "fa_bwd (dot, dK/dV, dQ)" if backward else fa.config_names()[cfg]
+    return dict(total_ms=total_ms, wall_s=wall, per_ms=per, kernel=kernel,
                 warmup_extra=extra, splits=splits)
 
 
@@ -228,21 +244,22 @@ def cpu_baseline(name):
                 wall_s=round(dt, 3))
 
 
-def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False):
+def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False, backward=False):
     w, fp8 = workload(name)
     log(f"workload {name}: {w}")
-    r = time_gpu(name, steps, warmup, config, splitkv)
+    r = time_gpu(name, steps, warmup, config, splitkv, backward)
     ms_step = r["total_ms"] / steps
-    flops = literal_flops(w)
+    flops = literal_flops(w) * (2.5 if backward else 1.0)
     value = flops / (ms_step * 1e-3) / 1e12
     mean_kernel_ms = sum(r["per_ms"]) / len(r["per_ms"])
     med = r["per_ms"][len(r["per_ms"]) // 2]
     p95 = r["per_ms"][min(len(r["per_ms"]) - 1, int(math.ceil(0.95 * len(r["per_ms"]))) - 1)]
-    path = "fa_fwd_fp8" if fp8 else f"fa_fwd_splitkv ({r['splits']} splits)" if splitkv else "fa_fwd"
+    path = ("fa_bwd" if backward else "fa_fwd_fp8" if fp8 else
+            f"fa_fwd_splitkv ({r['splits']} splits)" if splitkv else "fa_fwd")
     log(f"{path} kernel {r['kernel']}: mean {mean_kernel_ms * 1e3:.1f} us, median {med * 1e3:.1f} us, "
         f"p95 {p95 * 1e3:.1f} us, min {r['per_ms'][0] * 1e3:.1f} us, "
         f"{r['warmup_extra']} extra warm-up steps")
-    decode = w["Sq"] <= 16
+    decode = w["Sq"] <= 16 and not backward
     if decode:
         # Reading K and V bounds a decoding step: GB/s of algorithmic bytes per call.
         gbs = algorithmic_bytes(w) / (mean_kernel_ms * 1e-3) / 1e9
@@ -251,11 +268,11 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False):
                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
     else:
         achieved = flops / (mean_kernel_ms * 1e-3) / 1e12
-        metric, unit = (METRIC_FP8 if fp8 else METRIC), "TFLOP/s"
+        metric, unit = (METRIC_BWD if backward else METRIC_FP8 if fp8 else METRIC), "TFLOP/s"
         peak = PEAK_FP8QK_TFLOPS if fp8 else PEAK_TFLOPS
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                    "traffic": None if splitkv else traffic_bytes(name)}
+                    "traffic": None if (splitkv or backward) else traffic_bytes(name)}
     line = {
         "metric": metric,
         "value": round(value, 2),
@@ -281,8 +298,9 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False):
     }
     if not decode:
         line["pct_of_peak"] = round(100.0 * value / (PEAK_FP8QK_TFLOPS if fp8 else PEAK_TFLOPS), 2)
-        line["tflops_exact_pairs"] = round(exact_flops(w) / (ms_step * 1e-3) / 1e12, 2)
-    if with_cpu and not fp8:
+        line["tflops_exact_pairs"] = round(exact_flops(w) * (2.5 if backward else 1.0)
+                                           / (ms_step * 1e-3) / 1e12, 2)
+    if with_cpu and not fp8 and not backward:
         log("timing the fp64 CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(name)
     return line
@@ -315,6 +333,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--splitkv", action="store_true",
                     help="time fa_fwd_splitkv with the library's split count")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass fa_bwd (forward results precomputed)")
     ap.add_argument("--all", action="store_true",
                     help="also time every named workload (extra JSON lines on stderr)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -331,7 +351,7 @@ def main(argv=None):
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
     line = bench_line(a.workload, a.steps, a.warmup, a.config, with_cpu=not a.no_cpu_baseline,
-                      splitkv=a.splitkv)
+                      splitkv=a.splitkv, backward=a.backward)
     if a.all:
         from attention_fa_fwd_amd.inputs import FP8_WORKLOADS, WORKLOADS
 
@@ -342,6 +362,10 @@ def main(argv=None):
                     continue
                 extra = bench_line(name, a.steps, a.warmup, -1, with_cpu=False, splitkv=split)
                 print("[bench-extra] " + json.dumps(extra), file=sys.stderr, flush=True)
+        for name in (HEADLINE, "mha_causal_s4096_d128_fp16"):
+            extra = bench_line(name, max(1, a.steps // 4), a.warmup, -1, with_cpu=False,
+                               backward=True)
+            print("[bench-extra] " + json.dumps(extra), file=sys.stderr, flush=True)
     print(json.dumps(line), flush=True)
     return 0
 
