@@ -14,7 +14,7 @@ import math
 import os
 import threading
 
-__all__ = ["fa_fwd", "fa_fwd_into", "fa_bwd", "fa_bwd_into", "fa_fwd_fp8", "fa_fwd_fp8_into", "select_config_fp8", "fa_fwd_splitkv", "fa_fwd_splitkv_into", "splitkv_num_splits",
+__all__ = ["fa_fwd", "fa_fwd_into", "fa_bwd", "fa_bwd_into", "bwd_workspace_size", "fa_fwd_fp8", "fa_fwd_fp8_into", "select_config_fp8", "fa_fwd_splitkv", "fa_fwd_splitkv_into", "splitkv_num_splits",
            "splitkv_workspace_size", "select_config", "config_names", "num_configs", "FaError",
            "load_library", "LIB_PATH"]
 
@@ -47,7 +47,7 @@ def _declare(lib):
     lib.fa_bwd.argtypes = [_vp] * 9 + [_c_int] * 6 + [_c_float] + [_c_int] * 4 + [_vp, ctypes.c_size_t,
                                                                               _vp]
     lib.fa_bwd.restype = _c_int
-    lib.fa_bwd_workspace_size.argtypes = [_c_int] * 3
+    lib.fa_bwd_workspace_size.argtypes = [_c_int] * 7
     lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.fa_fwd_fp8.argtypes = _FWD_ARGS[:12] + [_c_float, _c_float, _c_int, _c_int, _c_int, _c_int,
                                                 _vp, _c_int]
@@ -339,7 +339,7 @@ def fa_bwd_into(q, k, v, out, lse, dout, dq, dk, dv, workspace, scale=None, caus
     """Backward pass into caller-provided dq [B,Hq,Sq,D], dk, dv [B,Hkv,Skv,D] (q's dtype).
 
     ``out`` and ``lse`` are the forward pass's results for the same arguments;
-    ``workspace`` holds at least ``B*Hq*Sq*4`` bytes (fa_bwd_workspace_size).
+    ``workspace`` holds at least ``bwd_workspace_size(...)`` bytes.
     """
     import torch
 
@@ -368,6 +368,12 @@ def fa_bwd_into(q, k, v, out, lse, dout, dq, dk, dv, workspace, scale=None, caus
     return dq, dk, dv
 
 
+def bwd_workspace_size(B, Hq, Hkv, Sq, Skv, D, causal=True):
+    """Workspace bytes fa_bwd needs: the row statistics plus, for a small K/V grid with a
+    head group to split, fp32 partial dk / dv sums."""
+    return int(load_library().fa_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, D, 1 if causal else 0))
+
+
 def fa_bwd(q, k, v, out, lse, dout, scale=None, causal=True, input_pos=0, window=0):
     """Gradients (dq, dk, dv) of the forward pass for upstream gradient ``dout``;
     allocates the outputs and the workspace with torch."""
@@ -376,7 +382,7 @@ def fa_bwd(q, k, v, out, lse, dout, scale=None, causal=True, input_pos=0, window
     q, k, v, out, dout = (t.contiguous() for t in (q, k, v, out, dout))
     B, Hq, Sq, D = q.shape
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    nbytes = int(load_library().fa_bwd_workspace_size(B, Hq, Sq))
+    nbytes = bwd_workspace_size(B, Hq, k.shape[1], Sq, k.shape[2], D, causal)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     return fa_bwd_into(q, k, v, out, lse.contiguous(), dout, dq, dk, dv, ws, scale=scale,
                        causal=causal, input_pos=input_pos, window=window)

@@ -1,5 +1,6 @@
-// fa_bwd.hip -- host side of the backward pass: argument checks and the three launches
-// (D = rowsum(dO * O), then dK/dV, then dQ) of fa_bwd_kernel.hpp, exported as fa_bwd.
+// fa_bwd.hip -- host side of the backward pass: argument checks and the launches of
+// fa_bwd_kernel.hpp (row statistics, dK/dV, the sum of dK/dV partials when the GQA group is
+// split over workgroups, dQ), exported as fa_bwd.
 
 #include <hip/hip_runtime.h>
 
@@ -15,6 +16,8 @@ namespace {
 
 using fa::BwdParams;
 
+constexpr int kNumCUs = 256;
+
 bool overlaps(uintptr_t a, size_t na, uintptr_t b, size_t nb) {
     return a < b + nb && b < a + na;
 }
@@ -24,23 +27,48 @@ __global__ void zero16(uint4* p, size_t n16) {
         p[i] = make_uint4(0, 0, 0, 0);
 }
 
+// Workgroups sharing one K/V block's query heads: the smallest divisor of the group size
+// that gives the dK/dV grid at least two workgroups per CU (causal: uneven work per block,
+// balanced by handing out the heaviest first) or one per CU (non-causal).
+int group_split(int B, int Hq, int Hkv, int Skv, int causal) {
+    const int group = Hq / Hkv;
+    const long long n = (long long)((Skv + 127) / 128) * B * Hkv;
+    const long long target = causal ? 2LL * kNumCUs : kNumCUs;
+    for (int d = 1; d <= group; ++d)
+        if (group % d == 0 && n * d >= target) return d;
+    return group;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t stats_bytes(int B, int Hq, int Sq) { return round256((size_t)B * Hq * Sq * 8); }
+
+size_t part_bytes(int gsplit, int B, int Hkv, int Skv, int D) {
+    return gsplit > 1 ? (size_t)gsplit * 2 * B * Hkv * Skv * D * 4 : 0;
+}
+
 template <int D, bool BF16>
-hipError_t launch_all(const BwdParams& p, const void* o, float* dvec, int causal, hipStream_t s) {
+hipError_t launch_all(const BwdParams& p, int causal, hipStream_t s) {
     const int rows = p.B * p.Hq * p.Sq;
-    hipLaunchKernelGGL((fa::fa_bwd_dot_kernel<D, BF16>), dim3((unsigned)((rows + 3) / 4)), dim3(256),
-                       0, s, o, p.dout, dvec, rows);
+    constexpr int RPB = 256 / (D / 8);
+    hipLaunchKernelGGL((fa::fa_bwd_dot_kernel<D, BF16>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
+                       0, s, p.o, p.dout, p.lse, p.stats, rows);
     BwdParams pk = p, pq = p;
     pk.n_tiles = (p.Skv + 127) / 128;
     pq.n_tiles = (p.Sq + 127) / 128;
-    const dim3 gk((unsigned)((long long)pk.n_tiles * p.B * p.Hkv));
+    const dim3 gk((unsigned)((long long)pk.n_tiles * p.B * p.Hkv * p.gsplit));
     const dim3 gq((unsigned)((long long)pq.n_tiles * p.B * p.Hq));
-    if (causal) {
-        hipLaunchKernelGGL((fa::fa_bwd_kernel<D, true, BF16, fa::BWD_DKDV>), gk, dim3(256), 0, s, pk);
-        hipLaunchKernelGGL((fa::fa_bwd_kernel<D, true, BF16, fa::BWD_DQ>), gq, dim3(256), 0, s, pq);
-    } else {
-        hipLaunchKernelGGL((fa::fa_bwd_kernel<D, false, BF16, fa::BWD_DKDV>), gk, dim3(256), 0, s, pk);
-        hipLaunchKernelGGL((fa::fa_bwd_kernel<D, false, BF16, fa::BWD_DQ>), gq, dim3(256), 0, s, pq);
+    if (causal) hipLaunchKernelGGL((fa::fa_bwd_kernel<D, true, BF16, fa::BWD_DKDV>), gk, dim3(256), 0, s, pk);
+    else hipLaunchKernelGGL((fa::fa_bwd_kernel<D, false, BF16, fa::BWD_DKDV>), gk, dim3(256), 0, s, pk);
+    if (p.gsplit > 1) {
+        const size_t n = (size_t)p.B * p.Hkv * p.Skv * D;
+        const size_t threads = n / 4;   // 2 tensors x n / 8
+        const dim3 gr((unsigned)std::min<size_t>((threads + 255) / 256, 8 * kNumCUs));
+        hipLaunchKernelGGL((fa::fa_bwd_reduce_kernel<BF16>), gr, dim3(256), 0, s, (const float*)p.part, p.dk,
+                           p.dv, n, p.gsplit, p.scale);
     }
+    if (causal) hipLaunchKernelGGL((fa::fa_bwd_kernel<D, true, BF16, fa::BWD_DQ>), gq, dim3(256), 0, s, pq);
+    else hipLaunchKernelGGL((fa::fa_bwd_kernel<D, false, BF16, fa::BWD_DQ>), gq, dim3(256), 0, s, pq);
     return hipGetLastError();
 }
 
@@ -48,9 +76,10 @@ hipError_t launch_all(const BwdParams& p, const void* o, float* dvec, int causal
 
 extern "C" {
 
-size_t fa_bwd_workspace_size(int B, int Hq, int Sq) {
-    if (B <= 0 || Hq <= 0 || Sq <= 0) return 0;
-    return (size_t)B * Hq * Sq * sizeof(float);
+size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal) {
+    if (B <= 0 || Hq <= 0 || Sq <= 0 || Hkv <= 0 || Skv <= 0 || Hq % Hkv != 0) return 0;
+    if (D != 64 && D != 128) return 0;
+    return stats_bytes(B, Hq, Sq) + part_bytes(group_split(B, Hq, Hkv, Skv, causal), B, Hkv, Skv, D);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
@@ -92,7 +121,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
             if (osz[j] && overlaps(outs[i], osz[i], outs[j], osz[j])) return FA_ERR_ALIAS;
     }
     if (q_empty && kv_empty) return FA_OK;
-    const size_t need = fa_bwd_workspace_size(B, Hq, Sq);
+    const size_t need = fa_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, D, causal);
     if (need > 0) {
         if (!workspace) return FA_ERR_NULL_POINTER;
         if ((uintptr_t)workspace & 15u) return FA_ERR_MISALIGNED;
@@ -120,7 +149,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
     p.o = out;
     p.dout = dout;
     p.lse = lse;
-    p.dvec = (const float*)workspace;
+    p.stats = (float*)workspace;
     p.dq = dq;
     p.dk = dk;
     p.dv = dv;
@@ -135,15 +164,17 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
     p.c = (float)((double)scale * 1.4426950408889634073599246810019);
     p.scale = scale;
     p.group = Hq / Hkv;
+    p.gsplit = group_split(B, Hq, Hkv, Skv, causal);
+    p.hpw = p.group / p.gsplit;
+    p.part = p.gsplit > 1 ? (float*)((unsigned char*)workspace + stats_bytes(B, Hq, Sq)) : nullptr;
     p.n_tiles = 0;
-    if ((long long)((Skv + 127) / 128) * B * Hkv > 0x7fffffffLL ||
+    if ((long long)((Skv + 127) / 128) * B * Hkv * p.gsplit > 0x7fffffffLL ||
         (long long)((Sq + 127) / 128) * B * Hq > 0x7fffffffLL)
         return FA_ERR_INVALID_SHAPE;
     hipError_t e;
-    float* dvec = (float*)workspace;
     const int bf16 = dtype == FA_DTYPE_BF16;
-    if (D == 128) e = bf16 ? launch_all<128, true>(p, out, dvec, causal, s) : launch_all<128, false>(p, out, dvec, causal, s);
-    else e = bf16 ? launch_all<64, true>(p, out, dvec, causal, s) : launch_all<64, false>(p, out, dvec, causal, s);
+    if (D == 128) e = bf16 ? launch_all<128, true>(p, causal, s) : launch_all<128, false>(p, causal, s);
+    else e = bf16 ? launch_all<64, true>(p, causal, s) : launch_all<64, false>(p, causal, s);
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -7,12 +7,15 @@
 //     P = exp(scale S - LSE),  dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),
 //     dS = P * (dP - D),       dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Three kernels, no atomics, deterministic:
-//  * fa_bwd_dot_kernel:  D_i = dO_i . O_i (fp32), one wave per row.
+// Kernels, no atomics, deterministic:
+//  * fa_bwd_dot_kernel: per query row the pair {LSE * log2(e) (+inf for a row with no
+//    visible key), D = dO . O} in fp32 -- the row statistics both gradient kernels read.
 //  * fa_bwd_kernel<DKDV>: a wave owns 32 keys of one K/V head (K and V rows in registers);
-//    the workgroup streams 32-row tiles of Q and dO of every query head of the GQA group
-//    through LDS and accumulates dK^T and dV^T in registers -- the grouped heads' sum
-//    happens in place.
+//    the workgroup streams 32-row tiles of Q, dO and the row statistics of the query heads
+//    it covers through LDS and accumulates dK^T and dV^T in registers, so the grouped
+//    heads' sum happens in place.  When there are too few K/V blocks to fill the chip, the
+//    group's query heads are split over several workgroups, each writing an fp32 partial
+//    that fa_bwd_reduce_kernel sums in a fixed order.
 //  * fa_bwd_kernel<DQ>: a wave owns 32 query rows (Q and dO rows in registers); the
 //    workgroup streams 32-key tiles of K and V and accumulates dQ^T.
 // Both use the forward kernel's MFMA formulation: the streamed tile is the A operand of
@@ -22,6 +25,12 @@
 // operand is the streamed tile transposed (ds_read_b64_tr_b16).  Since each streamed tile
 // is read both ways, its LDS layout uses one XOR swizzle of the 16-byte chunks that a
 // bank model finds conflict-free for both the row reads and the transposed reads.
+//
+// Pipeline (both gradient kernels): four LDS buffers.  Step j loads tile j+3, issues the
+// S / dP products of tile j+1 into a second register set, then turns tile j's S / dP into
+// P and dS and issues the two transposed products of tile j -- so the exp2 work of one
+// tile overlaps the matrix work of the next in one straight-line block.  A step ends by
+// waiting for tile j+2 only (tile j+3's loads stay in flight) and one barrier.
 #pragma once
 
 #include "fa_fwd_kernel.hpp"
@@ -35,15 +44,18 @@ struct BwdParams {
     const void* o;
     const void* dout;
     const float* lse;    // [B*Hq*Sq], natural log, -inf for rows with no visible key
-    const float* dvec;   // D = rowsum(dO * O), fp32 [B*Hq*Sq]
+    float* stats;        // [B*Hq*Sq][2]: LSE * log2(e) (+inf for an empty row), D
     void* dq;
     void* dk;
     void* dv;
+    float* part;         // gsplit > 1: fp32 partial dK, dV [gsplit][2][B*Hkv*Skv*D]
     int B, Hq, Hkv, Sq, Skv;
     int causal, input_pos, window;   // window > 0 only with causal
     float c;                         // scale * log2(e)
     float scale;
     int group;                       // Hq / Hkv
+    int gsplit;                      // workgroups sharing one K/V block's query heads
+    int hpw;                         // query heads per DKDV workgroup (group / gsplit)
     int n_tiles;                     // 128-row blocks per head (queries for DQ, keys for DKDV)
 };
 
@@ -58,34 +70,83 @@ __device__ __forceinline__ int b_swz(int row) {
 }
 
 template <bool BF16>
-__device__ __forceinline__ float half_to_f32(uint16_t x) {
-    if constexpr (BF16) return __uint_as_float((uint32_t)x << 16);
-    else return (float)__builtin_bit_cast(_Float16, x);
+__device__ __forceinline__ float half_to_f32(uint32_t x) {
+    if constexpr (BF16) return __uint_as_float(x << 16);
+    else return (float)__builtin_bit_cast(_Float16, (uint16_t)x);
 }
 
-// D_i = sum_d dO[i][d] * O[i][d] in fp32; rows = B*Hq*Sq; 4 rows per 256-thread block.
+// Buffer resource whose base and size are wave-uniform by construction; passing them
+// through readfirstlane lets the compiler keep the descriptor in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_uniform(const void* base, int nbytes) {
+    const uint64_t a = (uint64_t)base;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    const int n = __builtin_amdgcn_readfirstlane(nbytes);
+    return make_rsrc((const void*)(((uint64_t)hi << 32) | lo), n);
+}
+
+// 4 bytes per lane from a buffer straight into LDS: lane i writes lds + 4*i.
+__device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4,
+                                             voff, 0, 0, 0);
+}
+
+// Row statistics: stats[row] = {LSE * log2(e) or +inf for an empty row, sum_d dO * O};
+// D / 8 lanes per row, 16 bytes each, summed by a butterfly in a fixed order.
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void fa_bwd_dot_kernel(const void* o, const void* dout, float* dvec,
-                                                         int rows) {
-    constexpr int PER = D / 64;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (row >= rows) return;
-    const uint16_t* op = (const uint16_t*)o + (size_t)row * D + lane * PER;
-    const uint16_t* dp = (const uint16_t*)dout + (size_t)row * D + lane * PER;
+__global__ __launch_bounds__(256) void fa_bwd_dot_kernel(const void* o, const void* dout, const float* lse,
+                                                         float* stats, int rows) {
+    constexpr int TPR = D / 8, RPB = 256 / TPR;
+    const int row = blockIdx.x * RPB + threadIdx.x / TPR;
+    const int t = threadIdx.x % TPR;
     float acc = 0.0f;
+    if (row < rows) {
+        const u32x4 a = ((const u32x4*)((const uint16_t*)o + (size_t)row * D))[t];
+        const u32x4 g = ((const u32x4*)((const uint16_t*)dout + (size_t)row * D))[t];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc += half_to_f32<BF16>(op[e]) * half_to_f32<BF16>(dp[e]);
+        for (int e = 0; e < 4; ++e) {
+            acc = __builtin_fmaf(half_to_f32<BF16>(a[e] & 0xffffu), half_to_f32<BF16>(g[e] & 0xffffu), acc);
+            acc = __builtin_fmaf(half_to_f32<BF16>(a[e] >> 16), half_to_f32<BF16>(g[e] >> 16), acc);
+        }
+    }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-    if (lane == 0) dvec[row] = acc;
+    for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+    if (row < rows && t == 0) {
+        const float l = lse[row];
+        const float l2 = l == -__builtin_inff() ? __builtin_inff() : l * 1.44269504088896340736f;
+        *(f32x2*)(stats + 2 * (size_t)row) = (f32x2){l2, acc};
+    }
+}
+
+// dK = scale * sum_g part[g][0], dV = sum_g part[g][1], rounded to the storage type; n
+// elements per tensor (a multiple of 8), 8 per thread.
+template <bool BF16>
+__global__ __launch_bounds__(256) void fa_bwd_reduce_kernel(const float* part, void* dk, void* dv, size_t n,
+                                                            int gsplit, float scale) {
+    const size_t n8 = n / 8;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < 2 * n8; i += (size_t)gridDim.x * 256) {
+        const int t = i >= n8;
+        const size_t j = (i - (t ? n8 : 0)) * 8;
+        f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f}, c = a;
+        for (int g = 0; g < gsplit; ++g) {
+            const float* s = part + (size_t)(2 * g + t) * n + j;
+            a += *(const f32x4*)s;
+            c += *(const f32x4*)(s + 4);
+        }
+        const float mul = t ? 1.0f : scale;
+        a *= mul;
+        c *= mul;
+        const u32x4 wv = {pack2<BF16>(a[0], a[1]), pack2<BF16>(a[2], a[3]), pack2<BF16>(c[0], c[1]),
+                          pack2<BF16>(c[2], c[3])};
+        *(u32x4*)((uint16_t*)(t ? dv : dk) + j) = wv;
+    }
 }
 
 enum BwdMode { BWD_DQ = 0, BWD_DKDV = 1 };
 
 template <int D, bool CAUSAL, bool BF16, int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
-                          amdgpu_waves_per_eu(MODE == BWD_DQ ? 2 : 1, MODE == BWD_DQ ? 2 : 1)))
+                          amdgpu_waves_per_eu(1, 1)))
 void fa_bwd_kernel(BwdParams p) {
     constexpr int NT = 256, NW = 4;
     constexpr int BR = 32;               // streamed rows per tile
@@ -93,9 +154,15 @@ void fa_bwd_kernel(BwdParams p) {
     constexpr int ROWB = D * 2, TILE = BR * ROWB, CPR = D / 8;
     constexpr int LD = BR * CPR / NT;    // 16-byte chunks of a tile per thread
     constexpr int LOAD_STRIDE = NT * 16;
+    constexpr int NL = 2 * LD;           // tile loads per lane per step
     static_assert(BR * CPR % NT == 0 && (64 * NW / CPR) % 16 == 0, "tile load layout");
     constexpr bool DKDV = MODE == BWD_DKDV;
+    constexpr int STB = DKDV ? BR * 8 : 16;   // row statistics of a streamed tile
     typedef uint16_t T;
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    using P3 = std::integral_constant<int, 3>;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -103,16 +170,20 @@ void fa_bwd_kernel(BwdParams p) {
     const int l32 = lane & 31;
     const int h = lane >> 5;
 
-    // Workgroup -> (batch, head, 128-row block); causal: the heaviest blocks first.
-    const int nh = DKDV ? p.Hkv : p.Hq;
+    // Workgroup -> (batch, head [, group part], 128-row block); causal: heaviest blocks first.
+    const int nh = DKDV ? p.Hkv * p.gsplit : p.Hq;
     const int wg = blockIdx.x;
     const int bh = wg % (p.B * nh);
     const int trank = wg / (p.B * nh);
-    const int b = bh / nh, head = bh - b * nh;
+    const int b = bh / nh;
+    const int hx = bh - b * nh;
+    const int head = DKDV ? hx / p.gsplit : hx;   // K/V head (DKDV) or query head (DQ)
+    const int gp = DKDV ? hx - head * p.gsplit : 0;
     const int blk = CAUSAL ? (DKDV ? trank : p.n_tiles - 1 - trank) : trank;
     const int r0 = blk * 128;                 // first own row of the workgroup
     const int rw0 = r0 + w * 32;              // first own row of the wave
     const bool win = CAUSAL && p.window > 0;
+    const int W = p.window;
 
     // Own rows (B operands): DQ: Q and dO rows of query head `head`; DKDV: K and V rows.
     const int n_own = DKDV ? p.Skv : p.Sq;
@@ -126,80 +197,132 @@ void fa_bwd_kernel(BwdParams p) {
         x1[dk] = ((const u32x4*)x1p)[dk * 2 + h];
         x2[dk] = ((const u32x4*)x2p)[dk * 2 + h];
     }
-    // DQ: the lane's query row statistics (LSE in the exp2 domain, +inf for an empty row
-    // so that p = 0; and D).
+    // DQ: the lane's own query row statistics.
     float lse2_own = 0.0f, d_own = 0.0f;
     if constexpr (!DKDV) {
-        const size_t rr = (size_t)(b * p.Hq + head) * p.Sq + own_row;
-        const float l = p.lse[rr];
-        lse2_own = l == -__builtin_inff() ? __builtin_inff() : l * 1.44269504088896340736f;
-        d_own = p.dvec[rr];
+        const f32x2 st = *(const f32x2*)(p.stats + 2 * ((size_t)(b * p.Hq + head) * p.Sq + own_row));
+        lse2_own = st[0];
+        d_own = st[1];
     }
 
-    // Streamed tiles: DQ: K (t1) and V (t2) of head `head / group`; DKDV: Q (t1) and dO
-    // (t2) of each query head of the group.  Steps s = 0 .. n_steps-1.
-    int n_steps, s_first;   // DQ: key tiles [s_first, s_first + n_steps); DKDV: see below
-    int qt0 = 0, qt1 = 0;   // DKDV: query tiles [qt0, qt1) per head
+    // Streamed steps.  DQ: key tiles [tb, tb + n_steps) of K/V head head / group; tiles
+    // [ua, ub) need no mask.  DKDV: for each of the hpw query heads of the workgroup, query
+    // tiles [qt0, qt1); tiles [qa, qb) need no mask.  A tile needs no mask when it lies
+    // inside the tensors, the workgroup's own rows do too, and every (query, key) pair of
+    // the two blocks is visible (causal: key <= input_pos + query; window: key >=
+    // input_pos + query - window + 1).
     const int kv_head = DKDV ? head : head / p.group;
+    int n_steps;
+    int tb = 0, ua = 0, ub = 0;
+    int qt0 = 0, qt1 = 0, qa = 0, qb = 0;
     if constexpr (!DKDV) {
         const int q_last = min(r0 + 128, p.Sq) - 1;
-        const int Tc = CAUSAL ? (min(p.input_pos + q_last + 1, p.Skv) + BR - 1) / BR
-                              : (p.Skv + BR - 1) / BR;
-        const int tb = win ? min(max(0, p.input_pos + r0 - p.window + 1) / BR, Tc) : 0;
-        s_first = tb;
+        const int Tc = CAUSAL ? (min(p.input_pos + q_last + 1, p.Skv) + BR - 1) / BR : (p.Skv + BR - 1) / BR;
+        tb = win ? min(max(0, p.input_pos + r0 - W + 1) / BR, Tc) : 0;
         n_steps = Tc - tb;
+        int a = tb, e = min(Tc, p.Skv / BR);
+        if (CAUSAL) e = min(e, (p.input_pos + r0 + 1) / BR);
+        if (win) {
+            const int x = p.input_pos + r0 + 128 - W;
+            if (x > 0) a = max(a, (x + BR - 1) / BR);
+        }
+        if (r0 + 128 > p.Sq) e = a;
+        ua = min(a, Tc);
+        ub = max(min(e, Tc), ua);
     } else {
         // Query rows that see some key of [r0, min(r0 + 128, Skv)).
         const int k_last = min(r0 + 128, p.Skv) - 1;
         int lo = 0, hi = p.Sq - 1;
         if (CAUSAL) {
             lo = max(0, r0 - p.input_pos);
-            if (win) hi = min(hi, k_last + p.window - 1 - p.input_pos);
+            if (win) hi = min(hi, k_last + W - 1 - p.input_pos);
         }
         qt0 = lo / BR;
         qt1 = hi < lo ? qt0 : hi / BR + 1;
-        s_first = 0;
-        n_steps = (qt1 - qt0) * p.group;
+        n_steps = (qt1 - qt0) * p.hpw;
+        int a = qt0, e = min(qt1, p.Sq / BR);
+        if (CAUSAL) {
+            const int x = r0 + 127 - p.input_pos;
+            if (x > 0) a = max(a, (x + BR - 1) / BR);
+        }
+        if (win) {
+            const int y = r0 - p.input_pos + W - 32;
+            e = min(e, y < 0 ? 0 : y / BR + 1);
+        }
+        if (r0 + 128 > p.Skv) e = a;
+        qa = min(a, qt1);
+        qb = max(min(e, qt1), qa);
     }
+    const int nq = qt1 - qt0;
 
-    __shared__ __attribute__((aligned(16))) unsigned char t1_lds0[TILE], t1_lds1[TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char t2_lds0[TILE], t2_lds1[TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char t1_0[TILE], t1_1[TILE], t1_2[TILE], t1_3[TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char t2_0[TILE], t2_1[TILE], t2_2[TILE], t2_3[TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char st_0[STB], st_1[STB], st_2[STB], st_3[STB];
+    auto t1_of = [&](auto ph) FA_INLINE -> unsigned char* {
+        constexpr int P = decltype(ph)::value;
+        if constexpr (P == 0) return t1_0;
+        else if constexpr (P == 1) return t1_1;
+        else if constexpr (P == 2) return t1_2;
+        else return t1_3;
+    };
+    auto t2_of = [&](auto ph) FA_INLINE -> unsigned char* {
+        constexpr int P = decltype(ph)::value;
+        if constexpr (P == 0) return t2_0;
+        else if constexpr (P == 1) return t2_1;
+        else if constexpr (P == 2) return t2_2;
+        else return t2_3;
+    };
+    auto st_of = [&](auto ph) FA_INLINE -> unsigned char* {
+        constexpr int P = decltype(ph)::value;
+        if constexpr (P == 0) return st_0;
+        else if constexpr (P == 1) return st_1;
+        else if constexpr (P == 2) return st_2;
+        else return st_3;
+    };
 
     // Tile loads (direct to LDS): lane slot -> (row, physical chunk); it fetches the
-    // logical chunk the swizzle places there.  Rows past the tensor's end read zero.
+    // logical chunk the swizzle places there.  Rows past the tensor's end read zero; steps
+    // past the last one load nothing (zero-size range).  The fetch position advances by one
+    // step per call: DKDV walks the query tiles of one head, then the next head's.
     int src_off;
     {
         const int slot = w * 64 + lane;
         const int row = slot / CPR, pc = slot % CPR;
         src_off = row * ROWB + ((pc ^ b_swz<D>(row)) << 4);
     }
-    // Step s -> (tile start row, head slab) of the streamed tensors.
-    auto tile_of = [&](int s, int& row0, size_t& slab) FA_INLINE {
-        if constexpr (!DKDV) {
-            row0 = (s_first + s) * BR;
-            slab = (size_t)(b * p.Hkv + kv_head) * p.Skv;
-        } else {
-            const int nq = qt1 - qt0;
-            const int hl = s / nq;
-            row0 = (qt0 + (s - hl * nq)) * BR;
-            slab = (size_t)(b * p.Hq + kv_head * p.group + hl) * p.Sq;
-        }
-    };
     const int n_stream = DKDV ? p.Sq : p.Skv;
-    auto fetch = [&](int s, unsigned char* d1, unsigned char* d2) FA_INLINE {
-        int row0;
-        size_t slab;
-        tile_of(s, row0, slab);
-        const int rows = max(0, min(n_stream - row0, BR));
-        const T* s1 = (const T*)(DKDV ? p.q : p.k) + (slab + min(row0, n_stream)) * D;
-        const T* s2 = (const T*)(DKDV ? p.dout : p.v) + (slab + min(row0, n_stream)) * D;
-        const __amdgpu_buffer_rsrc_t r1 = make_rsrc(s1, rows * ROWB);
-        const __amdgpu_buffer_rsrc_t r2 = make_rsrc(s2, rows * ROWB);
+    const T* src1 = (const T*)(DKDV ? p.q : p.k);
+    const T* src2 = (const T*)(DKDV ? p.dout : p.v);
+    int f_s = 0, f_qt = qt0;
+    size_t f_slab = DKDV ? (size_t)(b * p.Hq + kv_head * p.group + gp * p.hpw) * p.Sq
+                         : (size_t)(b * p.Hkv + kv_head) * p.Skv;
+    size_t st_row = 0;   // DKDV: first statistics row and row count of the tile fetched last
+    int st_rows = 0;
+    auto fetch_tiles = [&](unsigned char* d1, unsigned char* d2) FA_INLINE {
+        const int row0 = DKDV ? f_qt * BR : (tb + f_s) * BR;
+        const int rows = f_s < n_steps ? min(n_stream - row0, BR) : 0;
+        const size_t first = rows > 0 ? f_slab + row0 : 0;
+        const __amdgpu_buffer_rsrc_t r1 = make_rsrc_uniform(src1 + first * D, rows * ROWB);
+        const __amdgpu_buffer_rsrc_t r2 = make_rsrc_uniform(src2 + first * D, rows * ROWB);
 #pragma unroll
         for (int i = 0; i < LD; ++i) {
             buffer_load_lds16(r1, d1 + (i * NW + w) * 1024, src_off, i * LOAD_STRIDE);
             buffer_load_lds16(r2, d2 + (i * NW + w) * 1024, src_off, i * LOAD_STRIDE);
         }
+        st_row = first;
+        st_rows = rows;
+        ++f_s;
+        if constexpr (DKDV) {
+            if (++f_qt == qt1) {
+                f_qt = qt0;
+                f_slab += p.Sq;
+            }
+        }
+    };
+    // DKDV, wave 0: the 32 rows' statistics (256 bytes, 4 per lane) of the tile fetched last.
+    auto fetch_stats = [&](unsigned char* ds) FA_INLINE {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc_uniform(p.stats + 2 * st_row, st_rows * 8);
+        buffer_load_lds4(r, ds, lane * 4);
     };
 
     // Row-read offsets (A operand rows l32, chunk 2dk + h) and transposed-read offsets.
@@ -219,22 +342,22 @@ void fa_bwd_kernel(BwdParams p) {
                 off_t[rr][db] = row * ROWB + ((c ^ b_swz<D>(row)) << 4) + (vq >> 1) * 8;
             }
     }
-    auto rows_mfma = [&](const unsigned char* tb, const u32x4 (&x)[DK]) FA_INLINE {
+    auto rows_mfma = [&](const unsigned char* tb_, const u32x4 (&x)[DK]) FA_INLINE {
         f32x16 acc = {};
 #pragma unroll
         for (int dk = 0; dk < DK; ++dk) {
-            const u32x4 a = *(const u32x4*)(tb + off_r[dk]);
+            const u32x4 a = *(const u32x4*)(tb_ + off_r[dk]);
             acc = mfma32<BF16>(a, x[dk], acc);
         }
         return acc;
     };
-    auto trans_mfma = [&](const unsigned char* tb, const u32x4 (&pk)[2], f32x16 (&acc)[DB]) FA_INLINE {
+    auto trans_mfma = [&](const unsigned char* tb_, const u32x4 (&pk)[2], f32x16 (&acc)[DB]) FA_INLINE {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                const u32x2 y0 = lds_read_tr16(tb + 16 * hf * ROWB + off_t[0][db]);
-                const u32x2 y1 = lds_read_tr16(tb + 16 * hf * ROWB + off_t[1][db]);
+                const u32x2 y0 = lds_read_tr16(tb_ + 16 * hf * ROWB + off_t[0][db]);
+                const u32x2 y1 = lds_read_tr16(tb_ + 16 * hf * ROWB + off_t[1][db]);
                 const u32x4 a = {y0[0], y0[1], y1[0], y1[1]};
                 acc[db] = mfma32<BF16>(a, pk[hf], acc[db]);
             }
@@ -246,47 +369,114 @@ void fa_bwd_kernel(BwdParams p) {
         acc1[db] = (f32x16){};
         acc2[db] = (f32x16){};
     }
+    f32x16 sc0 = {}, dp0 = {}, sc1 = {}, dp1 = {};   // S and dP of two consecutive tiles
 
-    auto step = [&](int s, const unsigned char* t1, const unsigned char* t2) FA_INLINE {
-        int row0;
-        size_t slab;
-        tile_of(s, row0, slab);
-        // DKDV: the statistics of the 16 streamed rows this lane holds.
-        float lse2[16], dv16[16];
+    // s_waitcnt vmcnt(N) then s_barrier, as one asm statement (also a compiler memory
+    // barrier).
+    auto wait_barrier = [&](auto n_tag) FA_INLINE {
+        constexpr int N = decltype(n_tag)::value;
+        static_assert(N < 64, "vmcnt range");
+        constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+        asm volatile("s_waitcnt %0\n\ts_barrier" ::"n"(imm) : "memory");
+    };
+    // End of a step: wave 0 of DKDV also loads the statistics of the tile fetched at the
+    // step's start; then wait until only those loads (the newest tile's) are in flight,
+    // and the workgroup barrier.
+    auto end_step = [&](auto pf) FA_INLINE {
         if constexpr (DKDV) {
+            if (w == 0) {
+                fetch_stats(st_of(pf));
+                wait_barrier(std::integral_constant<int, NL + 1>{});
+            } else {
+                wait_barrier(std::integral_constant<int, NL>{});
+            }
+        } else {
+            wait_barrier(std::integral_constant<int, NL>{});
+        }
+    };
+
+    int c_row0 = DKDV ? qt0 * BR : tb * BR;   // first streamed row of the step being computed
+    int c_qt = qt0;
+
+    // Step masks: DQ: key tiles outside [ua, ub); DKDV: query tiles outside [qa, qb).
+    auto step = [&](auto ph_tag) FA_INLINE {
+        constexpr int PH = decltype(ph_tag)::value;
+        const bool masked = DKDV ? (c_qt < qa || c_qt >= qb) : (c_row0 < ua * BR || c_row0 >= ub * BR);
+        using PN = std::integral_constant<int, (PH + 1) & 3>;
+        using PF = std::integral_constant<int, (PH + 3) & 3>;
+        using PC = std::integral_constant<int, PH>;
+        f32x16& sc = (PH & 1) ? sc1 : sc0;
+        f32x16& dp = (PH & 1) ? dp1 : dp0;
+        f32x16& scn = (PH & 1) ? sc0 : sc1;
+        f32x16& dpn = (PH & 1) ? dp0 : dp1;
+
+        fetch_tiles(t1_of(PF{}), t2_of(PF{}));
+        // Next tile's products (DQ: S^T and dP^T, lane = query; DKDV: S and dP, lane = key).
+        scn = rows_mfma(t1_of(PN{}), x1);
+        dpn = rows_mfma(t2_of(PN{}), x2);
+
+        // This tile: P and dS.  Element i of a lane is streamed row c_row0 + 4h + ci(i).
+        float l2v[16], ddv[16];
+        if constexpr (DKDV) {
+            const unsigned char* st = st_of(PC{});
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 u0 = *(const f32x4*)(st + (8 * g4 + 4 * h) * 8);
+                const f32x4 u1 = *(const f32x4*)(st + (8 * g4 + 4 * h) * 8 + 16);
+                l2v[4 * g4 + 0] = u0[0];
+                ddv[4 * g4 + 0] = u0[1];
+                l2v[4 * g4 + 1] = u0[2];
+                ddv[4 * g4 + 1] = u0[3];
+                l2v[4 * g4 + 2] = u1[0];
+                ddv[4 * g4 + 2] = u1[1];
+                l2v[4 * g4 + 3] = u1[2];
+                ddv[4 * g4 + 3] = u1[3];
+            }
+        } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = min(row0 + 8 * g4 + 4 * h + e, p.Sq - 1);
-                    const float l = p.lse[slab + r];
-                    lse2[4 * g4 + e] = l == -__builtin_inff() ? __builtin_inff() : l * 1.44269504088896340736f;
-                    dv16[4 * g4 + e] = p.dvec[slab + r];
-                }
+            for (int i = 0; i < 16; ++i) {
+                l2v[i] = lse2_own;
+                ddv[i] = d_own;
             }
         }
-        f32x16 sc = rows_mfma(t1, x1);    // DQ: S^T (lane = query); DKDV: S (lane = key)
-        f32x16 dp = rows_mfma(t2, x2);    // DQ: dP^T; DKDV: dP
-        // Mask: streamed row index and own row index of each element.
-        const int own = rw0 + l32;
-        u32x4 pk[2], dsk[2];
         float pe[16], de[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int sr = row0 + 8 * (i >> 2) + 4 * h + (i & 3);   // streamed row
-            const int qrow = DKDV ? sr : own;
-            const int key = DKDV ? own : sr;
-            bool vis = key < p.Skv && qrow < p.Sq;
-            if (CAUSAL) {
-                vis = vis && key <= p.input_pos + qrow;
-                if (win) vis = vis && key >= p.input_pos + qrow - p.window + 1;
-            }
-            const float l2 = DKDV ? lse2[i] : lse2_own;
-            const float dd = DKDV ? dv16[i] : d_own;
-            const float pv = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], p.c, -l2)) : 0.0f;
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], p.c, -l2v[i]));
             pe[i] = pv;
-            de[i] = pv * (dp[i] - dd);
+            de[i] = pv * (dp[i] - ddv[i]);
         }
+        // Mask (edge tiles only): the lane's element i is streamed row c_row0 + 4h + ci(i),
+        // ci(i) = 8(i/4) + i%4 < 32.  Visible elements form one range of ci, [lo, hi); bit
+        // ci of `vis` is set inside it, and a one-bit signed extract turns that bit into an
+        // all-ones / zero word that clears p and dS where masked.
+        if (masked) {
+            const int base = c_row0 + 4 * h;
+            const int own = rw0 + l32;
+            int lo = 0, hi;
+            if constexpr (DKDV) {   // streamed = query, own = key
+                hi = p.Sq - base;
+                if (CAUSAL) lo = own - p.input_pos - base;                 // query >= key - input_pos
+                if (win) hi = min(hi, own - p.input_pos - base + W);       // query < key - input_pos + W
+            } else {                // streamed = key, own = query
+                hi = p.Skv - base;
+                if (CAUSAL) hi = min(hi, p.input_pos + own - base + 1);    // key <= input_pos + query
+                if (win) lo = p.input_pos + own - base - W + 1;            // key >= input_pos + query - W + 1
+            }
+            if (own >= n_own) hi = 0;
+            lo = min(max(lo, 0), 32);
+            hi = min(max(hi, 0), 32);
+            const uint32_t below_hi = hi >= 32 ? ~0u : (1u << hi) - 1u;
+            const uint32_t below_lo = lo >= 32 ? ~0u : (1u << lo) - 1u;
+            const uint32_t vis = hi > lo ? below_hi & ~below_lo : 0u;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe((int)vis, 8 * (i >> 2) + (i & 3), 1);
+                pe[i] = __uint_as_float(__float_as_uint(pe[i]) & keep);
+                de[i] = __uint_as_float(__float_as_uint(de[i]) & keep);
+            }
+        }
+        u32x4 pk[2], dsk[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const float* e = pe + 8 * hf;
@@ -296,23 +486,50 @@ void fa_bwd_kernel(BwdParams p) {
             dsk[hf] = (u32x4){pack2<BF16>(f[0], f[1]), pack2<BF16>(f[2], f[3]), pack2<BF16>(f[4], f[5]),
                               pack2<BF16>(f[6], f[7])};
         }
-        trans_mfma(t1, dsk, acc1);        // DQ: dQ^T += K^T dS^T; DKDV: dK^T += Q^T dS
-        if constexpr (DKDV) trans_mfma(t2, pk, acc2);   // dV^T += dO^T P
+        // Keep the transposed reads below this point: hoisted above, they would be live
+        // alongside the next tile's S / dP and this tile's softmax temporaries.
+        __builtin_amdgcn_sched_barrier(0);
+        trans_mfma(t1_of(PC{}), dsk, acc1);                       // DQ: dQ^T += K^T dS^T; DKDV: dK^T += Q^T dS
+        if constexpr (DKDV) trans_mfma(t2_of(PC{}), pk, acc2);    // dV^T += dO^T P
+        end_step(PF{});
+        if constexpr (DKDV) {
+            if (++c_qt == qt1) c_qt = qt0;
+            c_row0 = c_qt * BR;
+        } else {
+            c_row0 += BR;
+        }
     };
 
     if (n_steps > 0) {
-        fetch(0, t1_lds0, t2_lds0);
-        __syncthreads();
-        int s = 0;
-        for (; s + 1 < n_steps; s += 2) {
-            fetch(s + 1, t1_lds1, t2_lds1);
-            step(s, t1_lds0, t2_lds0);
-            __syncthreads();
-            if (s + 2 < n_steps) fetch(s + 2, t1_lds0, t2_lds0);
-            step(s + 1, t1_lds1, t2_lds1);
-            __syncthreads();
+        // Prologue: tiles 0, 1, 2 in flight, wait for 0 and 1, products of tile 0.
+        fetch_tiles(t1_0, t2_0);
+        if (DKDV && w == 0) fetch_stats(st_0);
+        fetch_tiles(t1_1, t2_1);
+        if (DKDV && w == 0) fetch_stats(st_1);
+        fetch_tiles(t1_2, t2_2);
+        if (DKDV && w == 0) {
+            fetch_stats(st_2);
+            wait_barrier(std::integral_constant<int, NL + 1>{});
+        } else {
+            wait_barrier(std::integral_constant<int, NL>{});
         }
-        if (s < n_steps) step(s, t1_lds0, t2_lds0);
+        sc0 = rows_mfma(t1_0, x1);
+        dp0 = rows_mfma(t2_0, x2);
+
+        // Unrolled by four so the buffer phase of each copy of the step is fixed.
+        int i = 0;
+        for (; i + 3 < n_steps; i += 4) {
+            step(P0{});
+            step(P1{});
+            step(P2{});
+            step(P3{});
+        }
+        if (i < n_steps) { step(P0{}); ++i; }
+        if (i < n_steps) { step(P1{}); ++i; }
+        if (i < n_steps) { step(P2{}); ++i; }
+        // The last steps issued loads past the range (zero-size): let them land before the
+        // workgroup can end and its LDS be reused.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
     // Store: the wave's own rows; lane l holds 16 consecutive d of row rw0 + l32 per
@@ -332,9 +549,24 @@ void fa_bwd_kernel(BwdParams p) {
                 *(u32x4*)(orow + db * 32 + 16 * h + 8) = w1;
             }
         };
+        auto store_f32 = [&](float* base, const f32x16 (&acc)[DB]) FA_INLINE {
+            float* orow = base + (own_head * n_own + row) * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4)
+                    *(f32x4*)(orow + db * 32 + 16 * h + 4 * v4) =
+                        (f32x4){acc[db][4 * v4], acc[db][4 * v4 + 1], acc[db][4 * v4 + 2], acc[db][4 * v4 + 3]};
+        };
         if constexpr (DKDV) {
-            store(p.dk, own_head, acc1, p.scale);
-            store(p.dv, own_head, acc2, 1.0f);
+            if (p.gsplit == 1) {
+                store(p.dk, own_head, acc1, p.scale);
+                store(p.dv, own_head, acc2, 1.0f);
+            } else {
+                const size_t n = (size_t)p.B * p.Hkv * p.Skv * D;
+                store_f32(p.part + (size_t)(2 * gp) * n, acc1);
+                store_f32(p.part + (size_t)(2 * gp + 1) * n, acc2);
+            }
         } else {
             store(p.dq, own_head, acc1, p.scale);
         }

@@ -154,7 +154,9 @@ def time_gpu(name, steps, warmup, config=-1, splitkv=False, backward=False):
         g.manual_seed(1)
         dout = torch.randn(q.shape, generator=g, dtype=torch.float32).to(q.dtype).to(dev)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        ws = torch.empty(max(16, w["B"] * w["Hq"] * w["Sq"] * 4), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(16, fa.bwd_workspace_size(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"],
+                                                      w["D"], kw["causal"])),
+                         dtype=torch.uint8, device=dev)
 
         def step():
             fa.fa_bwd_into(q, k, v, out, lse, dout, dq, dk, dv, ws, scale=kw["scale"],

@@ -206,9 +206,12 @@ size_t fa_splitkv_workspace_size(int B, int Hq, int Sq, int D, int num_splits);
  *   dq / dk, dv         outputs, [B, Hq, Sq, D] / [B, Hkv, Skv, D] in `dtype`; they must not
  *                       overlap any input, each other or the workspace.
  *   scale .. window     as for fa_fwd_splitkv (window needs causal).
- *   workspace           >= fa_bwd_workspace_size(B, Hq, Sq) bytes of device memory, 16-byte
- *                       aligned, owned by the caller (it receives D, fp32 [B*Hq*Sq]).
- *   stream              the kernels (D, then dk/dv, then dq) are enqueued on it in order.
+ *   workspace           >= fa_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, D, causal) bytes of
+ *                       device memory, 16-byte aligned, owned by the caller (it receives
+ *                       the row statistics LSE * log2(e) and D = rowsum(dout * out), and
+ *                       fp32 partial dk / dv sums when the head group is split).
+ *   stream              the kernels (row statistics, dk/dv, the partial sum if any, dq)
+ *                       are enqueued on it in order.
  * Checks: as for fa_fwd (pointers, sizes, head group, head dim, dtype, scale, input_pos,
  * window, alignment, aliasing), then the workspace (NULL, misaligned, too small,
  * overlapping).  B*Hq*Sq == 0 with K/V rows present writes zero dk and dv.
@@ -220,8 +223,13 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
            int causal, int input_pos, int window, int dtype,
            void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes fa_bwd needs: B * Hq * Sq * 4 (0 for an empty problem). */
-size_t fa_bwd_workspace_size(int B, int Hq, int Sq);
+/* Workspace bytes fa_bwd needs (0 for an empty or invalid problem): the row statistics,
+ * B * Hq * Sq * 8 rounded up to 256, plus, when the dK/dV grid would have fewer than two
+ * workgroups per CU (causal) or one (non-causal) and the head group allows it, fp32
+ * partial sums of dk and dv for each of the g parts the group's query heads are split
+ * into (g * 2 * B * Hkv * Skv * D * 4; g = the smallest divisor of Hq / Hkv that reaches
+ * that grid size, else Hq / Hkv). */
+size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal);
 
 /* Configuration the dispatch table picks for these arguments, or a negative fa_status. */
 int fa_select_config(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,

@@ -74,7 +74,9 @@ BWD_CASES = [
     (3, 6, 3, 129, 64, 64, True, 0, 0),        # Sq > Skv
     (1, 8, 2, 300, 300, 128, True, 0, 45),     # sliding window
     (1, 8, 8, 129, 64, 128, True, 0, 9),       # window with empty rows
-    (1, 32, 4, 256, 256, 128, True, 0, 0),
+    (1, 32, 4, 256, 256, 128, True, 0, 0),     # small K/V grid: the group split 8 ways
+    (1, 32, 8, 256, 2048, 64, False, 0, 0),    # GQA 4 split over 2 workgroups
+    (2, 32, 16, 128, 2048, 64, True, 1920, 0), # GQA 2 with a K/V grid large enough not to split
 ]
 
 
@@ -88,6 +90,19 @@ def test_backward_shapes(case, dtype):
     scale = 1.0 / math.sqrt(D)
     got = run_bwd(q, k, v, do, scale, causal, pos, W)
     check(q, k, v, do, scale, causal, pos, W, got, f"{case} {dtype}")
+
+
+def test_backward_workspace_sizes():
+    """The workspace holds 8 bytes of row statistics per query row (rounded up to 256),
+    plus fp32 dk / dv partials for each part of a split head group."""
+    stats = lambda B, Hq, Sq: (B * Hq * Sq * 8 + 255) // 256 * 256
+    assert fa.bwd_workspace_size(1, 8, 8, 100, 100, 128, True) == stats(1, 8, 100)      # MHA
+    assert fa.bwd_workspace_size(1, 32, 4, 256, 256, 128, True) == \
+        stats(1, 32, 256) + 8 * 2 * 4 * 256 * 128 * 4                                    # split 8
+    assert fa.bwd_workspace_size(1, 32, 8, 256, 2048, 64, False) == \
+        stats(1, 32, 256) + 2 * 2 * 8 * 2048 * 64 * 4                                    # split 2
+    assert fa.bwd_workspace_size(2, 32, 16, 128, 2048, 64, True) == stats(2, 32, 128)    # none
+    assert fa.bwd_workspace_size(0, 8, 8, 100, 100, 128, True) == 0
 
 
 def test_backward_medium_gqa_causal():
