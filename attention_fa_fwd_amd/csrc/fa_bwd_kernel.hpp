@@ -17,7 +17,9 @@
 //    group's query heads are split over several workgroups, each writing an fp32 partial
 //    that fa_bwd_reduce_kernel sums in a fixed order.
 //  * fa_bwd_kernel<DQ>: a wave owns 32 query rows (Q and dO rows in registers); the
-//    workgroup streams 32-key tiles of K and V and accumulates dQ^T.
+//    workgroup streams 32-key tiles of K and V and accumulates dQ^T.  It fits 256
+//    registers, so two workgroups share a CU; DKDV holds twice the accumulators and runs
+//    one wave per SIMD.
 // Both use the forward kernel's MFMA formulation: the streamed tile is the A operand of
 // v_mfma_f32_32x32x16 (row reads from LDS), the wave's own rows are the B operand, so the
 // 32x32 accumulator gives each lane one of its own rows and 16 streamed rows; P and dS go
@@ -26,11 +28,11 @@
 // is read both ways, its LDS layout uses one XOR swizzle of the 16-byte chunks that a
 // bank model finds conflict-free for both the row reads and the transposed reads.
 //
-// Pipeline (both gradient kernels): four LDS buffers.  Step j loads tile j+3, issues the
+// Pipeline (both gradient kernels): NB LDS buffers.  Step j loads tile j+NB-1, issues the
 // S / dP products of tile j+1 into a second register set, then turns tile j's S / dP into
 // P and dS and issues the two transposed products of tile j -- so the exp2 work of one
 // tile overlaps the matrix work of the next in one straight-line block.  A step ends by
-// waiting for tile j+2 only (tile j+3's loads stay in flight) and one barrier.
+// waiting for tile j+2 only (later tiles' loads stay in flight) and one barrier.
 #pragma once
 
 #include "fa_fwd_kernel.hpp"
@@ -144,9 +146,28 @@ __global__ __launch_bounds__(256) void fa_bwd_reduce_kernel(const float* part, v
 
 enum BwdMode { BWD_DQ = 0, BWD_DKDV = 1 };
 
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>), in order.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// LDS buffer sets of the streamed-tile pipeline: step j loads tile j + NB - 1, so NB - 3
+// tiles' loads stay in flight across a step's closing wait.  Even, so that a step's
+// phase (j mod NB) also fixes which of the two S / dP register sets it uses.  DQ runs two
+// workgroups per CU and keeps to four sets; DKDV has the CU's LDS to itself.
+template <int MODE>
+struct BwdBuffers {
+    static constexpr int value = MODE == BWD_DKDV ? 4 : 4;
+};
+
 template <int D, bool CAUSAL, bool BF16, int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
-                          amdgpu_waves_per_eu(1, 1)))
+                          amdgpu_waves_per_eu(MODE == BWD_DQ ? 2 : 1, MODE == BWD_DQ ? 2 : 1)))
 void fa_bwd_kernel(BwdParams p) {
     constexpr int NT = 256, NW = 4;
     constexpr int BR = 32;               // streamed rows per tile
@@ -159,10 +180,8 @@ void fa_bwd_kernel(BwdParams p) {
     constexpr bool DKDV = MODE == BWD_DKDV;
     constexpr int STB = DKDV ? BR * 8 : 16;   // row statistics of a streamed tile
     typedef uint16_t T;
-    using P0 = std::integral_constant<int, 0>;
-    using P1 = std::integral_constant<int, 1>;
-    using P2 = std::integral_constant<int, 2>;
-    using P3 = std::integral_constant<int, 3>;
+    constexpr int NB = BwdBuffers<MODE>::value;
+    static_assert(NB % 2 == 0 && NB >= 4 && NB <= 6, "buffer sets");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -255,29 +274,36 @@ void fa_bwd_kernel(BwdParams p) {
     }
     const int nq = qt1 - qt0;
 
-    __shared__ __attribute__((aligned(16))) unsigned char t1_0[TILE], t1_1[TILE], t1_2[TILE], t1_3[TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char t2_0[TILE], t2_1[TILE], t2_2[TILE], t2_3[TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char st_0[STB], st_1[STB], st_2[STB], st_3[STB];
+    constexpr int T4 = NB > 4 ? TILE : 16, S4 = NB > 4 ? STB : 16;
+    __shared__ __attribute__((aligned(16))) unsigned char t1_0[TILE], t1_1[TILE], t1_2[TILE], t1_3[TILE], t1_4[T4], t1_5[T4];
+    __shared__ __attribute__((aligned(16))) unsigned char t2_0[TILE], t2_1[TILE], t2_2[TILE], t2_3[TILE], t2_4[T4], t2_5[T4];
+    __shared__ __attribute__((aligned(16))) unsigned char st_0[STB], st_1[STB], st_2[STB], st_3[STB], st_4[S4], st_5[S4];
     auto t1_of = [&](auto ph) FA_INLINE -> unsigned char* {
         constexpr int P = decltype(ph)::value;
         if constexpr (P == 0) return t1_0;
         else if constexpr (P == 1) return t1_1;
         else if constexpr (P == 2) return t1_2;
-        else return t1_3;
+        else if constexpr (P == 3) return t1_3;
+        else if constexpr (P == 4) return t1_4;
+        else return t1_5;
     };
     auto t2_of = [&](auto ph) FA_INLINE -> unsigned char* {
         constexpr int P = decltype(ph)::value;
         if constexpr (P == 0) return t2_0;
         else if constexpr (P == 1) return t2_1;
         else if constexpr (P == 2) return t2_2;
-        else return t2_3;
+        else if constexpr (P == 3) return t2_3;
+        else if constexpr (P == 4) return t2_4;
+        else return t2_5;
     };
     auto st_of = [&](auto ph) FA_INLINE -> unsigned char* {
         constexpr int P = decltype(ph)::value;
         if constexpr (P == 0) return st_0;
         else if constexpr (P == 1) return st_1;
         else if constexpr (P == 2) return st_2;
-        else return st_3;
+        else if constexpr (P == 3) return st_3;
+        else if constexpr (P == 4) return st_4;
+        else return st_5;
     };
 
     // Tile loads (direct to LDS): lane slot -> (row, physical chunk); it fetches the
@@ -380,19 +406,17 @@ void fa_bwd_kernel(BwdParams p) {
         asm volatile("s_waitcnt %0\n\ts_barrier" ::"n"(imm) : "memory");
     };
     // End of a step: wave 0 of DKDV also loads the statistics of the tile fetched at the
-    // step's start; then wait until only those loads (the newest tile's) are in flight,
-    // and the workgroup barrier.
+    // step's start; then wait until only the loads of the newest NB - 3 tiles are in
+    // flight (the next step's tile j+2 has landed), and the workgroup barrier.
+    auto wait_tiles = [&]() FA_INLINE {
+        if (DKDV && w == 0) wait_barrier(std::integral_constant<int, (NB - 3) * (NL + 1)>{});
+        else wait_barrier(std::integral_constant<int, (NB - 3) * NL>{});
+    };
     auto end_step = [&](auto pf) FA_INLINE {
         if constexpr (DKDV) {
-            if (w == 0) {
-                fetch_stats(st_of(pf));
-                wait_barrier(std::integral_constant<int, NL + 1>{});
-            } else {
-                wait_barrier(std::integral_constant<int, NL>{});
-            }
-        } else {
-            wait_barrier(std::integral_constant<int, NL>{});
+            if (w == 0) fetch_stats(st_of(pf));
         }
+        wait_tiles();
     };
 
     int c_row0 = DKDV ? qt0 * BR : tb * BR;   // first streamed row of the step being computed
@@ -402,8 +426,8 @@ void fa_bwd_kernel(BwdParams p) {
     auto step = [&](auto ph_tag) FA_INLINE {
         constexpr int PH = decltype(ph_tag)::value;
         const bool masked = DKDV ? (c_qt < qa || c_qt >= qb) : (c_row0 < ua * BR || c_row0 >= ub * BR);
-        using PN = std::integral_constant<int, (PH + 1) & 3>;
-        using PF = std::integral_constant<int, (PH + 3) & 3>;
+        using PN = std::integral_constant<int, (PH + 1) % NB>;
+        using PF = std::integral_constant<int, (PH + NB - 1) % NB>;
         using PC = std::integral_constant<int, PH>;
         f32x16& sc = (PH & 1) ? sc1 : sc0;
         f32x16& dp = (PH & 1) ? dp1 : dp0;
@@ -489,8 +513,38 @@ void fa_bwd_kernel(BwdParams p) {
         // Keep the transposed reads below this point: hoisted above, they would be live
         // alongside the next tile's S / dP and this tile's softmax temporaries.
         __builtin_amdgcn_sched_barrier(0);
-        trans_mfma(t1_of(PC{}), dsk, acc1);                       // DQ: dQ^T += K^T dS^T; DKDV: dK^T += Q^T dS
-        if constexpr (DKDV) trans_mfma(t2_of(PC{}), pk, acc2);    // dV^T += dO^T P
+        // DKDV: the transposed operands of dK's product are read first; dV's are read while
+        // dK's MFMAs run.
+        if constexpr (DKDV) {
+            u32x4 ya[DB][2], yb[DB][2];
+            const unsigned char* tA = t1_of(PC{});
+            const unsigned char* tB = t2_of(PC{});
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const u32x2 y0 = lds_read_tr16(tA + 16 * hf * ROWB + off_t[0][db]);
+                    const u32x2 y1 = lds_read_tr16(tA + 16 * hf * ROWB + off_t[1][db]);
+                    ya[db][hf] = (u32x4){y0[0], y0[1], y1[0], y1[1]};
+                }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const u32x2 y0 = lds_read_tr16(tB + 16 * hf * ROWB + off_t[0][db]);
+                    const u32x2 y1 = lds_read_tr16(tB + 16 * hf * ROWB + off_t[1][db]);
+                    yb[db][hf] = (u32x4){y0[0], y0[1], y1[0], y1[1]};
+                    acc1[db] = mfma32<BF16>(ya[db][hf], dsk[hf], acc1[db]);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) acc2[db] = mfma32<BF16>(yb[db][hf], pk[hf], acc2[db]);
+        } else {
+            trans_mfma(t1_of(PC{}), dsk, acc1);
+        }
         end_step(PF{});
         if constexpr (DKDV) {
             if (++c_qt == qt1) c_qt = qt0;
@@ -501,32 +555,40 @@ void fa_bwd_kernel(BwdParams p) {
     };
 
     if (n_steps > 0) {
-        // Prologue: tiles 0, 1, 2 in flight, wait for 0 and 1, products of tile 0.
-        fetch_tiles(t1_0, t2_0);
-        if (DKDV && w == 0) fetch_stats(st_0);
-        fetch_tiles(t1_1, t2_1);
-        if (DKDV && w == 0) fetch_stats(st_1);
-        fetch_tiles(t1_2, t2_2);
-        if (DKDV && w == 0) {
-            fetch_stats(st_2);
-            wait_barrier(std::integral_constant<int, NL + 1>{});
-        } else {
-            wait_barrier(std::integral_constant<int, NL>{});
-        }
+        // Prologue: tiles 0 .. NB-2 in flight, wait for 0 and 1, products of tile 0.
+        static_for<NB - 1>([&](auto ph) FA_INLINE {
+            fetch_tiles(t1_of(ph), t2_of(ph));
+            if (DKDV && w == 0) fetch_stats(st_of(ph));
+        });
+        wait_tiles();
         sc0 = rows_mfma(t1_0, x1);
         dp0 = rows_mfma(t2_0, x2);
 
-        // Unrolled by four so the buffer phase of each copy of the step is fixed.
+        // Unrolled by NB so the buffer phase of each copy of the step is fixed.
         int i = 0;
-        for (; i + 3 < n_steps; i += 4) {
+        using P0 = std::integral_constant<int, 0>;
+        using P1 = std::integral_constant<int, 1>;
+        using P2 = std::integral_constant<int, 2>;
+        using P3 = std::integral_constant<int, 3>;
+        using P4 = std::integral_constant<int, 4>;
+        using P5 = std::integral_constant<int, 5>;
+        for (; i + NB - 1 < n_steps; i += NB) {
             step(P0{});
             step(P1{});
             step(P2{});
             step(P3{});
+            if constexpr (NB > 4) {
+                step(P4{});
+                step(P5{});
+            }
         }
         if (i < n_steps) { step(P0{}); ++i; }
         if (i < n_steps) { step(P1{}); ++i; }
         if (i < n_steps) { step(P2{}); ++i; }
+        if constexpr (NB > 4) {
+            if (i < n_steps) { step(P3{}); ++i; }
+            if (i < n_steps) { step(P4{}); ++i; }
+        }
         // The last steps issued loads past the range (zero-size): let them land before the
         // workgroup can end and its LDS be reused.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
