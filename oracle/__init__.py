@@ -8,6 +8,7 @@ from .attention import (  # noqa: F401
     LN2,
     LOG2E,
     attention_backward_blocked,
+    attention_backward_sampled,
     attention_blocked,
     attention_fp8_blocked,
     attention_key_range,

@@ -51,7 +51,8 @@ Four forms are provided, written independently of one another:
                                from the format's definition, and the definition over
                                dequantised fp8 queries and keys.
 * ``attention_backward_blocked``: the gradients dQ, dK, dV from the softmax
-                               derivative (the backward pass).
+                               derivative (the backward pass); ``attention_backward_sampled``
+                               evaluates them at sampled rows of full-size problems.
 
 Parity status: every function here is pinned by the CPU test suite against
 brute force, an independent library routine (PyTorch's CPU float64
@@ -593,3 +594,85 @@ def attention_backward_blocked(q, k, v, do, scale, causal=False, input_pos=0, wi
                 dQ[b, hq, rows] = scale * (dS @ kh)
                 dK[b, g] += scale * (dS.T @ qr)
     return dQ, dK, dV
+
+
+def attention_backward_sampled(q, k, v, do, scale, causal, input_pos, dq_samples, dkv_samples,
+                               window=0):
+    """The gradients of ``attention_backward_blocked`` evaluated at sampled rows only.
+
+    ``dq_samples``: (b, hq, i) query rows whose dQ row is wanted; ``dkv_samples``: (b, g, j)
+    key rows whose dK and dV rows are wanted.  A dQ row needs only its own softmax row.  A
+    dK / dV row sums over every query row of every query head in its group that sees the
+    key, and each term needs that query row's normaliser and D_i = sum_j P_ij dP_ij, so
+    the (b, g) groups named in ``dkv_samples`` get their row statistics (log-sum-exp and
+    D) for all query rows first, then the sampled keys' columns of P and dS.  The
+    formulas are those of ``attention_backward_blocked``.  Returns (dQ [n, D], dK [m, D],
+    dV [m, D]) as float64 arrays.
+    """
+    B, Hq, Hkv, Sq, Skv, D = _shapes(q, k, v)
+    if not (math.isfinite(scale) and scale > 0):
+        raise ValueError("scale must be finite and > 0")
+    _check_window(causal, window)
+    do = np.asarray(do)
+    if do.shape != (B, Hq, Sq, D):
+        raise ValueError("do must have q's shape")
+    group = Hq // Hkv
+    dq_samples, dkv_samples = list(dq_samples), list(dkv_samples)
+
+    # dQ rows: the whole softmax row of each sampled query.
+    dQ = np.zeros((len(dq_samples), D))
+    for n, (b, hq, i) in enumerate(dq_samples):
+        g = kv_head_of(hq, Hq, Hkv)
+        vis = key_visibility([i], Skv, causal, input_pos, window)
+        if not vis.any():
+            continue
+        kh = np.asarray(k[b, g], np.float64)
+        vh = np.asarray(v[b, g], np.float64)
+        s = scaled_scores(np.asarray(q[b, hq, i:i + 1], np.float64), kh, scale)
+        m, e, l = masked_softmax_stats(s, vis)
+        P = e / l
+        dO_i = np.asarray(do[b, hq, i:i + 1], np.float64)
+        dP = dO_i @ vh.T
+        dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+        dQ[n] = scale * (dS @ kh)[0]
+
+    # dK / dV rows: row statistics of the whole group, then the sampled key columns.
+    dK = np.zeros((len(dkv_samples), D))
+    dV = np.zeros((len(dkv_samples), D))
+    for (b, g) in sorted({(b, g) for b, g, _ in dkv_samples}):
+        kh = np.asarray(k[b, g], np.float64)
+        vh = np.asarray(v[b, g], np.float64)
+        heads = range(g * group, (g + 1) * group)
+        lse = np.full((group, Sq), -np.inf)
+        dvec = np.zeros((group, Sq))
+        for t, hq in enumerate(heads):
+            for i0 in range(0, Sq, 512):
+                i1 = min(Sq, i0 + 512)
+                vis = key_visibility(np.arange(i0, i1), Skv, causal, input_pos, window)
+                rows = i0 + np.nonzero(vis.any(axis=1))[0]
+                if rows.size == 0:
+                    continue
+                s = scaled_scores(np.asarray(q[b, hq, rows], np.float64), kh, scale)
+                m, e, l = masked_softmax_stats(s, vis[rows - i0])
+                P = e / l
+                dP = np.asarray(do[b, hq, rows], np.float64) @ vh.T
+                lse[t, rows] = log_sum_exp(m, l)
+                dvec[t, rows] = (P * dP).sum(axis=1)
+        vis_all = key_visibility(np.arange(Sq), Skv, causal, input_pos, window)
+        for n, (bb, gg, j) in enumerate(dkv_samples):
+            if (bb, gg) != (b, g):
+                continue
+            rows = np.nonzero(vis_all[:, j])[0]
+            for t, hq in enumerate(heads):
+                if rows.size == 0:
+                    continue
+                qr = np.asarray(q[b, hq, rows], np.float64)
+                dOr = np.asarray(do[b, hq, rows], np.float64)
+                s = scale * (qr @ kh[j])
+                P = np.exp(s - lse[t, rows])
+                dP = dOr @ vh[j]
+                dS = P * (dP - dvec[t, rows])
+                dV[n] += P @ dOr
+                dK[n] += scale * (dS @ qr)
+    return dQ, dK, dV
+

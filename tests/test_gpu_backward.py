@@ -113,6 +113,47 @@ def test_backward_medium_gqa_causal():
     check(q, k, v, do, 1 / math.sqrt(128), True, 0, 0, got, "2048 gqa causal")
 
 
+def test_backward_headline_sampled():
+    """The causal GQA-8 8192-token bf16 workload in the launch configuration bench.py times
+    (fa_bwd_into with a preallocated workspace; the group split of 2 the library picks),
+    checked on sampled dQ rows of every head and sampled dK / dV rows of one K/V head
+    against the fp64 oracle evaluated at those rows."""
+    from attention_fa_fwd_amd.inputs import make_workload
+
+    name = "gqa8_causal_s8192_d128_bf16"
+    q, k, v, kw = make_workload(name, seed=0)
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    g = torch.Generator(device="cpu")
+    g.manual_seed(1)
+    do = torch.randn(q.shape, generator=g, dtype=torch.float32).to(q.dtype)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    out, lse = fa.fa_fwd(qd, kd, vd, scale=kw["scale"], causal=True)
+    ws = torch.empty(fa.bwd_workspace_size(B, Hq, Hkv, Sq, Skv, D, True), dtype=torch.uint8, device=DEV)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    _say("headline backward", name, "workspace", ws.numel())
+    fa.fa_bwd_into(qd, kd, vd, out, lse, dod, dq, dk, dv, ws, scale=kw["scale"], causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    qs = [(0, int(rng.integers(Hq)), i) for i in (0, 1, 31, 32, 127, 128, 4095, 8191)]
+    qs += [(0, int(rng.integers(Hq)), int(rng.integers(Sq))) for _ in range(24)]
+    gk = int(rng.integers(Hkv))
+    ks = [(0, gk, j) for j in (0, 1, 127, 128, 4096, 8064, 8191)]
+    ks += [(0, gk, int(rng.integers(Skv))) for _ in range(9)]
+    rq, rk, rv = oracle.attention_backward_sampled(q.double().numpy(), k.double().numpy(),
+                                                   v.double().numpy(), do.double().numpy(),
+                                                   kw["scale"], True, 0, qs, ks)
+    got = (np.stack([dq[b, h, i].double().cpu().numpy() for b, h, i in qs]),
+           np.stack([dk[b, g_, j].double().cpu().numpy() for b, g_, j in ks]),
+           np.stack([dv[b, g_, j].double().cpu().numpy() for b, g_, j in ks]))
+    top = max(float(np.max(np.abs(r))) for r in (rq, rk, rv))
+    for nm, gv, r in zip(("dq", "dk", "dv"), got, (rq, rk, rv)):
+        err = float(np.max(np.abs(gv - r)))
+        bound = TOL_REL[q.dtype] * max(float(np.max(np.abs(r))), 0.05 * top)
+        _say(nm, f"err {err:.3e} bound {bound:.3e}")
+        assert err <= bound, f"{nm} err {err:.3e} > {bound:.3e}"
+
+
 def test_backward_deterministic():
     q, k, v = make_qkv(1, 8, 2, 300, 500, 128, "bf16", seed=32)
     do = make_dout(q.shape, torch.bfloat16, 32)

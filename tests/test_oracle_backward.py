@@ -111,6 +111,35 @@ def test_backward_pins(pin):
     pin(_oracle)
 
 
+def _sampled_everywhere(q, k, v, do, scale, causal, pos, window):
+    """The sampled form evaluated at every row, reshaped to full gradient tensors."""
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    qs = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(Sq)]
+    ks = [(b, g, j) for b in range(B) for g in range(Hkv) for j in range(Skv)]
+    dq, dk, dv = oracle.attention_backward_sampled(q, k, v, do, scale, causal, pos, qs, ks, window)
+    return dq.reshape(q.shape), dk.reshape(k.shape), dv.reshape(v.shape)
+
+
+@pytest.mark.parametrize("pin", BWD_PINS, ids=lambda p: p.__name__)
+def test_backward_pins_sampled_form(pin):
+    pin(_sampled_everywhere)
+
+
+def test_backward_sampled_subset_matches_rows():
+    """Any subset of samples returns the same rows as the whole set (no cross-talk)."""
+    q, k, v = pins.tiny_case(2, 4, 2, 11, 13, 16, 90)
+    do = pins.rand(q.shape, 91)
+    full = _sampled_everywhere(q, k, v, do, 0.3, True, 2, 5)
+    qs, ks = [(1, 3, 10), (0, 0, 0), (1, 2, 4)], [(1, 1, 12), (0, 0, 3)]
+    dq, dk, dv = oracle.attention_backward_sampled(q, k, v, do, 0.3, True, 2, qs, ks, window=5)
+    for n, (b, h, i) in enumerate(qs):
+        assert np.max(np.abs(dq[n] - full[0][b, h, i])) < 1e-12
+    for n, (b, g, j) in enumerate(ks):
+        assert np.max(np.abs(dk[n] - full[1][b, g, j])) < 1e-12
+        assert np.max(np.abs(dv[n] - full[2][b, g, j])) < 1e-12
+
+
 def _planted(mistake):
     """A copy of the backward with one planted mistake (for the pins to catch)."""
     def bwd(q, k, v, do, scale, causal, pos, window):
