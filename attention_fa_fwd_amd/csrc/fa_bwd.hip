@@ -52,7 +52,7 @@ hipError_t launch_all(const BwdParams& p, int causal, hipStream_t s) {
     const int rows = p.B * p.Hq * p.Sq;
     constexpr int RPB = 256 / (D / 8);
     hipLaunchKernelGGL((fa::fa_bwd_dot_kernel<D, BF16>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
-                       0, s, p.o, p.dout, p.lse, p.stats, rows);
+                       0, s, p.o, p.dout, p.lse, p.stats, rows, (float)(1.0 / (double)p.scale));
     BwdParams pk = p, pq = p;
     pk.n_tiles = (p.Skv + 127) / 128;
     pq.n_tiles = (p.Sq + 127) / 128;

@@ -8,8 +8,10 @@
 //     dS = P * (dP - D),       dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Kernels, no atomics, deterministic:
-//  * fa_bwd_dot_kernel: per query row the pair {LSE * log2(e) (+inf for a row with no
-//    visible key), D = dO . O} in fp32 -- the row statistics both gradient kernels read.
+//  * fa_bwd_dot_kernel: per query row the pair {-LSE / scale (-inf for a row with no
+//    visible key), -D} with D = dO . O, in fp32 -- the row statistics both gradient kernels
+//    read.  DKDV starts its S and dP accumulators at these values, so the MFMAs produce
+//    S - LSE / scale and dP - D directly: P = exp2(c (S - LSE / scale)), dS = P (dP - D).
 //  * fa_bwd_kernel<DKDV>: a wave owns 32 keys of one K/V head (K and V rows in registers);
 //    the workgroup streams 32-row tiles of Q, dO and the row statistics of the query heads
 //    it covers through LDS and accumulates dK^T and dV^T in registers, so the grouped
@@ -46,7 +48,7 @@ struct BwdParams {
     const void* o;
     const void* dout;
     const float* lse;    // [B*Hq*Sq], natural log, -inf for rows with no visible key
-    float* stats;        // [B*Hq*Sq][2]: LSE * log2(e) (+inf for an empty row), D
+    float* stats;        // [B*Hq*Sq][2]: -LSE / scale (-inf for an empty row), -D
     void* dq;
     void* dk;
     void* dv;
@@ -93,11 +95,11 @@ __device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, unsig
                                              voff, 0, 0, 0);
 }
 
-// Row statistics: stats[row] = {LSE * log2(e) or +inf for an empty row, sum_d dO * O};
+// Row statistics: stats[row] = {-LSE / scale or -inf for an empty row, -sum_d dO * O};
 // D / 8 lanes per row, 16 bytes each, summed by a butterfly in a fixed order.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void fa_bwd_dot_kernel(const void* o, const void* dout, const float* lse,
-                                                         float* stats, int rows) {
+                                                         float* stats, int rows, float inv_scale) {
     constexpr int TPR = D / 8, RPB = 256 / TPR;
     const int row = blockIdx.x * RPB + threadIdx.x / TPR;
     const int t = threadIdx.x % TPR;
@@ -115,8 +117,8 @@ __global__ __launch_bounds__(256) void fa_bwd_dot_kernel(const void* o, const vo
     for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
     if (row < rows && t == 0) {
         const float l = lse[row];
-        const float l2 = l == -__builtin_inff() ? __builtin_inff() : l * 1.44269504088896340736f;
-        *(f32x2*)(stats + 2 * (size_t)row) = (f32x2){l2, acc};
+        const float nls = l == -__builtin_inff() ? -__builtin_inff() : -l * inv_scale;
+        *(f32x2*)(stats + 2 * (size_t)row) = (f32x2){nls, -acc};
     }
 }
 
@@ -216,12 +218,13 @@ void fa_bwd_kernel(BwdParams p) {
         x1[dk] = ((const u32x4*)x1p)[dk * 2 + h];
         x2[dk] = ((const u32x4*)x2p)[dk * 2 + h];
     }
-    // DQ: the lane's own query row statistics.
+    // DQ: the lane's own query row statistics, as LSE * log2(e) (+inf for an empty row,
+    // so that p = 0) and D.
     float lse2_own = 0.0f, d_own = 0.0f;
     if constexpr (!DKDV) {
         const f32x2 st = *(const f32x2*)(p.stats + 2 * ((size_t)(b * p.Hq + head) * p.Sq + own_row));
-        lse2_own = st[0];
-        d_own = st[1];
+        lse2_own = -st[0] * p.c;
+        d_own = -st[1];
     }
 
     // Streamed steps.  DQ: key tiles [tb, tb + n_steps) of K/V head head / group; tiles
@@ -345,10 +348,11 @@ void fa_bwd_kernel(BwdParams p) {
             }
         }
     };
-    // DKDV, wave 0: the 32 rows' statistics (256 bytes, 4 per lane) of the tile fetched last.
+    // DKDV, wave 0: the 32 rows' statistics (256 bytes, 4 per lane) of the tile fetched last,
+    // rearranged by the per-lane source offsets into two planes: 32 x -LSE / scale, 32 x -D.
     auto fetch_stats = [&](unsigned char* ds) FA_INLINE {
         const __amdgpu_buffer_rsrc_t r = make_rsrc_uniform(p.stats + 2 * st_row, st_rows * 8);
-        buffer_load_lds4(r, ds, lane * 4);
+        buffer_load_lds4(r, ds, lane < 32 ? lane * 8 : (lane - 32) * 8 + 4);
     };
 
     // Row-read offsets (A operand rows l32, chunk 2dk + h) and transposed-read offsets.
@@ -370,6 +374,28 @@ void fa_bwd_kernel(BwdParams p) {
     }
     auto rows_mfma = [&](const unsigned char* tb_, const u32x4 (&x)[DK]) FA_INLINE {
         f32x16 acc = {};
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) {
+            const u32x4 a = *(const u32x4*)(tb_ + off_r[dk]);
+            acc = mfma32<BF16>(a, x[dk], acc);
+        }
+        return acc;
+    };
+    // DKDV: accumulator start values from a statistics tile (planar: 32 x -LSE/scale, then
+    // 32 x -D): element i of a lane is row 8(i/4) + 4h + i%4, four consecutive rows a read.
+    auto stat_init = [&](const unsigned char* st, int plane) FA_INLINE {
+        f32x16 v;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 u = *(const f32x4*)(st + plane + (8 * g4 + 4 * h) * 4);
+            v[4 * g4 + 0] = u[0];
+            v[4 * g4 + 1] = u[1];
+            v[4 * g4 + 2] = u[2];
+            v[4 * g4 + 3] = u[3];
+        }
+        return v;
+    };
+    auto rows_mfma_init = [&](const unsigned char* tb_, const u32x4 (&x)[DK], f32x16 acc) FA_INLINE {
 #pragma unroll
         for (int dk = 0; dk < DK; ++dk) {
             const u32x4 a = *(const u32x4*)(tb_ + off_r[dk]);
@@ -436,39 +462,30 @@ void fa_bwd_kernel(BwdParams p) {
 
         fetch_tiles(t1_of(PF{}), t2_of(PF{}));
         // Next tile's products (DQ: S^T and dP^T, lane = query; DKDV: S and dP, lane = key).
-        scn = rows_mfma(t1_of(PN{}), x1);
-        dpn = rows_mfma(t2_of(PN{}), x2);
+        if constexpr (DKDV) {
+            scn = rows_mfma_init(t1_of(PN{}), x1, stat_init(st_of(PN{}), 0));
+            dpn = rows_mfma_init(t2_of(PN{}), x2, stat_init(st_of(PN{}), 128));
+        } else {
+            scn = rows_mfma(t1_of(PN{}), x1);
+            dpn = rows_mfma(t2_of(PN{}), x2);
+        }
 
         // This tile: P and dS.  Element i of a lane is streamed row c_row0 + 4h + ci(i).
-        float l2v[16], ddv[16];
+        float pe[16], de[16];
         if constexpr (DKDV) {
-            const unsigned char* st = st_of(PC{});
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x4 u0 = *(const f32x4*)(st + (8 * g4 + 4 * h) * 8);
-                const f32x4 u1 = *(const f32x4*)(st + (8 * g4 + 4 * h) * 8 + 16);
-                l2v[4 * g4 + 0] = u0[0];
-                ddv[4 * g4 + 0] = u0[1];
-                l2v[4 * g4 + 1] = u0[2];
-                ddv[4 * g4 + 1] = u0[3];
-                l2v[4 * g4 + 2] = u1[0];
-                ddv[4 * g4 + 2] = u1[1];
-                l2v[4 * g4 + 3] = u1[2];
-                ddv[4 * g4 + 3] = u1[3];
+            for (int i = 0; i < 16; ++i) {
+                const float pv = __builtin_amdgcn_exp2f(sc[i] * p.c);
+                pe[i] = pv;
+                de[i] = pv * dp[i];
             }
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                l2v[i] = lse2_own;
-                ddv[i] = d_own;
+                const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], p.c, -lse2_own));
+                pe[i] = pv;
+                de[i] = pv * (dp[i] - d_own);
             }
-        }
-        float pe[16], de[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], p.c, -l2v[i]));
-            pe[i] = pv;
-            de[i] = pv * (dp[i] - ddv[i]);
         }
         // Mask (edge tiles only): the lane's element i is streamed row c_row0 + 4h + ci(i),
         // ci(i) = 8(i/4) + i%4 < 32.  Visible elements form one range of ci, [lo, hi); bit
@@ -561,8 +578,13 @@ void fa_bwd_kernel(BwdParams p) {
             if (DKDV && w == 0) fetch_stats(st_of(ph));
         });
         wait_tiles();
-        sc0 = rows_mfma(t1_0, x1);
-        dp0 = rows_mfma(t2_0, x2);
+        if constexpr (DKDV) {
+            sc0 = rows_mfma_init(t1_0, x1, stat_init(st_0, 0));
+            dp0 = rows_mfma_init(t2_0, x2, stat_init(st_0, 128));
+        } else {
+            sc0 = rows_mfma(t1_0, x1);
+            dp0 = rows_mfma(t2_0, x2);
+        }
 
         // Unrolled by NB so the buffer phase of each copy of the step is fixed.
         int i = 0;

@@ -208,7 +208,7 @@ size_t fa_splitkv_workspace_size(int B, int Hq, int Sq, int D, int num_splits);
  *   scale .. window     as for fa_fwd_splitkv (window needs causal).
  *   workspace           >= fa_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, D, causal) bytes of
  *                       device memory, 16-byte aligned, owned by the caller (it receives
- *                       the row statistics LSE * log2(e) and D = rowsum(dout * out), and
+ *                       the row statistics -LSE / scale and -D, D = rowsum(dout * out), and
  *                       fp32 partial dk / dv sums when the head group is split).
  *   stream              the kernels (row statistics, dk/dv, the partial sum if any, dq)
  *                       are enqueued on it in order.
