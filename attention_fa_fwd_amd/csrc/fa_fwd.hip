@@ -455,7 +455,7 @@ const char* fa_strerror(int code) {
         case FA_ERR_INVALID_CONFIG: return "kernel configuration id out of range or not applicable to this call";
         case FA_ERR_LAUNCH: return "kernel launch failed";
         case FA_ERR_INVALID_SPLITS: return "num_splits must be in 0..256";
-        case FA_ERR_WORKSPACE: return "split-KV workspace smaller than fa_splitkv_workspace_size()";
+        case FA_ERR_WORKSPACE: return "workspace smaller than fa_splitkv_workspace_size() / fa_bwd_workspace_size()";
         case FA_ERR_INVALID_WINDOW: return "window must be >= 0, needs causal masking, and >= 1 for fa_fwd_window";
         default: return "unknown status code";
     }

@@ -26,10 +26,11 @@
  * from several host threads at once.
  *
  * Asynchrony: the call validates its arguments on the host (no HIP call), enqueues its
- * kernel (fa_fwd_splitkv: two kernels; fa_bwd: three) on `stream` (a hipStream_t passed as void*; NULL =
- * the null stream) and returns without synchronising.  Faults inside the kernel surface on the next synchronisation.
+ * kernels (fa_fwd: one; fa_fwd_splitkv: two; fa_bwd: three, or four when the GQA group is
+ * split) on `stream` (a hipStream_t passed as void*; NULL = the null stream) and returns
+ * without synchronising.  Faults inside a kernel surface on the next synchronisation.
  *
- * Errors: a nonzero return leaves out and lse untouched and launches nothing, except
+ * Errors: a nonzero return leaves every output untouched and launches nothing, except
  * FA_ERR_LAUNCH, which reports a failed launch.  Checks run in the order of the codes below,
  * except that the window check (FA_ERR_INVALID_WINDOW) follows the input_pos check.
  */
@@ -63,7 +64,7 @@ enum fa_status {
     FA_ERR_INVALID_CONFIG = -10,      /* fa_fwd_config: config id unknown or not applicable  */
     FA_ERR_LAUNCH = -11,              /* the kernel launch failed (hipGetLastError)           */
     FA_ERR_INVALID_SPLITS = -12,      /* fa_fwd_splitkv: num_splits outside 0..256            */
-    FA_ERR_WORKSPACE = -13,           /* fa_fwd_splitkv: workspace_bytes too small            */
+    FA_ERR_WORKSPACE = -13,           /* fa_fwd_splitkv, fa_bwd: workspace_bytes too small    */
     FA_ERR_INVALID_WINDOW = -14       /* window < 0, window > 0 without causal masking, or    */
                                       /* fa_fwd_window with window < 1                        */
 };
