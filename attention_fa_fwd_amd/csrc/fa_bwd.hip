@@ -49,9 +49,10 @@ size_t part_bytes(int gsplit, int B, int Hkv, int Skv, int D) {
 
 template <int D, bool BF16>
 hipError_t launch_all(const BwdParams& p, int causal, hipStream_t s) {
-    const int rows = p.B * p.Hq * p.Sq;
+    const size_t rows = (size_t)p.B * p.Hq * p.Sq;
     constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL((fa::fa_bwd_dot_kernel<D, BF16>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
+    const dim3 gd((unsigned)std::min<size_t>((rows + RPB - 1) / RPB, (size_t)1 << 20));
+    hipLaunchKernelGGL((fa::fa_bwd_dot_kernel<D, BF16>), gd, dim3(256),
                        0, s, p.o, p.dout, p.lse, p.stats, rows, (float)(1.0 / (double)p.scale));
     BwdParams pk = p, pq = p;
     pk.n_tiles = (p.Skv + 127) / 128;

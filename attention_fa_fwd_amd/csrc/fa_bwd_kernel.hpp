@@ -99,26 +99,28 @@ __device__ __forceinline__ void buffer_load_lds4(__amdgpu_buffer_rsrc_t r, unsig
 // D / 8 lanes per row, 16 bytes each, summed by a butterfly in a fixed order.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void fa_bwd_dot_kernel(const void* o, const void* dout, const float* lse,
-                                                         float* stats, int rows, float inv_scale) {
+                                                         float* stats, size_t rows, float inv_scale) {
     constexpr int TPR = D / 8, RPB = 256 / TPR;
-    const int row = blockIdx.x * RPB + threadIdx.x / TPR;
     const int t = threadIdx.x % TPR;
-    float acc = 0.0f;
-    if (row < rows) {
-        const u32x4 a = ((const u32x4*)((const uint16_t*)o + (size_t)row * D))[t];
-        const u32x4 g = ((const u32x4*)((const uint16_t*)dout + (size_t)row * D))[t];
+    for (size_t row0 = (size_t)blockIdx.x * RPB; row0 < rows; row0 += (size_t)gridDim.x * RPB) {
+        const size_t row = row0 + threadIdx.x / TPR;
+        float acc = 0.0f;
+        if (row < rows) {
+            const u32x4 a = ((const u32x4*)((const uint16_t*)o + row * D))[t];
+            const u32x4 g = ((const u32x4*)((const uint16_t*)dout + row * D))[t];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc = __builtin_fmaf(half_to_f32<BF16>(a[e] & 0xffffu), half_to_f32<BF16>(g[e] & 0xffffu), acc);
-            acc = __builtin_fmaf(half_to_f32<BF16>(a[e] >> 16), half_to_f32<BF16>(g[e] >> 16), acc);
+            for (int e = 0; e < 4; ++e) {
+                acc = __builtin_fmaf(half_to_f32<BF16>(a[e] & 0xffffu), half_to_f32<BF16>(g[e] & 0xffffu), acc);
+                acc = __builtin_fmaf(half_to_f32<BF16>(a[e] >> 16), half_to_f32<BF16>(g[e] >> 16), acc);
+            }
         }
-    }
 #pragma unroll
-    for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-    if (row < rows && t == 0) {
-        const float l = lse[row];
-        const float nls = l == -__builtin_inff() ? -__builtin_inff() : -l * inv_scale;
-        *(f32x2*)(stats + 2 * (size_t)row) = (f32x2){nls, -acc};
+        for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+        if (row < rows && t == 0) {
+            const float l = lse[row];
+            const float nls = l == -__builtin_inff() ? -__builtin_inff() : -l * inv_scale;
+            *(f32x2*)(stats + 2 * row) = (f32x2){nls, -acc};
+        }
     }
 }
 

@@ -55,8 +55,8 @@ constexpr long long kNumCUs = 256;
 constexpr long long kFullGrid = 512;
 
 hipError_t launch_merge(const Params& p, int D, int bf16, hipStream_t s) {
-    const int rows = p.B * p.Hq * p.Sq;
-    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    const size_t rows = (size_t)p.B * p.Hq * p.Sq;
+    const dim3 grid((unsigned)std::min<size_t>((rows + 3) / 4, (size_t)1 << 20)), block(256);
     if (D == 128) {
         if (bf16) hipLaunchKernelGGL((fa::fa_merge_kernel<128, true>), grid, block, 0, s, p.o_part, p.lse_part, p.o, p.lse, rows, p.num_splits);
         else hipLaunchKernelGGL((fa::fa_merge_kernel<128, false>), grid, block, 0, s, p.o_part, p.lse_part, p.o, p.lse, rows, p.num_splits);

@@ -45,16 +45,14 @@ __device__ __forceinline__ uint32_t merge_pack2(float a, float b) {
     }
 }
 
-// o_part [S][rows][D] and lse_part [S][rows] fp32; o [rows][D] in the storage type, lse
-// [rows] fp32.  Launch: ceil(rows / 4) blocks of 256 threads; num_splits <= 256.
+// One output row: the row's partial LSE values and weights across the wave, then its
+// D outputs, D / 64 per lane.
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void fa_merge_kernel(const float* o_part, const float* lse_part,
-                                                       void* o, float* lse, int rows, int num_splits) {
+__device__ __forceinline__ void fa_merge_row(const float* o_part, const float* lse_part, void* o, float* lse,
+                                             size_t rows, int num_splits, size_t row) {
     constexpr int PER = D / 64;                  // output elements per lane
     constexpr int SPL = kMergeMaxSplits / 64;    // ranges held per lane
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    if (row >= rows) return;
     constexpr float LOG2E = 1.44269504088896340736f;
 
     float ls[SPL];
@@ -112,6 +110,16 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* o_part, cons
         orow[0] = (uint16_t)(merge_pack2<BF16>(acc[0] * inv, 0.0f) & 0xffffu);
     }
     if (lane == 0) lse[row] = total > 0.0f ? mx + __builtin_logf(total) : -__builtin_inff();
+}
+
+// o_part [S][rows][D] and lse_part [S][rows] fp32; o [rows][D] in the storage type, lse
+// [rows] fp32.  Blocks of 256 threads, one wave per row, striding over the rows by the grid;
+// num_splits <= 256.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void fa_merge_kernel(const float* o_part, const float* lse_part,
+                                                       void* o, float* lse, size_t rows, int num_splits) {
+    for (size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += (size_t)gridDim.x * 4)
+        fa_merge_row<D, BF16>(o_part, lse_part, o, lse, rows, num_splits, row);
 }
 
 }  // namespace fa
