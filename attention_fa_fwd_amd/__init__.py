@@ -14,7 +14,9 @@ import math
 import os
 import threading
 
-__all__ = ["fa_fwd", "fa_fwd_into", "fa_bwd", "fa_bwd_into", "bwd_workspace_size", "fa_fwd_fp8", "fa_fwd_fp8_into", "select_config_fp8", "fa_fwd_splitkv", "fa_fwd_splitkv_into", "splitkv_num_splits",
+__all__ = ["fa_fwd", "fa_fwd_into", "fa_bwd", "fa_bwd_into", "bwd_workspace_size", "fa_fwd_fp8",
+           "fa_fwd_fp8_into", "select_config_fp8", "fa_fwd_splitkv_fp8", "fa_fwd_splitkv_fp8_into",
+           "splitkv_num_splits_fp8", "fa_fwd_splitkv", "fa_fwd_splitkv_into", "splitkv_num_splits",
            "splitkv_workspace_size", "select_config", "config_names", "num_configs", "FaError",
            "load_library", "LIB_PATH"]
 
@@ -59,6 +61,11 @@ def _declare(lib):
     lib.fa_fwd_splitkv.argtypes = _FWD_ARGS[:14] + [_c_int, _c_int, _c_int, _c_int, _vp,
                                                     ctypes.c_size_t, _vp]
     lib.fa_fwd_splitkv.restype = _c_int
+    lib.fa_fwd_splitkv_fp8.argtypes = _FWD_ARGS[:12] + [_c_float, _c_float] + [_c_int] * 6 + [
+        _vp, ctypes.c_size_t, _vp]
+    lib.fa_fwd_splitkv_fp8.restype = _c_int
+    lib.fa_splitkv_num_splits_fp8.argtypes = [_c_int] * 11
+    lib.fa_splitkv_num_splits_fp8.restype = _c_int
     lib.fa_splitkv_num_splits.argtypes = [_c_int] * 11
     lib.fa_splitkv_num_splits.restype = _c_int
     lib.fa_splitkv_workspace_size.argtypes = [_c_int] * 5
@@ -272,13 +279,10 @@ def config_names():
     return [lib.fa_config_name(i).decode() for i in range(lib.fa_num_configs())]
 
 
-def fa_fwd_fp8_into(q8, k8, v, out, lse, q_descale, k_descale, scale=None, causal=True,
-                    input_pos=0, window=0, config=-1, stream=None):
-    """fp8 E4M3 q8 [B,Hq,Sq,D], k8 [B,Hkv,Skv,D] (torch.float8_e4m3fn) with per-tensor
-    descale factors; v [B,Hkv,Skv,D] and out in fp16 / bf16; lse fp32 (fa_fwd_fp8)."""
+def _check_fp8_tensors(q8, k8, v, out, lse):
+    """Device, contiguity, dtype and shape checks of the fp8 entry points; returns the sizes."""
     import torch
 
-    lib = load_library()
     for name, t in (("q8", q8), ("k8", k8), ("v", v), ("out", out), ("lse", lse)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
@@ -298,6 +302,17 @@ def fa_fwd_fp8_into(q8, k8, v, out, lse, q_descale, k_descale, scale=None, causa
         raise ValueError(f"shape mismatch q{tuple(q8.shape)} k{tuple(k8.shape)} v{tuple(v.shape)}")
     if tuple(out.shape) != tuple(q8.shape) or tuple(lse.shape) != (B, Hq, Sq):
         raise ValueError("out must be [B, Hq, Sq, D] and lse [B, Hq, Sq]")
+    return B, Hq, Hkv, Sq, Skv, D
+
+
+def fa_fwd_fp8_into(q8, k8, v, out, lse, q_descale, k_descale, scale=None, causal=True,
+                    input_pos=0, window=0, config=-1, stream=None):
+    """fp8 E4M3 q8 [B,Hq,Sq,D], k8 [B,Hkv,Skv,D] (torch.float8_e4m3fn) with per-tensor
+    descale factors; v [B,Hkv,Skv,D] and out in fp16 / bf16; lse fp32 (fa_fwd_fp8)."""
+    import torch
+
+    lib = load_library()
+    B, Hq, Hkv, Sq, Skv, D = _check_fp8_tensors(q8, k8, v, out, lse)
     _check_window(causal, window)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -324,6 +339,68 @@ def fa_fwd_fp8(q8, k8, v, q_descale, k_descale, scale=None, causal=True, input_p
     lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=q8.device)
     return fa_fwd_fp8_into(q8, k8, v, out, lse, q_descale, k_descale, scale=scale, causal=causal,
                            input_pos=input_pos, window=window, config=config)
+
+
+def splitkv_num_splits_fp8(B, Hq, Hkv, Sq, Skv, D, causal, input_pos, v_dtype, config=-1,
+                           window=0) -> int:
+    """Split count fa_fwd_splitkv_fp8 picks for num_splits=0 (v_dtype: torch dtype or code)."""
+    code = v_dtype if isinstance(v_dtype, int) else _dtype_code(v_dtype)
+    rc = load_library().fa_splitkv_num_splits_fp8(B, Hq, Hkv, Sq, Skv, D, 1 if causal else 0,
+                                                  int(input_pos), int(window), code, int(config))
+    _check(rc if rc < 0 else 0)
+    return rc
+
+
+def fa_fwd_splitkv_fp8_into(q8, k8, v, out, lse, workspace, q_descale, k_descale, num_splits=0,
+                            scale=None, causal=True, input_pos=0, window=0, config=-1,
+                            stream=None):
+    """Split-KV forward with fp8 E4M3 q8, k8 and fp16 / bf16 v into caller-provided
+    ``out``, ``lse`` and ``workspace`` (``splitkv_workspace_size`` bytes; None when one
+    split runs)."""
+    import torch
+
+    lib = load_library()
+    B, Hq, Hkv, Sq, Skv, D = _check_fp8_tensors(q8, k8, v, out, lse)
+    _check_window(causal, window)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q8.device).cuda_stream
+    if workspace is not None:
+        if not workspace.is_cuda or workspace.device != q8.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on q8's device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    else:
+        ws_ptr, ws_bytes = None, 0
+    with torch.cuda.device(q8.device):
+        rc = lib.fa_fwd_splitkv_fp8(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    lse.data_ptr(), B, Hq, Hkv, Sq, Skv, D, float(scale),
+                                    float(q_descale), float(k_descale), 1 if causal else 0,
+                                    int(input_pos), int(window), _dtype_code(v.dtype),
+                                    int(num_splits), int(config), ws_ptr, ws_bytes, stream)
+    _check(rc)
+    return out, lse
+
+
+def fa_fwd_splitkv_fp8(q8, k8, v, q_descale, k_descale, scale=None, causal=True, input_pos=0,
+                       num_splits=0, window=0, config=-1):
+    """Split-KV attention with fp8 E4M3 queries and keys; allocates out, lse and the
+    workspace with torch."""
+    import torch
+
+    q8, k8, v = q8.contiguous(), k8.contiguous(), v.contiguous()
+    B, Hq, Sq, D = q8.shape
+    Hkv, Skv = k8.shape[1], k8.shape[2]
+    if num_splits == 0:
+        num_splits = splitkv_num_splits_fp8(B, Hq, Hkv, Sq, Skv, D, causal, input_pos, v.dtype,
+                                            config, window)
+    out = torch.empty(q8.shape, dtype=v.dtype, device=q8.device)
+    lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=q8.device)
+    nbytes = splitkv_workspace_size(B, Hq, Sq, D, num_splits)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q8.device) if nbytes else None
+    return fa_fwd_splitkv_fp8_into(q8, k8, v, out, lse, ws, q_descale, k_descale,
+                                   num_splits=num_splits, scale=scale, causal=causal,
+                                   input_pos=input_pos, window=window, config=config)
 
 
 def select_config_fp8(B, Hq, Hkv, Sq, D, causal, v_dtype) -> int:

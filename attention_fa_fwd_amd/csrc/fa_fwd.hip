@@ -221,7 +221,8 @@ int auto_splits(const ConfigEntry& c, const Call& a) {
     const int tiles = max_key_tiles(c, a.Sq, a.Skv, a.causal, a.causal ? a.input_pos : 0,
                                     a.causal ? a.window : 0);
     const long long by_len = tiles / 8;
-    const double kv_bytes = 4.0 * a.B * a.Hkv * std::min<double>(a.Skv, (double)tiles * c.BN) * c.D;
+    const double kv_elem_bytes = a.qk8 ? 3.0 : 4.0;   // K (1 or 2 bytes) + V (2 bytes)
+    const double kv_bytes = kv_elem_bytes * a.B * a.Hkv * std::min<double>(a.Skv, (double)tiles * c.BN) * c.D;
     const double part_bytes = 8.0 * a.B * a.Hq * (double)a.Sq * (c.D + 1);   // per range
     const long long by_traffic = (long long)(kv_bytes / part_bytes);
     return (int)std::max(1LL, std::min({want, by_len, by_traffic, (long long)kMaxSplits}));
@@ -393,6 +394,33 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float
                        num_splits, config, workspace, workspace_bytes, stream);
 }
 
+int fa_fwd_splitkv_fp8(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                       int Hq, int Hkv, int Sq, int Skv, int D, float scale, float q_descale,
+                       float k_descale, int causal, int input_pos, int window, int v_dtype,
+                       int num_splits, int config, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    Call a = make_call(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos,
+                       window, v_dtype);
+    a.qk8 = 1;
+    a.q_descale = q_descale;
+    a.k_descale = k_descale;
+    return run_splitkv(a, num_splits, config, workspace, workspace_bytes, stream);
+}
+int fa_splitkv_num_splits_fp8(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                              int input_pos, int window, int v_dtype, int config) {
+    if (B < 0 || Hq < 0 || Sq < 0 || Hkv < 1 || Skv < 1) return FA_ERR_INVALID_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_HEAD_GROUP;
+    if (D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (v_dtype != FA_DTYPE_FP16 && v_dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
+    if (input_pos < 0 || (long long)input_pos + Sq > INT_MAX) return FA_ERR_INVALID_INPUT_POS;
+    if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_WINDOW;
+    Call a = make_call(nullptr, nullptr, nullptr, nullptr, nullptr, B, Hq, Hkv, Sq, Skv, D, 1.0f,
+                       causal, input_pos, window, v_dtype);
+    a.qk8 = 1;
+    config = resolve_config(config, a);
+    if (config < 0) return config;
+    return auto_splits(kConfigs[config], a);
+}
 int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
                           int input_pos, int window, int dtype, int config) {
     if (B < 0 || Hq < 0 || Sq < 0 || Hkv < 1 || Skv < 1) return FA_ERR_INVALID_SHAPE;

@@ -49,6 +49,9 @@ FP8_WORKLOADS = {
                                               dtype="bf16", causal=True, input_pos=0),
     "mha_causal_s4096_d128_fp8qk_fp16": dict(B=1, Hq=32, Hkv=32, Sq=4096, Skv=4096, D=128,
                                              dtype="fp16", causal=True, input_pos=0),
+    # Decoding against an fp8 key cache (the bf16 decode workload's shape).
+    "gqa4_decode_b4_kv16384_d128_fp8qk_bf16": dict(B=4, Hq=32, Hkv=8, Sq=1, Skv=16384, D=128,
+                                                   dtype="bf16", causal=True, input_pos=16383),
 }
 
 

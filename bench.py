@@ -15,9 +15,9 @@ its working clock (the first ~30 launches of the headline kernel run up to 30% s
 so a fixed small W would time the clock ramp rather than the kernel.  The extra steps are
 reported as "warmup_extra_steps".
 
---splitkv times fa_fwd_splitkv (the library's split count, workspace allocated before the
-timed region) instead; decoding workloads (one query row) are reported in GB/s against
-the HBM roofline, since reading K and V bounds them.
+--splitkv times fa_fwd_splitkv (fa_fwd_splitkv_fp8 for an fp8 workload; the library's split
+count, workspace allocated before the timed region) instead; decoding workloads (one query
+row) are reported in GB/s against the HBM roofline, since reading K and V bounds them.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--splitkv]
                        [--backward] [--all]
@@ -112,11 +112,12 @@ def traffic_bytes(workload):
     return e.get("hbm_bytes_per_launch")
 
 
-def algorithmic_bytes(w):
-    """q, k, v read once; out and lse written once."""
-    qo = 2 * w["B"] * w["Hq"] * w["Sq"] * w["D"] * 2
-    kv = 2 * w["B"] * w["Hkv"] * w["Skv"] * w["D"] * 2
-    return qo + kv + w["B"] * w["Hq"] * w["Sq"] * 4
+def algorithmic_bytes(w, fp8=False):
+    """q, k, v read once; out and lse written once (q and k one byte per element with fp8)."""
+    qk = 1 if fp8 else 2
+    q_o = w["B"] * w["Hq"] * w["Sq"] * w["D"] * (qk + 2)
+    k_v = w["B"] * w["Hkv"] * w["Skv"] * w["D"] * (qk + 2)
+    return q_o + k_v + w["B"] * w["Hq"] * w["Sq"] * 4
 
 
 def workload(name):
@@ -162,6 +163,18 @@ def time_gpu(name, steps, warmup, config=-1, splitkv=False, backward=False):
             fa.fa_bwd_into(q, k, v, out, lse, dout, dq, dk, dv, ws, scale=kw["scale"],
                            causal=kw["causal"], input_pos=kw["input_pos"], window=kw["window"],
                            stream=sp)
+    elif fp8 and splitkv:
+        splits = fa.splitkv_num_splits_fp8(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"],
+                                           w["causal"], w["input_pos"], v.dtype, config,
+                                           kw["window"])
+        nbytes = fa.splitkv_workspace_size(w["B"], w["Hq"], w["Sq"], w["D"], splits)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+
+        def step():
+            fa.fa_fwd_splitkv_fp8_into(q, k, v, out, lse, ws, kw["q_descale"], kw["k_descale"],
+                                       num_splits=splits, scale=kw["scale"], causal=kw["causal"],
+                                       input_pos=kw["input_pos"], window=kw["window"],
+                                       config=config, stream=sp)
     elif fp8:
         def step():
             fa.fa_fwd_fp8_into(q, k, v, out, lse, kw["q_descale"], kw["k_descale"],
@@ -264,7 +277,9 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False, bac
     mean_kernel_ms = sum(r["per_ms"]) / len(r["per_ms"])
     med = r["per_ms"][len(r["per_ms"]) // 2]
     p95 = r["per_ms"][min(len(r["per_ms"]) - 1, int(math.ceil(0.95 * len(r["per_ms"]))) - 1)]
-    path = ("fa_bwd" if backward else "fa_fwd_fp8" if fp8 else
+    path = ("fa_bwd" if backward else
+            f"fa_fwd_splitkv_fp8 ({r['splits']} splits)" if fp8 and splitkv else
+            "fa_fwd_fp8" if fp8 else
             f"fa_fwd_splitkv ({r['splits']} splits)" if splitkv else "fa_fwd")
     log(f"{path} kernel {r['kernel']}: mean {mean_kernel_ms * 1e3:.1f} us, median {med * 1e3:.1f} us, "
         f"p95 {p95 * 1e3:.1f} us, min {r['per_ms'][0] * 1e3:.1f} us, "
@@ -272,7 +287,7 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False, bac
     decode = w["Sq"] <= 16 and not backward
     if decode:
         # Reading K and V bounds a decoding step: GB/s of algorithmic bytes per call.
-        gbs = algorithmic_bytes(w) / (mean_kernel_ms * 1e-3) / 1e9
+        gbs = algorithmic_bytes(w, fp8) / (mean_kernel_ms * 1e-3) / 1e9
         metric, value, unit = "attention decode GB/s of algorithmic HBM bytes", gbs, "GB/s"
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
@@ -366,7 +381,8 @@ def main(argv=None):
         from attention_fa_fwd_amd.inputs import FP8_WORKLOADS, WORKLOADS
 
         for name in list(WORKLOADS) + list(FP8_WORKLOADS):
-            runs = [False, True] if name in WORKLOADS and WORKLOADS[name]["Sq"] <= 16 else [False]
+            shape = WORKLOADS.get(name) or FP8_WORKLOADS[name]
+            runs = [False, True] if shape["Sq"] <= 16 else [False]
             for split in runs:
                 if name == a.workload and split == a.splitkv:
                     continue

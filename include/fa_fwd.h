@@ -26,7 +26,7 @@
  * from several host threads at once.
  *
  * Asynchrony: the call validates its arguments on the host (no HIP call), enqueues its
- * kernels (fa_fwd: one; fa_fwd_splitkv: two; fa_bwd: three, or four when the GQA group is
+ * kernels (fa_fwd: one; fa_fwd_splitkv(_fp8): two; fa_bwd: three, or four when the GQA group is
  * split) on `stream` (a hipStream_t passed as void*; NULL = the null stream) and returns
  * without synchronising.  Faults inside a kernel surface on the next synchronisation.
  *
@@ -186,6 +186,25 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float
  * and there are at most 256 ranges.  Negative fa_status on invalid sizes. */
 int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
                           int input_pos, int window, int dtype, int config);
+
+/*
+ * Split-KV forward pass with fp8 E4M3 queries and keys, the two entry points above
+ * combined: q, k, v, scale, q_descale, k_descale, window and v_dtype as for fa_fwd_fp8;
+ * num_splits, config, workspace and workspace_bytes as for fa_fwd_splitkv (the workspace
+ * size does not depend on the input types: fa_splitkv_workspace_size).  Decoding against
+ * an fp8 key cache reads 3 bytes per K/V element instead of 4.  Checks: those of
+ * fa_fwd_fp8, then those of fa_fwd_splitkv's split and workspace arguments.
+ */
+int fa_fwd_splitkv_fp8(const void* q, const void* k, const void* v, void* out, float* lse,
+                       int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+                       float q_descale, float k_descale, int causal, int input_pos, int window,
+                       int v_dtype, int num_splits, int config, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Split count fa_fwd_splitkv_fp8 uses for num_splits = 0 (the rule of
+ * fa_splitkv_num_splits, with 3 bytes per K/V element), or a negative fa_status. */
+int fa_splitkv_num_splits_fp8(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                              int input_pos, int window, int v_dtype, int config);
 
 /* Workspace bytes fa_fwd_splitkv needs for num_splits ranges:
  * num_splits * B * Hq * Sq * (D + 1) * 4 (fp32 partial O, then fp32 partial LSE), 0 when

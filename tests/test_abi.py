@@ -263,6 +263,46 @@ def test_fp8_validation(lib):
     assert call_fp8(lib, out=Q + qbytes - 16) == -9
 
 
+def call_split_fp8(lib, num_splits=2, ws=W, ws_bytes=1 << 28, qd=0.01, kd=0.02, window=0,
+                   config=-1, **over):
+    a = dict(GOOD, **dict(dict(D=128), **over))
+    return lib.fa_fwd_splitkv_fp8(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"],
+                                  a["Hkv"], a["Sq"], a["Skv"], a["D"], a["scale"], qd, kd,
+                                  a["causal"], a["input_pos"], window, a["dtype"], num_splits,
+                                  config, ws, ws_bytes, None)
+
+
+def test_fp8_splitkv_validation(lib):
+    """fa_fwd_splitkv_fp8 runs fa_fwd_fp8's checks, then the split and workspace checks
+    (no call here reaches a launch)."""
+    assert call_split_fp8(lib, D=64) == -4
+    assert call_split_fp8(lib, qd=float("nan")) == -6
+    assert call_split_fp8(lib, kd=0.0) == -6
+    assert call_split_fp8(lib, window=5, causal=0) == -14
+    assert call_split_fp8(lib, num_splits=-1) == -12
+    assert call_split_fp8(lib, num_splits=257) == -12
+    assert call_split_fp8(lib, ws=None) == -1
+    assert call_split_fp8(lib, ws=W + 8) == -8
+    need = fa.splitkv_workspace_size(1, 4, 8, 128, 2)
+    assert call_split_fp8(lib, ws_bytes=need - 1) == -13
+    assert call_split_fp8(lib, ws=Q) == -9                # workspace overlapping q
+    assert call_split_fp8(lib, Sq=0, q=0, out=0, lse=0) == 0
+    names = fa.config_names()
+    bf16 = names.index("D128_BN32_Mw1x32_WPH1_HPW4_causal_bf16")
+    assert call_split_fp8(lib, config=bf16, dtype=1) == -10
+
+
+def test_fp8_splitkv_num_splits(lib):
+    """The split rule of fa_splitkv_num_splits with 3 bytes per K/V element: the decoding
+    shape (32 workgroups) gets 16 ranges; a full grid gets 1."""
+    f = lib.fa_splitkv_num_splits_fp8
+    assert f(4, 32, 8, 1, 16384, 128, 1, 16383, 0, 1, -1) == 16
+    assert f(1, 32, 4, 8192, 8192, 128, 1, 0, 0, 1, -1) == 1
+    assert f(4, 32, 8, 1, 16384, 64, 1, 16383, 0, 1, -1) == -4
+    assert f(4, 32, 8, 1, 16384, 128, 1, 16383, 0, 3, -1) == -5
+    assert fa.splitkv_num_splits_fp8(4, 32, 8, 1, 16384, 128, True, 16383, 1) == 16
+
+
 def test_fp8_configs(lib):
     names = fa.config_names()
     fp8 = [i for i, nm in enumerate(names) if "_fp8qk_" in nm]

@@ -119,7 +119,7 @@ def test_fp8_named_workload(name):
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
     rng = np.random.default_rng(3)
     B, Hq, Sq = w["B"], w["Hq"], w["Sq"]
-    rows = [0, 1, 31, 32, 63, 64, 127, 128, Sq // 2, Sq - 1]
+    rows = [r for r in (0, 1, 31, 32, 63, 64, 127, 128, Sq // 2, Sq - 1) if r < Sq]
     samples = [(0, int(rng.integers(Hq)), i) for i in rows]
     samples += [(0, int(rng.integers(Hq)), int(rng.integers(Sq))) for _ in range(40)]
     qf = oracle.fp8_e4m3_decode(_codes(q8)) * kw["q_descale"]
@@ -130,3 +130,59 @@ def test_fp8_named_workload(name):
     l = np.array([float(lse[b, h, i]) for b, h, i in samples])
     assert float(np.max(np.abs(o - O))) <= TOL_O[v.dtype]
     assert float(np.max(np.abs(l - L))) <= TOL_LSE
+
+
+FP8_SPLIT_CASES = [
+    # B, Hq, Hkv, Sq, Skv, input_pos, window, num_splits (0 = the library's choice)
+    (2, 8, 2, 1, 3000, 2999, 0, 0),       # decoding rows
+    (2, 8, 2, 1, 3000, 2999, 0, 5),
+    (1, 8, 2, 130, 2000, 1870, 0, 3),     # a chunk of queries against a cache
+    (1, 8, 2, 130, 2000, 1870, 300, 16),  # with a sliding window
+    (1, 4, 4, 64, 333, 0, 0, 2),          # causal from 0, ragged key tail
+]
+
+
+def run_split(q8, k8, v, qd, kd, scale, pos, W, splits):
+    out, lse = fa.fa_fwd_splitkv_fp8(q8.to(DEV), k8.to(DEV), v.to(DEV), qd, kd, scale=scale,
+                                     causal=True, input_pos=pos, num_splits=splits, window=W)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+@pytest.mark.parametrize("vdt", ["fp16", "bf16"])
+@pytest.mark.parametrize("case", FP8_SPLIT_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_fp8_splitkv_shapes(case, vdt):
+    """fa_fwd_splitkv_fp8: fp8 queries and keys over split key ranges, merged."""
+    B, Hq, Hkv, Sq, Skv, pos, W, splits = case
+    _say("splitkv", case, vdt)
+    q8, k8, v, qd, kd = make_qkv_fp8(B, Hq, Hkv, Sq, Skv, 128, vdt, seed=sum(case) % 97)
+    scale = 1.0 / math.sqrt(128)
+    out, lse = run_split(q8, k8, v, qd, kd, scale, pos, W, splits)
+    O, L = oracle_fp8(q8, k8, v, scale, qd, kd, True, pos, W)
+    check(O, L, out, lse, v.dtype, f"{case} {vdt}")
+
+
+def test_fp8_splitkv_one_split_is_fa_fwd_fp8():
+    """One split runs the plain kernel: bit-identical to fa_fwd_fp8."""
+    q8, k8, v, qd, kd = make_qkv_fp8(1, 8, 2, 100, 700, 128, "bf16", seed=23)
+    a = run_split(q8, k8, v, qd, kd, 0.09, 600, 0, 1)
+    b = run(q8, k8, v, qd, kd, 0.09, True, 600)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_fp8_splitkv_decode_workload():
+    """The fp8 decoding workload (B=4, GQA 4, one query row against 16384 fp8 keys) in the
+    launch configuration bench.py times (the library's split count), every output row."""
+    name = "gqa4_decode_b4_kv16384_d128_fp8qk_bf16"
+    _say("workload", name)
+    q8, k8, v, kw = make_fp8_workload(name, seed=0)
+    w = FP8_WORKLOADS[name]
+    splits = fa.splitkv_num_splits_fp8(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"], True,
+                                       kw["input_pos"], v.dtype)
+    assert splits > 1
+    out, lse = run_split(q8, k8, v, kw["q_descale"], kw["k_descale"], kw["scale"], kw["input_pos"],
+                         0, splits)
+    O, L = oracle_fp8(q8, k8, v, kw["scale"], kw["q_descale"], kw["k_descale"], True,
+                      kw["input_pos"])
+    check(O, L, out, lse, v.dtype, name)
+
