@@ -1,0 +1,150 @@
+"""Seeded random-shape GPU parity sweep over every entry point against the fp64 oracle.
+
+Each case draws head dim, dtype, GQA group, ragged lengths, causality, input_pos, a sliding
+window and (for split-KV) a split count from a fixed seed, runs one entry point and compares
+every output element with the oracle under the same tolerances as the hand-picked tests:
+O <= 4e-3 (fp16) / 1.6e-2 (bf16), LSE <= 1e-3, gradients as in test_gpu_backward.py.
+The cases are small (the whole sweep runs in seconds) but span one to several tiles in every
+dimension, so tails, partial tiles and empty windows are exercised in combinations the
+hand-picked lists do not name.
+"""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_fa_fwd_amd as fa
+import oracle
+from attention_fa_fwd_amd.inputs import DTYPES, make_qkv, make_qkv_fp8
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {torch.float16: 4e-3, torch.bfloat16: 1.6e-2}
+TOL_LSE = 1e-3
+DEV = torch.device("cuda:0")
+N_CASES = 24
+
+
+def _say(*a):
+    print("[random]", *a, file=sys.stderr, flush=True)
+
+
+def draw(rng, fp8=False, backward=False):
+    """One random problem: (B, Hq, Hkv, Sq, Skv, D, dtype, causal, input_pos, window)."""
+    D = 128 if fp8 else int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["fp16", "bf16"]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
+    B = int(rng.integers(1, 3))
+    Sq = int(rng.integers(1, 300 if backward else 400))
+    causal = bool(rng.random() < 0.75)
+    if causal:
+        input_pos = int(rng.choice([0, 0, int(rng.integers(0, 500))]))
+        Skv = int(rng.integers(1, 600)) if input_pos else int(rng.integers(max(1, Sq // 2), 600))
+        window = int(rng.choice([0, 0, int(rng.integers(1, 400))]))
+    else:
+        input_pos, window = 0, 0
+        Skv = int(rng.integers(1, 600))
+    return B, Hq, Hkv, Sq, Skv, D, dtype, causal, input_pos, window
+
+
+def check_fwd(O, L, out, lse, dtype, what):
+    o, l = out.cpu().double().numpy(), lse.cpu().double().numpy()
+    empty = ~np.isfinite(L)
+    assert np.all(l[empty] == -np.inf) and np.all(o[empty] == 0.0), f"empty rows {what}"
+    assert np.isfinite(o).all() and np.isfinite(l[~empty]).all(), f"non-finite output {what}"
+    eo = float(np.max(np.abs(o - O))) if o.size else 0.0
+    el = float(np.max(np.abs(l[~empty] - L[~empty]))) if (~empty).any() else 0.0
+    assert eo <= TOL_O[dtype], f"O err {eo:.3e} {what}"
+    assert el <= TOL_LSE, f"LSE err {el:.3e} {what}"
+
+
+def _f64(t):
+    return t.double().numpy()
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_forward(i):
+    """fa_fwd / fa_fwd_window on a random problem."""
+    rng = np.random.default_rng(1000 + i)
+    B, Hq, Hkv, Sq, Skv, D, dt, causal, pos, W = draw(rng)
+    what = (B, Hq, Hkv, Sq, Skv, D, dt, causal, pos, W)
+    _say("forward", what)
+    q, k, v = make_qkv(B, Hq, Hkv, Sq, Skv, D, dt, seed=i)
+    scale = float(rng.uniform(0.05, 0.2))
+    out, lse = fa.fa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale=scale, causal=causal,
+                         input_pos=pos, window=W)
+    torch.cuda.synchronize()
+    O, L = oracle.attention_blocked(_f64(q), _f64(k), _f64(v), scale, causal, pos, window=W)
+    check_fwd(O, L, out, lse, q.dtype, what)
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_splitkv(i):
+    """fa_fwd_splitkv with a random split count (0 = the library's choice)."""
+    rng = np.random.default_rng(2000 + i)
+    B, Hq, Hkv, Sq, Skv, D, dt, causal, pos, W = draw(rng)
+    splits = int(rng.choice([0, 2, 3, 7, 16, 64]))
+    what = (B, Hq, Hkv, Sq, Skv, D, dt, causal, pos, W, splits)
+    _say("splitkv", what)
+    q, k, v = make_qkv(B, Hq, Hkv, Sq, Skv, D, dt, seed=100 + i)
+    out, lse = fa.fa_fwd_splitkv(q.to(DEV), k.to(DEV), v.to(DEV), scale=0.1, causal=causal,
+                                 input_pos=pos, num_splits=splits, window=W)
+    torch.cuda.synchronize()
+    O, L = oracle.attention_blocked(_f64(q), _f64(k), _f64(v), 0.1, causal, pos, window=W)
+    check_fwd(O, L, out, lse, q.dtype, what)
+
+
+@pytest.mark.parametrize("i", range(N_CASES // 2))
+def test_random_fp8(i):
+    """fa_fwd_fp8 and fa_fwd_splitkv_fp8 on random problems (head dim 128)."""
+    rng = np.random.default_rng(3000 + i)
+    B, Hq, Hkv, Sq, Skv, D, dt, causal, pos, W = draw(rng, fp8=True)
+    what = (B, Hq, Hkv, Sq, Skv, D, dt, causal, pos, W)
+    _say("fp8", what)
+    q8, k8, v, qd, kd = make_qkv_fp8(B, Hq, Hkv, Sq, Skv, D, dt, seed=200 + i)
+    O, L = oracle.attention_fp8_blocked(q8.view(torch.uint8).numpy(), k8.view(torch.uint8).numpy(),
+                                        _f64(v), 0.09, qd, kd, causal, pos, window=W)
+    out, lse = fa.fa_fwd_fp8(q8.to(DEV), k8.to(DEV), v.to(DEV), qd, kd, scale=0.09, causal=causal,
+                             input_pos=pos, window=W)
+    torch.cuda.synchronize()
+    check_fwd(O, L, out, lse, v.dtype, what)
+    splits = int(rng.choice([0, 2, 5]))
+    out, lse = fa.fa_fwd_splitkv_fp8(q8.to(DEV), k8.to(DEV), v.to(DEV), qd, kd, scale=0.09,
+                                     causal=causal, input_pos=pos, num_splits=splits, window=W)
+    torch.cuda.synchronize()
+    check_fwd(O, L, out, lse, v.dtype, what + (splits,))
+
+
+@pytest.mark.parametrize("i", range(N_CASES // 2))
+def test_random_backward(i):
+    """fa_bwd on random problems, every gradient element against the oracle."""
+    rng = np.random.default_rng(4000 + i)
+    B, Hq, Hkv, Sq, Skv, D, dt, causal, pos, W = draw(rng, backward=True)
+    what = (B, Hq, Hkv, Sq, Skv, D, dt, causal, pos, W)
+    _say("backward", what)
+    q, k, v = make_qkv(B, Hq, Hkv, Sq, Skv, D, dt, seed=300 + i)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(500 + i)
+    do = torch.randn(q.shape, generator=g).to(DTYPES[dt])
+    scale = 1.0 / math.sqrt(D)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    out, lse = fa.fa_fwd(qd, kd, vd, scale=scale, causal=causal, input_pos=pos, window=W)
+    grads = fa.fa_bwd(qd, kd, vd, out, lse, dod, scale=scale, causal=causal, input_pos=pos,
+                      window=W)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward_blocked(_f64(q), _f64(k), _f64(v), _f64(do), scale, causal,
+                                            pos, W)
+    top = max(float(np.max(np.abs(r))) if r.size else 0.0 for r in ref)
+    tol = {"fp16": 4e-3, "bf16": 1.6e-2}[dt]
+    for name, gv, r in zip(("dq", "dk", "dv"), grads, ref):
+        gd = gv.cpu().double().numpy()
+        assert np.isfinite(gd).all(), f"{name} non-finite {what}"
+        err = float(np.max(np.abs(gd - r))) if r.size else 0.0
+        bound = tol * max(float(np.max(np.abs(r))) if r.size else 0.0, 0.05 * top, 1e-6)
+        assert err <= bound, f"{name} err {err:.3e} > {bound:.3e} {what}"
