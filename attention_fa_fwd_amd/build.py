@@ -74,6 +74,27 @@ def build_library(verbose: bool = True, extra_flags=None, jobs=None) -> str:
     return LIB_PATH
 
 
+C_CALLER_SRC = os.path.join(ROOT, "tests", "c", "fa_c_caller.c")
+C_CALLER_BIN = os.path.join(ROOT, "tests", "c", "fa_c_caller")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_c_caller(verbose: bool = True) -> str:
+    """Compile the plain-C test caller of the library (gcc, C99, HIP runtime API) against
+    the built libfa_fwd.so; returns the binary's path."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler (gcc) found for the C-ABI test caller")
+    cmd = [cc, "-std=c99", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           f"-I{ROCM}/include", f"-I{INCLUDE}", C_CALLER_SRC, "-o", C_CALLER_BIN,
+           f"-L{PKG}", "-lfa_fwd", f"-L{ROCM}/lib", "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../attention_fa_fwd_amd", f"-Wl,-rpath,{ROCM}/lib"]
+    if verbose:
+        print("[build]", " ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return C_CALLER_BIN
+
+
 def main(argv=None) -> int:
     build_library(verbose=True, extra_flags=(argv if argv is not None else sys.argv[1:]))
     return 0

@@ -11,8 +11,8 @@ import pytest
 
 import attention_fa_fwd_amd as fa
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
-                      "fa_fwd.h")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_fwd.h")
 
 # Fake, well-aligned, non-overlapping device addresses: validation only compares them.
 P = 1 << 30
@@ -319,3 +319,19 @@ def test_fp8_configs(lib):
     assert lib.fa_fwd_config(*args, fp8[0]) == -10
     with pytest.raises(fa.FaError):
         fa.select_config_fp8(1, 32, 4, 8192, 64, True, 1)
+
+
+def test_header_compiles_as_c99():
+    """include/fa_fwd.h is a C header: the plain-C test caller (which includes it) passes a
+    C99 syntax check with warnings as errors."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("gcc not available")
+    src = os.path.join(ROOT, "tests", "c", "fa_c_caller.c")
+    r = subprocess.run([cc, "-std=c99", "-fsyntax-only", "-Wall", "-Wextra", "-Werror",
+                        "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", f"-I{ROOT}/include", src],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
