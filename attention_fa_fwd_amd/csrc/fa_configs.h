@@ -14,11 +14,12 @@
 
 // Head dim 128: 32-key tiles (a 32 x 64 tile is too small to split over 512 threads, and
 // with three LDS buffers and three register sets a 64-key tile does not fit two waves per
-// SIMD).
+// SIMD).  1 x 8: all eight query heads of a GQA-8 group on one 32-row block.
 #define FA_SHAPES_BN32(X, C, B, Q, CN, TN)                                                  \
     X(128, 32, 1, 1, 4, C, B, Q, CN, TN) X(128, 32, 1, 2, 4, C, B, Q, CN, TN)               \
     X(128, 32, 1, 2, 2, C, B, Q, CN, TN) X(128, 32, 1, 4, 2, C, B, Q, CN, TN)               \
-    X(128, 32, 1, 4, 1, C, B, Q, CN, TN) X(128, 32, 1, 8, 1, C, B, Q, CN, TN)
+    X(128, 32, 1, 4, 1, C, B, Q, CN, TN) X(128, 32, 1, 8, 1, C, B, Q, CN, TN)               \
+    X(128, 32, 1, 1, 8, C, B, Q, CN, TN)
 
 #define FA_LIST_D64(X)                                                                      \
     FA_SHAPES_BN64(X, 64, true, true, "causal", "bf16")                                     \

@@ -163,7 +163,12 @@ int select(int B, int Hq, int Hkv, int Sq, int D, int causal, int dtype, int qk8
     const int group = Hq / Hkv;
     const int bn = D == 128 ? 32 : 64;
     int big, small;
-    if (group % 4 == 0) {
+    if (group % 8 == 0 && D == 128) {
+        // All eight heads of a group on one 32-row block: the K/V tile is shared by eight
+        // waves as with 2 x 4, and the waves reach the causal diagonal together.
+        big = find(D, bf16, cz, q8, bn, 1, 1, 8);
+        small = find(D, bf16, cz, q8, bn, 1, 1, 4);
+    } else if (group % 4 == 0) {
         big = find(D, bf16, cz, q8, bn, 1, 2, 4);
         small = find(D, bf16, cz, q8, bn, 1, 1, 4);
     } else if (group % 2 == 0) {

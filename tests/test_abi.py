@@ -306,9 +306,9 @@ def test_fp8_splitkv_num_splits(lib):
 def test_fp8_configs(lib):
     names = fa.config_names()
     fp8 = [i for i, nm in enumerate(names) if "_fp8qk_" in nm]
-    assert len(fp8) == 24 and all(names[i].startswith("D128_BN32_") for i in fp8)
+    assert len(fp8) == 28 and all(names[i].startswith("D128_BN32_") for i in fp8)
     c = fa.select_config_fp8(1, 32, 4, 8192, 128, True, 1)
-    assert names[c] == "D128_BN32_Mw1x32_WPH2_HPW4_causal_fp8qk_bf16"
+    assert names[c] == "D128_BN32_Mw1x32_WPH1_HPW8_causal_fp8qk_bf16"
     c = fa.select_config_fp8(1, 32, 32, 4096, 128, True, 0)
     assert names[c] == "D128_BN32_Mw1x32_WPH8_HPW1_causal_fp8qk_fp16"
     # a bf16 configuration is not applicable to an fp8 call, nor the reverse

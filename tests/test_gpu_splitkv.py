@@ -98,7 +98,7 @@ def test_split_shapes(case, dtype):
 @pytest.mark.parametrize("causal", [False, True])
 def test_every_config_split(dtype, causal):
     """Every compiled configuration that fits the call, with 3 ranges."""
-    q, k, v = make_qkv(1, 8, 2, 333, 333, 128, dtype, seed=9)
+    q, k, v = make_qkv(1, 16, 2, 333, 333, 128, dtype, seed=9)   # GQA 8: every shape applies
     pos = 7 if causal else 0
     tested = 0
     for cid, name in enumerate(fa.config_names()):
