@@ -30,6 +30,12 @@ HIPCC_FLAGS = [
     "-Wall",
     "-Wno-unused-command-line-argument",
 ]
+# Extra flags of single translation units.  The backward kernels run about 2% faster
+# without the post-register-allocation machine scheduler (interleaved timing of both
+# backward workloads); the forward kernels are unaffected by it and keep the default.
+PER_FILE_FLAGS = {
+    "fa_bwd.hip": ["-mllvm", "-enable-post-misched=0"],
+}
 
 
 def hipcc() -> str:
@@ -56,7 +62,8 @@ def build_library(verbose: bool = True, extra_flags=None, jobs=None) -> str:
         for src in sources():
             obj = os.path.join(tmpdir, os.path.basename(src)[:-4] + ".o")
             objs.append(obj)
-            cmds.append([cc, *flags, f"-I{INCLUDE}", f"-I{CSRC}", "-c", src, "-o", obj])
+            extra = PER_FILE_FLAGS.get(os.path.basename(src), [])
+            cmds.append([cc, *flags, *extra, f"-I{INCLUDE}", f"-I{CSRC}", "-c", src, "-o", obj])
         n = jobs or min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
 
         def run(cmd):

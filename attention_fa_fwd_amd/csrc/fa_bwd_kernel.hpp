@@ -277,7 +277,6 @@ void fa_bwd_kernel(BwdParams p) {
         qa = min(a, qt1);
         qb = max(min(e, qt1), qa);
     }
-    const int nq = qt1 - qt0;
 
     constexpr int T4 = NB > 4 ? TILE : 16, S4 = NB > 4 ? STB : 16;
     __shared__ __attribute__((aligned(16))) unsigned char t1_0[TILE], t1_1[TILE], t1_2[TILE], t1_3[TILE], t1_4[T4], t1_5[T4];
