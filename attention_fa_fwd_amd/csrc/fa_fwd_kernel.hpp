@@ -221,14 +221,22 @@ __device__ __forceinline__ int k_swz(int row) {
     if constexpr (D == 128) return row & 15;
     else return (row & 7) ^ ((row >> 3) & 1);
 }
-// V rows (transpose reads touch 4 consecutive keys x 4 chunks per 16 lanes): a swizzle
-// taken from key mod 4 that spreads those 16 pieces over distinct banks.
+// V rows: a swizzle taken from key mod 4.  A transposed read serves 32 lanes per pass: 4
+// consecutive keys x 4 chunks x 16 bytes = 256 bytes, which must fall on the 64 distinct
+// 4-byte banks.  Head dim 128 (256-byte rows, all four keys on the same banks): the four keys
+// take chunk XORs {0, 4, 9, 13}.  Head dim 64 (128-byte rows, keys k and k + 2 on the same
+// banks): XORs {0, 1, 4, 5}, so keys k and k + 2 use opposite halves of the row.  Both also
+// keep each 16-lane half of a pass on distinct banks.
+template <int D>
 __device__ __forceinline__ int v_swz_of(int key_mod4) {
-    return ((key_mod4 & 1) << 2) | ((key_mod4 >> 1) & 1) | (((key_mod4 >> 1) & 1) << 3);
+    if constexpr (D == 128)
+        return ((key_mod4 & 1) << 2) | ((key_mod4 >> 1) & 1) | (((key_mod4 >> 1) & 1) << 3);
+    else
+        return (((key_mod4 >> 1) & 1) << 2) | (key_mod4 & 1);
 }
 template <int D>
 __device__ __forceinline__ int v_swz(int row) {
-    return v_swz_of(row & 3) & (D / 8 - 1);
+    return v_swz_of<D>(row & 3);
 }
 
 template <class C>
@@ -434,7 +442,7 @@ void fa_fwd_kernel(Params p) {
     // 8*(g&1) + 4*(qq>>1), with jj, qq from the lane's index in its 16-lane group g.
     const int vs = lane & 15, vj = vs >> 2, vq = vs & 3, vg = lane >> 4;
     const int v_lane_row = 4 * (vg >> 1) + vj;
-    const int vu = (2 * (vq & 1) + (vg & 1)) ^ (v_swz_of(vj) & (CPR - 1));   // chunk ^ 4*db
+    const int vu = (2 * (vq & 1) + (vg & 1)) ^ v_swz_of<D>(vj);   // chunk ^ 4*db
     int voff[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
