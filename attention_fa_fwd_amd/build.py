@@ -81,6 +81,23 @@ def build_library(verbose: bool = True, extra_flags=None, jobs=None) -> str:
     return LIB_PATH
 
 
+PROBE_SRC = os.path.join(PKG, "probe", "fa_peak_probe.hip")
+PROBE_PATH = os.path.join(PKG, "libfa_probe.so")
+
+
+def build_probe(verbose: bool = True) -> str:
+    """Compile the benchmark's device and MFMA-peak probe (``probe/fa_peak_probe.hip``) into
+    ``libfa_probe.so``, apart from the attention library; returns its path."""
+    flags = [f for f in HIPCC_FLAGS]
+    tmp = PROBE_PATH + ".tmp"
+    cmd = [hipcc(), *flags, PROBE_SRC, "-o", tmp]
+    if verbose:
+        print("[build]", " ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, PROBE_PATH)
+    return PROBE_PATH
+
+
 C_CALLER_SRC = os.path.join(ROOT, "tests", "c", "fa_c_caller.c")
 C_CALLER_BIN = os.path.join(ROOT, "tests", "c", "fa_c_caller")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")

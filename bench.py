@@ -331,6 +331,35 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False, bac
     return line
 
 
+PROBE_LIB = os.path.join(ROOT, "attention_fa_fwd_amd", "libfa_probe.so")
+
+
+def peak_check(iters=100000):
+    """The peak re-derived on this device and checked by measurement: compute units and peak
+    engine clock from hipDeviceProp (x 4096 dense bf16 FLOP/clk/CU), and a loop of nothing but
+    bf16 MFMAs on every SIMD (libfa_probe.so) with the shader clock it ran at."""
+    import ctypes
+
+    if not os.path.exists(PROBE_LIB):
+        return {"error": "libfa_probe.so not built"}
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.fa_probe_device.argtypes = [ctypes.POINTER(ctypes.c_int)] * 2
+    lib.fa_probe_mfma.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    cus, khz = ctypes.c_int(0), ctypes.c_int(0)
+    rc = lib.fa_probe_device(ctypes.byref(cus), ctypes.byref(khz))
+    if rc != 0:
+        return {"error": f"fa_probe_device: hip error {rc}"}
+    tf, ghz = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    rc = lib.fa_probe_mfma(iters, ctypes.byref(tf), ctypes.byref(ghz))
+    if rc != 0:
+        return {"error": f"fa_probe_mfma: hip error {rc}"}
+    derived = cus.value * khz.value * 1e3 * 4096 / 1e12
+    return {"cus": cus.value, "max_clock_mhz": round(khz.value / 1e3, 1),
+            "derived_peak_tflops": round(derived, 1),
+            "mfma_loop_tflops": round(tf.value, 1), "mfma_loop_clock_ghz": round(ghz.value, 3),
+            "mfma_loop_frac_of_derived_peak": round(tf.value / derived, 4) if derived else None}
+
+
 COPY_BYTES = 1 << 30
 
 
@@ -377,6 +406,9 @@ def main(argv=None):
         return 2
     line = bench_line(a.workload, a.steps, a.warmup, a.config, with_cpu=not a.no_cpu_baseline,
                       splitkv=a.splitkv, backward=a.backward)
+    if line["unit"] == "TFLOP/s":
+        log("MFMA peak probe ...")
+        line["peak_check"] = peak_check()
     if a.all:
         from attention_fa_fwd_amd.inputs import FP8_WORKLOADS, WORKLOADS
 
