@@ -19,8 +19,11 @@ reported as "warmup_extra_steps".
 count, workspace allocated before the timed region) instead; decoding workloads (one query
 row) are reported in GB/s against the HBM roofline, since reading K and V bounds them.
 
+--cold writes 512 MiB (twice the last-level cache) before each launch, outside the events
+that time it, so every launch starts with cold caches.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--splitkv]
-                       [--backward] [--all]
+                       [--backward] [--cold] [--all]
 """
 
 from __future__ import annotations
@@ -48,6 +51,7 @@ METRIC_BWD = "attention bwd TFLOP/s (2.5x the forward FLOPs: five matrix product
 METRIC_FP8 = "attention fwd TFLOP/s, fp8 E4M3 Q/K (Q K^T on the fp8 MFMA), fp16/bf16 P V"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.json")
 MIN_WARMUP_S = 0.3
+COLD_FLUSH_BYTES = 512 << 20
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
 KERNEL_SOURCES = [os.path.join(ROOT, "attention_fa_fwd_amd", "csrc", f)
                   for f in ("fa_fwd_kernel.hpp", "fa_fwd.hip")]
@@ -129,7 +133,7 @@ def workload(name):
     return WORKLOADS[name], False
 
 
-def time_gpu(name, steps, warmup, config=-1, splitkv=False, backward=False):
+def time_gpu(name, steps, warmup, config=-1, splitkv=False, backward=False, cold=False):
     import torch
 
     import attention_fa_fwd_amd as fa
@@ -207,17 +211,35 @@ def time_gpu(name, steps, warmup, config=-1, splitkv=False, backward=False):
             step()
         extra += 10
         torch.cuda.synchronize()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    evs[0].record(stream)
-    for i in range(steps):
-        step()
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))  # ms per launch
-    total_ms = evs[0].elapsed_time(evs[-1])
+    if cold:
+        # Cold caches: write COLD_FLUSH_BYTES (twice the 256 MB last-level cache) before each
+        # launch, outside the events that time it.
+        flush = torch.empty(COLD_FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            flush.fill_(i & 255)
+            ev0[i].record(stream)
+            step()
+            ev1[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = sorted(ev0[i].elapsed_time(ev1[i]) for i in range(steps))
+        total_ms = sum(per)
+    else:
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        evs[0].record(stream)
+        for i in range(steps):
+            step()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))  # ms per launch
+        total_ms = evs[0].elapsed_time(evs[-1])
     if config >= 0:
         cfg = config
     elif fp8:
@@ -267,10 +289,11 @@ def cpu_baseline(name, min_s=10.0):
                 wall_s=round(dt, 3))
 
 
-def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False, backward=False):
+def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False, backward=False,
+               cold=False):
     w, fp8 = workload(name)
     log(f"workload {name}: {w}")
-    r = time_gpu(name, steps, warmup, config, splitkv, backward)
+    r = time_gpu(name, steps, warmup, config, splitkv, backward, cold)
     ms_step = r["total_ms"] / steps
     flops = literal_flops(w) * (2.5 if backward else 1.0)
     value = flops / (ms_step * 1e-3) / 1e12
@@ -297,7 +320,7 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False, bac
         peak = PEAK_FP8QK_TFLOPS if fp8 else PEAK_TFLOPS
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                    "traffic": None if (splitkv or backward) else traffic_bytes(name)}
+                    "traffic": None if (splitkv or backward or cold) else traffic_bytes(name)}
     line = {
         "metric": metric,
         "value": round(value, 2),
@@ -316,6 +339,8 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False, bac
                    "Skv": w["Skv"], "D": w["D"], "causal": w["causal"],
                    "input_pos": w["input_pos"], "window": w.get("window", 0),
                    "kernel": r["kernel"], "path": path,
+                   "caches": (f"cold: {COLD_FLUSH_BYTES >> 20} MiB written before each launch, "
+                              "outside its events") if cold else "warm: launches back to back",
                    "parallelism": "single GPU"},
         "kernel_us": {"mean": round(mean_kernel_ms * 1e3, 2), "median": round(med * 1e3, 2),
                       "p95": round(p95 * 1e3, 2), "min": round(r["per_ms"][0] * 1e3, 2)},
@@ -389,6 +414,9 @@ def main(argv=None):
                     help="time fa_fwd_splitkv with the library's split count")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass fa_bwd (forward results precomputed)")
+    ap.add_argument("--cold", action="store_true",
+                    help="write 512 MiB between launches (cold L2 and last-level cache) and time "
+                         "each launch alone")
     ap.add_argument("--all", action="store_true",
                     help="also time every named workload (extra JSON lines on stderr)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -405,7 +433,7 @@ def main(argv=None):
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
     line = bench_line(a.workload, a.steps, a.warmup, a.config, with_cpu=not a.no_cpu_baseline,
-                      splitkv=a.splitkv, backward=a.backward)
+                      splitkv=a.splitkv, backward=a.backward, cold=a.cold)
     if line["unit"] == "TFLOP/s":
         log("MFMA peak probe ...")
         line["peak_check"] = peak_check()

@@ -115,6 +115,22 @@ def test_bench_line_backward_and_decode(monkeypatch):
     assert "gqa8_causal_s8192_d128_fp8qk_bf16" in FP8_WORKLOADS
 
 
+def test_bench_line_cold(monkeypatch):
+    seen = {}
+
+    def stub(*a, **k):
+        seen["args"] = a
+        return _fake_timing([600.0] * 4, 4)
+
+    monkeypatch.setattr(bench, "time_gpu", stub)
+    line = bench.bench_line(bench.HEADLINE, 4, 0, with_cpu=False, cold=True)
+    assert seen["args"][-1] is True                     # cold passed through to the timing
+    assert line["config"]["caches"].startswith("cold")
+    assert line["roofline"]["traffic"] is None          # warm counters do not describe it
+    warm = bench.bench_line(bench.HEADLINE, 4, 0, with_cpu=False)
+    assert warm["config"]["caches"].startswith("warm")
+
+
 def test_traffic_lookup_follows_kernel_sources(tmp_path, monkeypatch):
     f = tmp_path / "traffic.json"
     entry = {"workloads": {bench.HEADLINE: {"hbm_bytes_per_launch": 123456}}}
