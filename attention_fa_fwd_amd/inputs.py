@@ -44,6 +44,15 @@ WORKLOADS = {
 
 # Workloads with fp8 E4M3 queries and keys (per-tensor descale factors) and fp16 / bf16
 # values: the headline and the causal multi-head shapes.
+# A sequence-length sweep of causal MHA at B=4, H=32, D=128, fp16: the shape of the length
+# sweep in "Tuning Flash Attention for peak performance in NVIDIA CUDA Tile" (Tables 1-6),
+# timed for context only.
+SWEEP_WORKLOADS = {
+    f"mha_causal_b4_s{S}_d128_fp16": dict(B=4, Hq=32, Hkv=32, Sq=S, Skv=S, D=128, dtype="fp16",
+                                          causal=True, input_pos=0)
+    for S in (1024, 2048, 4096, 8192, 16384)
+}
+
 FP8_WORKLOADS = {
     "gqa8_causal_s8192_d128_fp8qk_bf16": dict(B=1, Hq=32, Hkv=4, Sq=8192, Skv=8192, D=128,
                                               dtype="bf16", causal=True, input_pos=0),
@@ -102,7 +111,7 @@ def make_qkv_fp8(B, Hq, Hkv, Sq, Skv, D, v_dtype, seed=0):
 
 def make_workload(name, seed=0):
     """Inputs and call arguments for a named workload: (q, k, v, kwargs)."""
-    w = dict(WORKLOADS[name])
+    w = dict(WORKLOADS[name] if name in WORKLOADS else SWEEP_WORKLOADS[name])
     q, k, v = make_qkv(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"], w["dtype"], seed)
     kw = dict(scale=default_scale(w["D"]), causal=w["causal"], input_pos=w["input_pos"],
               window=w.get("window", 0))

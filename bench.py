@@ -23,7 +23,7 @@ row) are reported in GB/s against the HBM roofline, since reading K and V bounds
 that time it, so every launch starts with cold caches.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--splitkv]
-                       [--backward] [--cold] [--all]
+                       [--backward] [--cold] [--sweep] [--all]
 """
 
 from __future__ import annotations
@@ -126,10 +126,12 @@ def algorithmic_bytes(w, fp8=False):
 
 def workload(name):
     """(shape dict, is fp8) of a named workload."""
-    from attention_fa_fwd_amd.inputs import FP8_WORKLOADS, WORKLOADS
+    from attention_fa_fwd_amd.inputs import FP8_WORKLOADS, SWEEP_WORKLOADS, WORKLOADS
 
     if name in FP8_WORKLOADS:
         return FP8_WORKLOADS[name], True
+    if name in SWEEP_WORKLOADS:
+        return SWEEP_WORKLOADS[name], False
     return WORKLOADS[name], False
 
 
@@ -417,6 +419,9 @@ def main(argv=None):
     ap.add_argument("--cold", action="store_true",
                     help="write 512 MiB between launches (cold L2 and last-level cache) and time "
                          "each launch alone")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time causal MHA at B=4, H=32, D=128, fp16, S = 1K..16K (context; "
+                         "extra JSON lines on stderr)")
     ap.add_argument("--all", action="store_true",
                     help="also time every named workload (extra JSON lines on stderr)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -451,6 +456,12 @@ def main(argv=None):
         for name in (HEADLINE, "mha_causal_s4096_d128_fp16"):
             extra = bench_line(name, max(1, a.steps // 4), a.warmup, -1, with_cpu=False,
                                backward=True)
+            print("[bench-extra] " + json.dumps(extra), file=sys.stderr, flush=True)
+    if a.sweep:
+        from attention_fa_fwd_amd.inputs import SWEEP_WORKLOADS
+
+        for name in SWEEP_WORKLOADS:
+            extra = bench_line(name, max(1, a.steps // 4), a.warmup, -1, with_cpu=False)
             print("[bench-extra] " + json.dumps(extra), file=sys.stderr, flush=True)
     print(json.dumps(line), flush=True)
     return 0
