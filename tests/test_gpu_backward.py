@@ -77,6 +77,9 @@ BWD_CASES = [
     (1, 32, 4, 256, 256, 128, True, 0, 0),     # small K/V grid: the group split 8 ways
     (1, 32, 8, 256, 2048, 64, False, 0, 0),    # GQA 4 split over 2 workgroups
     (2, 32, 16, 128, 2048, 64, True, 1920, 0), # GQA 2 with a K/V grid large enough not to split
+    (1, 6, 2, 200, 300, 128, True, 40, 0),     # GQA 3: odd group
+    (1, 12, 2, 150, 150, 64, True, 0, 0),      # GQA 6
+    (1, 21, 3, 96, 200, 128, False, 0, 0),     # GQA 7, non-causal
 ]
 
 

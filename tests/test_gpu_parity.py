@@ -67,6 +67,11 @@ SMALL = [
     (1, 8, 4, 200, 200, 128, True, 500),      # input_pos + i beyond Skv: all keys visible
     (3, 6, 3, 129, 64, 64, True, 0),          # Sq > Skv
     (1, 32, 4, 256, 256, 128, True, 0),
+    (1, 6, 2, 200, 300, 128, True, 40),       # GQA 3: odd group, one head per wave group
+    (1, 10, 2, 100, 180, 128, False, 0),      # GQA 5
+    (2, 12, 2, 150, 150, 64, True, 0),        # GQA 6: pairs of heads per workgroup
+    (1, 24, 2, 96, 160, 128, True, 64),       # GQA 12: four heads per workgroup, three groups
+    (1, 14, 2, 70, 70, 128, True, 0),         # GQA 7
 ]
 
 
