@@ -1,6 +1,6 @@
 """Seeded random-shape GPU parity sweep over every entry point against the fp64 oracle.
 
-Each case draws head dim, dtype, GQA group, ragged lengths, causality, input_pos, a sliding
+Each case draws head dim, dtype, GQA group (1, 2, 3, 4, 6 or 8), ragged lengths, causality, input_pos, a sliding
 window and (for split-KV) a split count from a fixed seed, runs one entry point and compares
 every output element with the oracle under the same tolerances as the hand-picked tests:
 O <= 4e-3 (fp16) / 1.6e-2 (bf16), LSE <= 1e-3, gradients as in test_gpu_backward.py.
@@ -39,7 +39,7 @@ def draw(rng, fp8=False, backward=False):
     D = 128 if fp8 else int(rng.choice([64, 128]))
     dtype = str(rng.choice(["fp16", "bf16"]))
     Hkv = int(rng.choice([1, 2, 4]))
-    Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
+    Hq = Hkv * int(rng.choice([1, 2, 3, 4, 6, 8]))
     B = int(rng.integers(1, 3))
     Sq = int(rng.integers(1, 300 if backward else 400))
     causal = bool(rng.random() < 0.75)
