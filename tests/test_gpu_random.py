@@ -2,8 +2,8 @@
 
 Each case draws head dim, dtype, GQA group (1, 2, 3, 4, 6 or 8), ragged lengths, causality,
 input_pos, a sliding window and (for split-KV) a split count from a fixed seed, runs one entry
-point and compares
-every output element with the oracle under the same tolerances as the hand-picked tests:
+point and compares every output element with the oracle under the same tolerances as the
+hand-picked tests:
 O <= 4e-3 (fp16) / 1.6e-2 (bf16), LSE <= 1e-3, gradients as in test_gpu_backward.py.
 The cases are small (the whole sweep runs in seconds) but span one to several tiles in every
 dimension, so tails, partial tiles and empty windows are exercised in combinations the
