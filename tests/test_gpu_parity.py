@@ -194,3 +194,59 @@ def test_runs_on_a_side_stream():
         out, lse = fa.fa_fwd(qd, kd, vd, causal=True)
     s.synchronize()
     check_full(q, k, v, 1 / math.sqrt(128), True, 0, out.cpu(), lse.cpu(), "side stream")
+
+
+def test_concurrent_threads_and_streams():
+    """The library keeps no state between calls: four host threads, each on its own stream and
+    problem, interleave 20 calls of fa_fwd / fa_fwd_splitkv / fa_bwd; every result matches,
+    bit for bit, the same call run alone."""
+    import threading
+
+    dev = torch.device("cuda:0")
+    problems = [
+        (1, 8, 2, 300, 300, 128, "bf16", True, 0),
+        (2, 4, 4, 1, 900, 128, "fp16", True, 899),
+        (1, 6, 3, 129, 257, 64, "fp16", False, 0),
+        (1, 8, 1, 200, 200, 128, "bf16", True, 40),
+    ]
+    inputs = []
+    for n, (B, Hq, Hkv, Sq, Skv, D, dt, causal, pos) in enumerate(problems):
+        q, k, v = make_qkv(B, Hq, Hkv, Sq, Skv, D, dt, seed=60 + n)
+        g = torch.Generator(device="cpu")
+        g.manual_seed(70 + n)
+        do = torch.randn(q.shape, generator=g).to(q.dtype)
+        inputs.append(tuple(t.to(dev) for t in (q, k, v, do)) + (causal, pos))
+
+    def run(i):
+        q, k, v, do, causal, pos = inputs[i]
+        out, lse = fa.fa_fwd(q, k, v, causal=causal, input_pos=pos)
+        o2, l2 = fa.fa_fwd_splitkv(q, k, v, causal=causal, input_pos=pos, num_splits=3)
+        grads = fa.fa_bwd(q, k, v, out, lse, do, causal=causal, input_pos=pos)
+        return (out, lse, o2, l2) + tuple(grads)
+
+    torch.cuda.synchronize()
+    alone = [tuple(t.clone() for t in run(i)) for i in range(len(problems))]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream(device=dev)
+            with torch.cuda.stream(s):
+                for _ in range(20):
+                    got = run(i)
+            s.synchronize()
+            for a, b in zip(alone[i], got):
+                if not torch.equal(a, b):
+                    errors.append(f"problem {i}: result differs from the call run alone")
+                    return
+        except Exception as e:  # collected and reported by the main thread
+            errors.append(f"problem {i}: {e!r}")
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(problems))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
+    assert not errors, errors
