@@ -250,3 +250,61 @@ def test_concurrent_threads_and_streams():
         t.join(timeout=120)
     assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
     assert not errors, errors
+
+
+def test_hip_graph_capture_and_replay():
+    """fa_fwd, fa_bwd and the split-KV decode path captured in one HIP graph (torch.cuda.graph):
+    the library only launches kernels on the given stream, so the calls are capturable.  The
+    graph is replayed four times; before each replay the inputs are overwritten eagerly, and
+    every replay's outputs must equal, bit for bit, the same calls run eagerly."""
+    dev = torch.device("cuda:0")
+    B, Hq, Hkv, S, D = 1, 8, 2, 256, 128
+    dB, dHq, dHkv, dSkv = 2, 8, 2, 2048
+    bf = torch.bfloat16
+    q = torch.empty((B, Hq, S, D), dtype=bf, device=dev)
+    k = torch.empty((B, Hkv, S, D), dtype=bf, device=dev)
+    v, do = torch.empty_like(k), torch.empty_like(q)
+    out, lse = torch.empty_like(q), torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(16, fa.bwd_workspace_size(B, Hq, Hkv, S, S, D, True)), dtype=torch.uint8, device=dev)
+    qd = torch.empty((dB, dHq, 1, D), dtype=bf, device=dev)
+    kd = torch.empty((dB, dHkv, dSkv, D), dtype=bf, device=dev)
+    vd = torch.empty_like(kd)
+    od, ld = torch.empty_like(qd), torch.empty((dB, dHq, 1), dtype=torch.float32, device=dev)
+    wsd = torch.empty(fa.splitkv_workspace_size(dB, dHq, 1, D, 8), dtype=torch.uint8, device=dev)
+
+    def calls(o, l, gq, gk, gv, odec, ldec):
+        fa.fa_fwd_into(q, k, v, o, l, causal=True)
+        fa.fa_bwd_into(q, k, v, o, l, do, gq, gk, gv, ws, causal=True)
+        fa.fa_fwd_splitkv_into(qd, kd, vd, odec, ldec, wsd, num_splits=8, causal=True,
+                               input_pos=dSkv - 1)
+
+    gen = torch.Generator(device=dev)
+
+    def refill(seed):
+        gen.manual_seed(seed)
+        for t in (q, k, v, do, qd, kd, vd):
+            t.copy_(torch.randn(t.shape, generator=gen, device=dev, dtype=torch.float32))
+
+    refill(0)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        calls(out, lse, dq, dk, dv, od, ld)       # warm-up outside the capture
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls(out, lse, dq, dk, dv, od, ld)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        refill(100 + rep)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = [torch.empty_like(t) for t in (out, lse, dq, dk, dv, od, ld)]
+        calls(*ref)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("out", "lse", "dq", "dk", "dv", "out_dec", "lse_dec"),
+                              (out, lse, dq, dk, dv, od, ld), ref):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager call"
