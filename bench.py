@@ -314,8 +314,10 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False, bac
         # Reading K and V bounds a decoding step: GB/s of algorithmic bytes per call.
         gbs = algorithmic_bytes(w, fp8) / (mean_kernel_ms * 1e-3) / 1e9
         metric, value, unit = "attention decode GB/s of algorithmic HBM bytes", gbs, "GB/s"
+        # Counted bytes of the attention kernel (the merge kernel's are not included).
+        traffic = None if (fp8 or cold) else traffic_bytes(name + ("/splitkv" if splitkv else ""))
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+                    "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
     else:
         achieved = flops / (mean_kernel_ms * 1e-3) / 1e12
         metric, unit = (METRIC_BWD if backward else METRIC_FP8 if fp8 else METRIC), "TFLOP/s"

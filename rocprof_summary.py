@@ -12,6 +12,7 @@
       dispatch), each scaled by what the same counter reads for a plain copy of known
       size (bench.py --calibrate-copy).  Writes the JSON bench.py reads, stamped with the
       hash of the kernel sources, so bench.py reports null once the kernel has changed.
+      A workload NAME/splitkv records the split-KV attention kernel of NAME.
 
 Summaries are printed as text; redirect them into profiles/.
 """
@@ -108,7 +109,7 @@ def traffic(a):
     f_fetch = bench.COPY_BYTES / (cf_kib * 1024.0)
     f_write = bench.COPY_BYTES / (cw_kib * 1024.0)
     hbm = fetch_kib * 1024.0 * f_fetch + write_kib * 1024.0 * f_write
-    w = WORKLOADS[a.workload]
+    w = WORKLOADS[a.workload.split("/")[0]]   # NAME or NAME/splitkv
     algo = (2 * w["B"] * w["Hq"] * w["Sq"] * w["D"] * 2 + 2 * w["B"] * w["Hkv"] * w["Skv"] * w["D"] * 2
             + w["B"] * w["Hq"] * w["Sq"] * 4)
     path = a.out or bench.TRAFFIC_FILE
