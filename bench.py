@@ -439,6 +439,12 @@ def main(argv=None):
     if a.steps < 1 or a.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
+    from attention_fa_fwd_amd import build as fa_build
+
+    if not os.path.exists(fa_build.LIB_PATH):   # nothing built yet: build it first
+        fa_build.build_library(verbose=False)
+    if not os.path.exists(fa_build.PROBE_PATH):
+        fa_build.build_probe(verbose=False)
     line = bench_line(a.workload, a.steps, a.warmup, a.config, with_cpu=not a.no_cpu_baseline,
                       splitkv=a.splitkv, backward=a.backward, cold=a.cold)
     if line["unit"] == "TFLOP/s":
