@@ -151,3 +151,24 @@ def test_rejected_arguments(args):
     assert r.stdout == ""
     if args[0] == "--gpus":
         assert "one GPU only" in r.stderr
+
+
+def test_every_named_workload_resolves(monkeypatch):
+    """Each workload bench.py can time (the list, the fp8 list and the context sweep) resolves
+    to one shape with the right type flag, and a line built from it carries that name."""
+    from attention_fa_fwd_amd.inputs import SWEEP_WORKLOADS
+
+    names = [*WORKLOADS, *FP8_WORKLOADS, *SWEEP_WORKLOADS]
+    assert len(set(names)) == len(names)            # no name in two lists
+    monkeypatch.setattr(bench, "time_gpu", lambda *a, **k: _fake_timing([250.0] * 2, 2))
+    for name in names:
+        w, fp8 = bench.workload(name)
+        assert fp8 == (name in FP8_WORKLOADS)
+        assert bench.literal_flops(w) > 0 and bench.algorithmic_bytes(w, fp8=fp8) > 0
+        line = bench.bench_line(name, 2, 0, with_cpu=False)
+        assert line["config"]["workload"] == name
+    by_len = sorted(SWEEP_WORKLOADS.values(), key=lambda w: w["Sq"])
+    assert [w["Sq"] for w in by_len] == [1024, 2048, 4096, 8192, 16384]
+    for S, w in zip((1024, 2048, 4096, 8192, 16384), by_len):
+        assert (w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"], w["causal"]) == (4, 32, 32, S, S, 128, True)
+        assert bench.literal_flops(w) == 4.0 * 4 * 32 * S * S * 128 / 2
