@@ -315,7 +315,7 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False, bac
         gbs = algorithmic_bytes(w, fp8) / (mean_kernel_ms * 1e-3) / 1e9
         metric, value, unit = "attention decode GB/s of algorithmic HBM bytes", gbs, "GB/s"
         # Counted bytes of the attention kernel (the merge kernel's are not included).
-        traffic = None if (fp8 or cold) else traffic_bytes(name + ("/splitkv" if splitkv else ""))
+        traffic = None if cold else traffic_bytes(name + ("/splitkv" if splitkv else ""))
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
     else:

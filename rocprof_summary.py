@@ -100,7 +100,6 @@ def _counter(db, cname, key):
 def traffic(a):
     sys.path.insert(0, ROOT)
     import bench
-    from attention_fa_fwd_amd.inputs import WORKLOADS
 
     fetch_kib = _counter(a.fetch, "FETCH_SIZE", KERNEL_KEY)
     write_kib = _counter(a.write, "WRITE_SIZE", KERNEL_KEY)
@@ -109,9 +108,8 @@ def traffic(a):
     f_fetch = bench.COPY_BYTES / (cf_kib * 1024.0)
     f_write = bench.COPY_BYTES / (cw_kib * 1024.0)
     hbm = fetch_kib * 1024.0 * f_fetch + write_kib * 1024.0 * f_write
-    w = WORKLOADS[a.workload.split("/")[0]]   # NAME or NAME/splitkv
-    algo = (2 * w["B"] * w["Hq"] * w["Sq"] * w["D"] * 2 + 2 * w["B"] * w["Hkv"] * w["Skv"] * w["D"] * 2
-            + w["B"] * w["Hq"] * w["Sq"] * 4)
+    w, fp8 = bench.workload(a.workload.split("/")[0])   # NAME or NAME/splitkv
+    algo = bench.algorithmic_bytes(w, fp8)
     path = a.out or bench.TRAFFIC_FILE
     try:
         with open(path) as f:
