@@ -3,6 +3,8 @@
 
   python rocprof_summary.py trace DB --command CMD
       kernel-trace summary: calls, mean / median / min / max duration per kernel.
+      With --bench-out FILE (the traced bench.py run's stdout) it also quotes that run's own
+      JSON line: its value and its per-launch event timing, for comparison with the trace.
   python rocprof_summary.py pmc DB --command CMD
       per-kernel mean of each collected counter, plus MFMA utilisation, LDS bank-conflict
       rate and VALU instruction mix when their counters are present.
@@ -44,7 +46,26 @@ def short(name, n=96):
     return name if len(name) <= n else name[:n - 3] + "..."
 
 
-def trace(db, command):
+def bench_of_run(path):
+    """Lines comparing the trace with the bench.py line printed by the traced run itself:
+    its value and its own per-launch event timing (mean, from HIP events)."""
+    line = None
+    with open(path, errors="replace") as f:
+        for raw in f:
+            raw = raw.strip()
+            if raw.startswith('{"metric"'):
+                line = json.loads(raw)
+    if line is None:
+        return ["", "# bench.py line of the same run: not found in " + os.path.basename(path)]
+    k = line.get("kernel_us", {})
+    return ["", "# bench.py line of the same run (HIP events on the launch stream):",
+            f"#   workload {line['config']['workload']}, path {line['config'].get('path')}, "
+            f"kernel {line['config'].get('kernel')}",
+            f"#   value {line['value']} {line['unit']}, kernel_us mean {k.get('mean')} "
+            f"median {k.get('median')} min {k.get('min')}"]
+
+
+def trace(db, command, bench_out=None):
     rows = _rows(db, "select name, duration from kernels")
     by = {}
     for name, dur in rows:
@@ -55,6 +76,8 @@ def trace(db, command):
     for name, d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
         out.append(f"{short(name):<98} {len(d):>5} {statistics.mean(d):>9.1f} "
                    f"{statistics.median(d):>9.1f} {min(d):>9.1f} {max(d):>9.1f}")
+    if bench_out:
+        out += bench_of_run(bench_out)
     return "\n".join(out)
 
 
@@ -150,6 +173,9 @@ def main(argv=None):
         s = sub.add_parser(n)
         s.add_argument("db")
         s.add_argument("--command", default="")
+        if n == "trace":
+            s.add_argument("--bench-out", default=None,
+                           help="stdout of the traced bench.py run, to quote its own timing")
     t = sub.add_parser("traffic")
     for k in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--workload"):
         t.add_argument(k, required=True)
@@ -157,7 +183,7 @@ def main(argv=None):
     t.add_argument("--out", default=None)
     a = ap.parse_args(argv)
     if a.cmd == "trace":
-        print(trace(a.db, a.command))
+        print(trace(a.db, a.command, a.bench_out))
     elif a.cmd == "pmc":
         print(pmc(a.db, a.command))
     else:
