@@ -36,14 +36,15 @@ position.  A row whose V(i) is empty (possible only with a window, when
 input_pos + i - W + 1 >= Skv) is read as O = 0 and LSE = -inf, the values of an
 empty sum.
 
-Four forms are provided, written independently of one another:
+Several forms are provided, written independently of one another:
 
 * ``attention_naive``          pure-Python loops over the definition (tiny shapes);
 * ``attention_blocked``        the definition with NumPy matmuls, row block by row
                                block (the oracle used for parity and the CPU baseline);
-* ``attention_online_tiled``   the tile-by-tile online-softmax algorithm of the
-                               [cuTile] kernel, with its loop bound, K-loop split,
-                               exp2 domain and rescaling, in float64.
+* ``attention_online_tiled``   online softmax over key blocks: a running (max, sum,
+                               output) state per query block, folded one key block
+                               at a time, with fully masked blocks skipped and the
+                               mask consulted only on partly visible blocks.
 * ``attention_key_range`` and ``merge_partials``: the definition over one key
                                range, and the online-softmax fold of several ranges
                                into one result (split-KV).
@@ -67,7 +68,7 @@ import math
 import numpy as np
 
 LN2 = math.log(2.0)
-LOG2E = 1.0 / LN2  # the [cuTile] kernel's INV_LOG_2, Part 1 "Defining the kernel interface"
+LOG2E = 1.0 / LN2
 
 
 # ----------------------------------------------------------------------------
@@ -96,10 +97,10 @@ def attention_naive(q, k, v, scale, causal=False, input_pos=0, window=0):
     """Brute-force definition with pure-Python loops; float64; tiny shapes only.
 
     Follows [cuTile] "What is attention?" (textbook softmax(scale Q K^T + M) V),
-    "Causal attention" (key n visible to query m iff offs_m >= offs_n, where the
-    query position offs_m carries input_pos, Part 1 "Initializing
-    accumulators") and "Grouped-query attention" (query heads in contiguous
-    groups of Hq/Hkv share one K/V head).  window > 0 (causal only) also hides
+    "Causal attention" (key j visible to query i iff j is not later than the
+    query's position input_pos + i, Part 1 "Initializing accumulators") and
+    "Grouped-query attention" (query heads in contiguous groups of Hq/Hkv share
+    one K/V head).  window > 0 (causal only) also hides
     keys before input_pos + i - window + 1; a row left with no key gets O = 0,
     LSE = -inf.
 
@@ -242,7 +243,10 @@ def attention_blocked(q, k, v, scale, causal=False, input_pos=0, rows_per_block=
 
     Row blocking only bounds memory: every row is computed from its full set of
     visible scores in one pass, exactly as defined (module docstring); rows
-    with no visible key (sliding window only) get O = 0 and LSE = -inf.
+    with no visible key (sliding window only) get O = 0 and LSE = -inf.  A block
+    reads only the keys from the first to the last one that some row of the
+    block can see: the keys outside that span are masked for every row of the
+    block, so they would add exp(-inf) = 0 to every sum.
     Returns (O [B,Hq,Sq,D], LSE [B,Hq,Sq]) as float64 arrays.
     """
     B, Hq, Hkv, Sq, Skv, D = _shapes(q, k, v)
@@ -262,9 +266,10 @@ def attention_blocked(q, k, v, scale, causal=False, input_pos=0, rows_per_block=
                 rows = i0 + np.nonzero(vis.any(axis=1))[0]
                 if rows.size == 0:
                     continue
-                s = scaled_scores(np.asarray(q[b, hq, rows], np.float64), kh, scale)
-                m, e, l = masked_softmax_stats(s, vis[rows - i0])
-                O[b, hq, rows] = normalise(e, l, vh)
+                j0, j1 = visible_key_span(vis[rows - i0])
+                s = scaled_scores(np.asarray(q[b, hq, rows], np.float64), kh[j0:j1], scale)
+                m, e, l = masked_softmax_stats(s, vis[rows - i0, j0:j1])
+                O[b, hq, rows] = normalise(e, l, vh[j0:j1])
                 L[b, hq, rows] = log_sum_exp(m, l)
     return O, L
 
@@ -303,128 +308,133 @@ def attention_rows(q, k, v, scale, causal, input_pos, samples, window=0):
 
 
 # ----------------------------------------------------------------------------
-# Form (iii): the tile-by-tile online-softmax algorithm of the cuTile kernel
+# Form (iii): online softmax, one key block at a time
 # ----------------------------------------------------------------------------
 
 def _cdiv(a, b):
     return -(-a // b)
 
 
-def tile_plan(q_tile, tile_m, tile_n, Skv, causal, input_pos):
-    """Loop bound and mask start for one query tile, as the [cuTile] kernel sets them.
+def visible_key_span(vis):
+    """(first, last + 1) of the keys that at least one row of a visibility block sees.
 
-    Part 1 "The main loop over K/V tiles": with causal masking the loop stops
-    at cdiv(min(input_pos + (q_tile + 1) * TILE_M, Skv), TILE_N); tiles past it
-    are fully masked and never visited.  Otherwise it covers cdiv(Skv, TILE_N).
-    Part 2 "K-loop split": tiles before mask_start =
-    min((input_pos + q_tile * TILE_M) // TILE_N, Skv // TILE_N) need no mask.
-
-    Returns (Tc, mask_start).
+    Keys outside this span are masked for every row of the block.  Requires a
+    block in which some row sees some key.
     """
-    if causal:
-        m_end = input_pos + (q_tile + 1) * tile_m
-        tc = _cdiv(min(m_end, Skv), tile_n)
-    else:
-        tc = _cdiv(Skv, tile_n)
-    mask_start = min((input_pos + q_tile * tile_m) // tile_n, Skv // tile_n)
-    return tc, mask_start
+    seen = np.nonzero(vis.any(axis=0))[0]
+    return int(seen[0]), int(seen[-1]) + 1
+
+
+def tile_plan(q_tile, tile_m, tile_n, Skv, causal, input_pos):
+    """Key blocks a query block must visit, and how many leading blocks need no mask.
+
+    Derived from the visibility rule (``key_visibility``) for the rows
+    q_tile*tile_m .. (q_tile+1)*tile_m - 1 (padded rows included, as a kernel
+    computes them):
+      * the latest key any of those rows sees is min(input_pos + last row,
+        Skv - 1) under causal masking, else Skv - 1, so the blocks up to the one
+        holding it are visited and the rest are skipped ([cuTile] Part 1, main
+        loop over K/V tiles; "Causal attention": fully masked tiles are never
+        loaded);
+      * every row sees the keys 0 .. min(input_pos + first row, Skv - 1) under
+        causal masking (all Skv keys otherwise); the whole key blocks inside
+        that common prefix need no mask ([cuTile] Part 2 "K-loop split").
+    Returns (n_visited, n_unmasked); n_unmasked <= n_visited.
+    """
+    first_row = q_tile * tile_m
+    last_row = first_row + tile_m - 1
+    last_key = min(input_pos + last_row, Skv - 1) if causal else Skv - 1
+    common_keys = min(input_pos + first_row, Skv - 1) + 1 if causal else Skv
+    n_visited = last_key // tile_n + 1
+    return n_visited, min(common_keys // tile_n, n_visited)
 
 
 def classify_tiles(Sq, Skv, tile_m, tile_n, causal, input_pos=0):
     """Count (unmasked, masked, skipped) K/V tiles over all query tiles.
 
-    [cuTile] Part 2 "K-loop split": tiles below mask_start run without mask
-    code, tiles from mask_start to the loop bound build the mask, and the rest
-    are skipped.  A tile counts as masked only where the mask is needed, i.e.
-    under causal masking or a ragged key tail.
+    [cuTile] Part 2 "K-loop split": tiles inside every row's visible prefix run
+    without mask code, the other visited tiles build the mask, and the rest
+    are skipped.  Without causal masking and with Skv a whole number of tiles,
+    no tile needs a mask.
     """
     n_q = _cdiv(Sq, tile_m)
     n_k = _cdiv(Skv, tile_n)
-    even_k = Skv % tile_n == 0
     unmasked = masked = 0
     for t in range(n_q):
-        tc, ms = tile_plan(t, tile_m, tile_n, Skv, causal, input_pos)
-        if causal or not even_k:
-            unmasked += min(ms, tc)
-            masked += max(0, tc - ms)
-        else:
-            unmasked += tc
+        visited, free = tile_plan(t, tile_m, tile_n, Skv, causal, input_pos)
+        unmasked += free
+        masked += visited - free
     return unmasked, masked, n_q * n_k - unmasked - masked
+
+
+def _block_state(s, vis, v_blk):
+    """Partial softmax state of one key block: its row maximum, its row sum of
+    exp(s - max) and its un-normalised output, over the visible entries only.
+    A row with no visible entry in the block gets (-inf, 0, 0)."""
+    s = np.where(vis, s, -np.inf)
+    blk_max = s.max(axis=1)
+    ref = np.where(np.isfinite(blk_max), blk_max, 0.0)
+    w = np.exp(s - ref[:, None])
+    return blk_max, w.sum(axis=1), w @ v_blk
+
+
+def _fold(state, part):
+    """Combine two partial softmax states over disjoint key sets ("Understanding
+    online softmax": when the running maximum grows, what was summed so far is
+    scaled by exp(old max - new max)).  -inf maxima carry zero weight."""
+    run_max, run_sum, run_out = state
+    blk_max, blk_sum, blk_out = part
+    new_max = np.maximum(run_max, blk_max)
+    ref = np.where(np.isfinite(new_max), new_max, 0.0)
+    a = np.where(np.isfinite(run_max), np.exp(run_max - ref), 0.0)
+    c = np.where(np.isfinite(blk_max), np.exp(blk_max - ref), 0.0)
+    return new_max, a * run_sum + c * blk_sum, a[:, None] * run_out + c[:, None] * blk_out
 
 
 def attention_online_tiled(q, k, v, scale, causal=False, input_pos=0, tile_m=64, tile_n=64,
                            split_loop=True):
-    """The [cuTile] kernel's tile loop, in float64, one (batch, head, query tile) at a time.
+    """Online softmax over key blocks, in float64, one (batch, head, query block) at a time.
 
-    Steps, in the page's order and notation (Part 1):
-      * "Block ID mapping": kv head = head // QUERY_GROUP_SIZE.
-      * "Initializing accumulators": qk_scale = scale / ln 2; offs_m = tile
-        rows + input_pos; m_i = -inf, l_i = 0, acc = 0.
-      * "Loading the query tile": rows past Sq are padded with zeros and
-        dropped at the store.
-      * "The main loop over K/V tiles": Tc from ``tile_plan``; qk = q k^T.
-      * "Applying the causal mask" / Part 2 "K-loop split": on tiles j >=
-        mask_start (every tile when ``split_loop`` is False), keys past Skv
-        and, under causal masking, keys with offs_n > offs_m get -inf.
-      * "Online softmax update": m_ij = max(m_i, rowmax(qk) * qk_scale);
-        p = exp2(qk * qk_scale - m_ij); alpha = exp2(m_i - m_ij);
-        l_i = l_i * alpha + rowsum(p); acc = acc * alpha.
-      * "Accumulating the output": acc += p V; m_i = m_ij.
-      * "Final normalization and store": O = acc / l_i.
-    The log-sum-exp (on no page) is ln 2 * (m_i + log2 l_i) from the same state.
-    p is not rounded to the input type here: the oracle stays in float64.
+    The algorithm of [cuTile] "How Flash Attention solves the memory bandwidth
+    problem" and "Understanding online softmax": a query block keeps a running
+    (maximum, sum, un-normalised output) and folds in one key block after
+    another; only at the end is the output divided by the sum and the
+    log-sum-exp formed (Part 1, final normalisation).  The key blocks visited
+    and the ones that need no mask come from ``tile_plan``: blocks past the
+    last visible key are never touched, and with ``split_loop`` the blocks
+    every row sees in full are folded without consulting the mask (Part 2
+    "K-loop split"); with ``split_loop`` False every block is masked.  Rows past
+    Sq are not formed; keys past Skv do not exist.  The log-sum-exp (on no page)
+    is max + ln(sum).  The GQA head map is ``kv_head_of``.
     Returns (O [B,Hq,Sq,D], LSE [B,Hq,Sq]).
     """
     B, Hq, Hkv, Sq, Skv, D = _shapes(q, k, v)
     if not (math.isfinite(scale) and scale > 0):
         raise ValueError("scale must be finite and > 0")
-    group = Hq // Hkv
-    qk_scale = scale * LOG2E
-    even_k = Skv % tile_n == 0
     O = np.empty((B, Hq, Sq, D))
     L = np.empty((B, Hq, Sq))
     for b in range(B):
-        for head in range(Hq):
-            off_kv_h = head // group
-            kh = np.asarray(k[b, off_kv_h], np.float64)
-            vh = np.asarray(v[b, off_kv_h], np.float64)
-            for bid_x in range(_cdiv(Sq, tile_m)):
-                rows = bid_x * tile_m + np.arange(tile_m)
-                valid = rows < Sq
-                qt = np.zeros((tile_m, D))
-                qt[valid] = np.asarray(q[b, head, rows[valid]], np.float64)
-                offs_m = (rows + input_pos)[:, None]
-                m_i = np.full(tile_m, -np.inf)
-                l_i = np.zeros(tile_m)
-                acc = np.zeros((tile_m, D))
-                tc, mask_start = tile_plan(bid_x, tile_m, tile_n, Skv, causal, input_pos)
-                for j in range(tc):
-                    cols = j * tile_n + np.arange(tile_n)
-                    in_k = cols < Skv
-                    kt = np.zeros((tile_n, D))
-                    vt = np.zeros((tile_n, D))
-                    kt[in_k] = kh[cols[in_k]]
-                    vt[in_k] = vh[cols[in_k]]
-                    qk = qt @ kt.T
-                    if (causal or not even_k) and (j >= mask_start or not split_loop):
-                        mask = np.ones((tile_m, tile_n), dtype=bool)
-                        if not even_k:
-                            mask &= in_k[None, :]
-                        if causal:
-                            mask &= offs_m >= cols[None, :]
-                        qk = qk + np.where(mask, 0.0, -np.inf)
-                    qk_max = qk.max(axis=1)
-                    m_ij = np.maximum(m_i, qk_max * qk_scale)
-                    p = np.exp2(qk * qk_scale - m_ij[:, None])
-                    l_ij = p.sum(axis=1)
-                    alpha = np.exp2(m_i - m_ij)
-                    l_i = l_i * alpha + l_ij
-                    acc = acc * alpha[:, None] + p @ vt
-                    m_i = m_ij
-                out = acc / l_i[:, None]
-                lse = (m_i + np.log2(l_i)) * LN2
-                O[b, head, rows[valid]] = out[valid]
-                L[b, head, rows[valid]] = lse[valid]
+        for hq in range(Hq):
+            g = kv_head_of(hq, Hq, Hkv)
+            kh = np.asarray(k[b, g], np.float64)
+            vh = np.asarray(v[b, g], np.float64)
+            for qt in range(_cdiv(Sq, tile_m)):
+                r0, r1 = qt * tile_m, min(Sq, (qt + 1) * tile_m)
+                q_blk = np.asarray(q[b, hq, r0:r1], np.float64)
+                n = r1 - r0
+                state = (np.full(n, -np.inf), np.zeros(n), np.zeros((n, D)))
+                n_visited, n_free = tile_plan(qt, tile_m, tile_n, Skv, causal, input_pos)
+                for kt in range(n_visited):
+                    c0, c1 = kt * tile_n, min(Skv, (kt + 1) * tile_n)
+                    s = scaled_scores(q_blk, kh[c0:c1], scale)
+                    if split_loop and kt < n_free:
+                        vis = np.ones(s.shape, dtype=bool)
+                    else:
+                        vis = key_visibility(np.arange(r0, r1), Skv, causal, input_pos)[:, c0:c1]
+                    state = _fold(state, _block_state(s, vis, vh[c0:c1]))
+                run_max, run_sum, run_out = state
+                O[b, hq, r0:r1] = run_out / run_sum[:, None]
+                L[b, hq, r0:r1] = run_max + np.log(run_sum)
     return O, L
 
 

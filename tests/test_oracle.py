@@ -60,7 +60,8 @@ def test_rows_form_equals_blocked():
 
 
 def test_tile_plan_against_brute_force():
-    """Tc and mask_start bound exactly the visible / mask-free tiles (any tiling)."""
+    """The visited and mask-free block counts bound exactly the visible / fully visible
+    key blocks (any tiling)."""
     rng = np.random.default_rng(0)
     for _ in range(400):
         tm, tn = int(rng.integers(1, 70)), int(rng.integers(1, 70))
@@ -152,23 +153,64 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
 
 
 TILED_MUTANTS = {
-    "mask_start_plus_one": lambda t, tm, tn, Skv, c, pos: (
-        oa_tile_plan(t, tm, tn, Skv, c, pos)[0], oa_tile_plan(t, tm, tn, Skv, c, pos)[1] + 1),
-    "loop_bound_minus_one": lambda t, tm, tn, Skv, c, pos: (
-        max(1, oa_tile_plan(t, tm, tn, Skv, c, pos)[0] - 1), oa_tile_plan(t, tm, tn, Skv, c, pos)[1]),
-    "loop_bound_ignores_input_pos": lambda t, tm, tn, Skv, c, pos: (
-        oa_tile_plan(t, tm, tn, Skv, c, 0)[0], oa_tile_plan(t, tm, tn, Skv, c, pos)[1]),
+    # the last visited key block dropped
+    "one_block_short": ("tile_plan", lambda t, tm, tn, Skv, c, pos: (
+        max(1, _tile_plan(t, tm, tn, Skv, c, pos)[0] - 1), _tile_plan(t, tm, tn, Skv, c, pos)[1])),
+    # one more block folded without its mask
+    "unmasked_block_too_many": ("tile_plan", lambda t, tm, tn, Skv, c, pos: (
+        _tile_plan(t, tm, tn, Skv, c, pos)[0],
+        min(_tile_plan(t, tm, tn, Skv, c, pos)[1] + 1, _tile_plan(t, tm, tn, Skv, c, pos)[0]))),
+    # visited blocks computed without the query offset
+    "plan_ignores_input_pos": ("tile_plan", lambda t, tm, tn, Skv, c, pos: (
+        _tile_plan(t, tm, tn, Skv, c, 0)[0], _tile_plan(t, tm, tn, Skv, c, 0)[1])),
+    # the running state not rescaled when the maximum grows
+    "fold_without_rescale": ("_fold", lambda st, pt: (
+        np.maximum(st[0], pt[0]), st[1] + pt[1], st[2] + pt[2])),
+    # the block's weights taken relative to zero instead of its own maximum
+    "block_not_shifted": ("_block_state", lambda s, vis, vb: (
+        np.where(vis, s, -np.inf).max(axis=1),
+        np.exp(np.where(vis, s, -np.inf)).sum(axis=1), np.exp(np.where(vis, s, -np.inf)) @ vb)),
 }
-oa_tile_plan = oa.tile_plan
+_tile_plan = oa.tile_plan
 
 
 @pytest.mark.parametrize("name", sorted(TILED_MUTANTS))
 def test_online_pin_catches_planted_tiling_mistake(name, monkeypatch):
-    monkeypatch.setattr(oa, "tile_plan", TILED_MUTANTS[name])
+    attr, fn = TILED_MUTANTS[name]
+    monkeypatch.setattr(oa, attr, fn)
     q, k, v = pins.tiny_case(1, 2, 1, 100, 130, 64, 4)
-    O1, _ = oracle.attention_blocked(q, k, v, 0.125, True, 30)
-    O2, _ = oa.attention_online_tiled(q, k, v, 0.125, True, 30, 32, 16)
-    assert np.max(np.abs(O1 - O2)) > 1e-6
+    O1, L1 = oracle.attention_blocked(q, k, v, 0.125, True, 30)
+    O2, L2 = oa.attention_online_tiled(q, k, v, 0.125, True, 30, 32, 16)
+    assert max(np.max(np.abs(O1 - O2)), np.max(np.abs(L1 - L2))) > 1e-6
+
+
+# --- the key span that attention_blocked reads for a block of rows ----------------------
+
+SPAN_MUTANTS = {
+    "span_end_short": lambda vis: (oa_span(vis)[0], oa_span(vis)[1] - 1),
+    "span_start_late": lambda vis: (min(oa_span(vis)[0] + 1, oa_span(vis)[1] - 1), oa_span(vis)[1]),
+}
+oa_span = oa.visible_key_span
+
+
+@pytest.mark.parametrize("rows_per_block", [1, 5, 16])
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_blocked_oracle_pins_many_blocks(pin, rows_per_block):
+    """The pins again with several row blocks per head, each block reading only its own
+    visible key span."""
+    pin(functools.partial(oracle.attention_blocked, rows_per_block=rows_per_block))
+
+
+@pytest.mark.parametrize("name", sorted(SPAN_MUTANTS))
+def test_pins_catch_planted_span_mistake(name, monkeypatch):
+    monkeypatch.setattr(oa, "visible_key_span", SPAN_MUTANTS[name])
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(functools.partial(oa.attention_blocked, rows_per_block=5))
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"planted mistake {name} was not caught by any pin"
 
 
 def test_scale_rejected():
