@@ -35,6 +35,15 @@ WORKLOADS = {
     "gqa8_swa4096_causal_s16384_d128_bf16": dict(B=1, Hq=32, Hkv=4, Sq=16384, Skv=16384, D=128,
                                                   dtype="bf16", causal=True, input_pos=0,
                                                   window=4096),
+    # Head dim 64 ("TiledAttention" Table 5 shape family) at sizes whose grids fill the GPU,
+    # so the dispatch takes the eight-wave head-dim-64 workgroups: 8 positions x 1 head
+    # (MHA), 2 positions x 4 heads (GQA 4) and 4 positions x 2 heads (GQA 2).
+    "mha_causal_s4096_d64_fp16": dict(B=1, Hq=32, Hkv=32, Sq=4096, Skv=4096, D=64,
+                                      dtype="fp16", causal=True, input_pos=0),
+    "gqa4_causal_s4096_d64_bf16": dict(B=1, Hq=32, Hkv=8, Sq=4096, Skv=4096, D=64,
+                                       dtype="bf16", causal=True, input_pos=0),
+    "gqa2_s2048_d64_fp16": dict(B=1, Hq=32, Hkv=16, Sq=2048, Skv=2048, D=64, dtype="fp16",
+                                causal=False, input_pos=0),
     # One new token per sequence against a 16K-token cache: the under-filled grid that
     # split-KV is for (32 workgroups unsplit).
     "gqa4_decode_b4_kv16384_d128_bf16": dict(B=4, Hq=32, Hkv=8, Sq=1, Skv=16384, D=128,

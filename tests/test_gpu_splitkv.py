@@ -94,22 +94,23 @@ def test_split_shapes(case, dtype):
         check_full(q, k, v, scale, causal, pos, out, lse, f"{shape} {dtype} splits={s}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_every_config_split(dtype, causal):
+def test_every_config_split(D, dtype, causal):
     """Every compiled configuration that fits the call, with 3 ranges."""
-    q, k, v = make_qkv(1, 16, 2, 333, 333, 128, dtype, seed=9)   # GQA 8: every shape applies
+    q, k, v = make_qkv(1, 16, 2, 333, 333, D, dtype, seed=9)   # GQA 8: every shape applies
     pos = 7 if causal else 0
     tested = 0
     for cid, name in enumerate(fa.config_names()):
-        if not name.startswith("D128_") or "_fp8qk_" in name or (("_causal_" in name) != causal) or \
+        if not name.startswith(f"D{D}_") or "_fp8qk_" in name or (("_causal_" in name) != causal) or \
                 (("_bf16" in name) != (dtype == "bf16")):
             continue
         _say("config", name)
         out, lse = run_split(q, k, v, 0.09, causal, pos, 3, config=cid)
         check_full(q, k, v, 0.09, causal, pos, out, lse, name)
         tested += 1
-    assert tested >= 3
+    assert tested == (7 if D == 128 else 6)
 
 
 def test_one_split_is_the_plain_kernel():

@@ -82,19 +82,20 @@ def test_window_shapes(case, dtype):
     check(q, k, v, scale, pos, W, out, lse, f"{case} {dtype}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
-def test_window_every_config(dtype):
-    q, k, v = make_qkv(1, 16, 2, 333, 400, 128, dtype, seed=12)   # GQA 8: every shape applies
+def test_window_every_config(D, dtype):
+    q, k, v = make_qkv(1, 16, 2, 333, 400, D, dtype, seed=12)   # GQA 8: every shape applies
     tested = 0
     for cid, name in enumerate(fa.config_names()):
-        if not name.startswith("D128_") or "_fp8qk_" in name or "_causal_" not in name or \
+        if not name.startswith(f"D{D}_") or "_fp8qk_" in name or "_causal_" not in name or \
                 (("_bf16" in name) != (dtype == "bf16")):
             continue
         _say("config", name)
         out, lse = run_window(q, k, v, 0.09, 50, 90, config=cid)
         check(q, k, v, 0.09, 50, 90, out, lse, name)
         tested += 1
-    assert tested >= 3
+    assert tested == (7 if D == 128 else 6)
 
 
 def test_window_wide_equals_causal_bitwise():
