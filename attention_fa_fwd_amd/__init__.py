@@ -17,6 +17,7 @@ import threading
 __all__ = ["fa_fwd", "fa_fwd_into", "fa_bwd", "fa_bwd_into", "bwd_workspace_size", "fa_fwd_fp8",
            "fa_fwd_fp8_into", "select_config_fp8", "fa_fwd_splitkv_fp8", "fa_fwd_splitkv_fp8_into",
            "splitkv_num_splits_fp8", "fa_fwd_splitkv", "fa_fwd_splitkv_into", "splitkv_num_splits",
+           "fa_fwd_splitkv_noalloc", "fa_fwd_splitkv_noalloc_into", "NOALLOC_SCRATCH_BYTES",
            "splitkv_workspace_size", "select_config", "config_names", "num_configs", "FaError",
            "load_library", "LIB_PATH"]
 
@@ -24,6 +25,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_fwd.s
 
 FA_DTYPE_FP16 = 0
 FA_DTYPE_BF16 = 1
+# Size of the fixed split-KV scratch of fa_fwd_splitkv_noalloc (FA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 _lock = threading.Lock()
@@ -61,6 +64,8 @@ def _declare(lib):
     lib.fa_fwd_splitkv.argtypes = _FWD_ARGS[:14] + [_c_int, _c_int, _c_int, _c_int, _vp,
                                                     ctypes.c_size_t, _vp]
     lib.fa_fwd_splitkv.restype = _c_int
+    lib.fa_fwd_splitkv_noalloc.argtypes = _FWD_ARGS[:14] + [_c_int, _c_int, _c_int, _c_int, _vp]
+    lib.fa_fwd_splitkv_noalloc.restype = _c_int
     lib.fa_fwd_splitkv_fp8.argtypes = _FWD_ARGS[:12] + [_c_float, _c_float] + [_c_int] * 6 + [
         _vp, ctypes.c_size_t, _vp]
     lib.fa_fwd_splitkv_fp8.restype = _c_int
@@ -244,6 +249,43 @@ def fa_fwd_splitkv(q, k, v, scale=None, causal=True, input_pos=0, num_splits=0, 
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     return fa_fwd_splitkv_into(q, k, v, out, lse, ws, num_splits=num_splits, scale=scale,
                                causal=causal, input_pos=input_pos, config=config, window=window)
+
+
+def fa_fwd_splitkv_noalloc_into(q, k, v, out, lse, num_splits=0, scale=None, causal=True,
+                                input_pos=0, config=-1, stream=None, window=0):
+    """Split-KV forward into caller-provided ``out`` and ``lse`` with no workspace: the
+    partials live in the library's fixed scratch (``NOALLOC_SCRATCH_BYTES`` per GPU), so
+    the call allocates nothing.  Calls that overlap in time on one GPU share that scratch
+    and must not run concurrently."""
+    import torch
+
+    lib = load_library()
+    B, Hq, Hkv, Sq, Skv, D = _check_tensors(q, k, v, out, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        rc = lib.fa_fwd_splitkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                        lse.data_ptr(), B, Hq, Hkv, Sq, Skv, D, float(scale),
+                                        1 if causal else 0, int(input_pos), int(window),
+                                        _dtype_code(q.dtype), int(num_splits), int(config), stream)
+    _check(rc)
+    return out, lse
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, scale=None, causal=True, input_pos=0, num_splits=0, config=-1,
+                           window=0):
+    """``fa_fwd_splitkv`` without a workspace (the library's fixed scratch holds the
+    partials); allocates only ``out`` and ``lse``.  Returns (out, lse)."""
+    import torch
+
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    return fa_fwd_splitkv_noalloc_into(q, k, v, out, lse, num_splits=num_splits, scale=scale,
+                                       causal=causal, input_pos=input_pos, config=config,
+                                       window=window)
 
 
 def fa_fwd(q, k, v, scale=None, causal=True, input_pos=0, config=-1, window=0):

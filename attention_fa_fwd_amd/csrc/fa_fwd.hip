@@ -10,10 +10,12 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "fa_fwd.h"
 #include "fa_configs.h"
@@ -323,6 +325,61 @@ int run_splitkv(const Call& a, int num_splits, int config, void* workspace,
     return launch(a, config, num_splits, workspace, stream);
 }
 
+// --- Scratch of fa_fwd_splitkv_noalloc --------------------------------------------------
+// The split-KV partials of callers that cannot allocate device memory live in this array.
+// Each GPU the library runs on holds its own copy, at its own address, until the process
+// ends.  In host code `scratch` names a host-side stand-in, never the device memory: the
+// address of a device's copy is looked up once per device (hipGetSymbolAddress, with that
+// device current) and only that address is passed to kernels.
+constexpr size_t kScratchBytes = (size_t)FA_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's copy of `scratch`.
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return FA_ERR_LAUNCH;
+    }
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (ptr == nullptr) {
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+                (void)hipGetLastError();
+                return FA_ERR_LAUNCH;
+            }
+            g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return FA_OK;
+}
+
+// fa_fwd_splitkv with the partials in `scratch` instead of a caller's workspace.
+int run_splitkv_noalloc(const Call& a, int num_splits, int config, void* stream) {
+    int rc = validate(a);
+    if (rc != FA_OK) return rc;
+    config = resolve_config(config, a);
+    if (config < 0) return config;
+    if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_INVALID_SPLITS;
+    if (num_splits == 0) num_splits = auto_splits(kConfigs[config], a);
+    if ((long long)a.B * a.Hq * a.Sq == 0) return FA_OK;
+    void* ws = nullptr;
+    if (num_splits > 1) {
+        if (workspace_bytes_for(a.B, a.Hq, a.Sq, a.D, num_splits) > kScratchBytes)
+            return FA_ERR_SCRATCH;
+        rc = scratch_address(&ws);
+        if (rc != FA_OK) return rc;
+    }
+    return launch(a, config, num_splits, ws, stream);
+}
+
 Call make_call(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
                int Hkv, int Sq, int Skv, int D, float scale, int causal, int input_pos,
                int window, int dtype) {
@@ -397,6 +454,15 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float
     return run_splitkv(make_call(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal,
                                  input_pos, window, dtype),
                        num_splits, config, workspace, workspace_bytes, stream);
+}
+
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                           int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+                           int causal, int input_pos, int window, int dtype, int num_splits,
+                           int config, void* stream) {
+    return run_splitkv_noalloc(make_call(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale,
+                                         causal, input_pos, window, dtype),
+                               num_splits, config, stream);
 }
 
 int fa_fwd_splitkv_fp8(const void* q, const void* k, const void* v, void* out, float* lse, int B,
@@ -490,6 +556,7 @@ const char* fa_strerror(int code) {
         case FA_ERR_INVALID_SPLITS: return "num_splits must be in 0..256";
         case FA_ERR_WORKSPACE: return "workspace smaller than fa_splitkv_workspace_size() / fa_bwd_workspace_size()";
         case FA_ERR_INVALID_WINDOW: return "window must be >= 0, needs causal masking, and >= 1 for fa_fwd_window";
+        case FA_ERR_SCRATCH: return "split-KV partials larger than the fixed scratch of fa_fwd_splitkv_noalloc (FA_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status code";
     }
 }

@@ -65,8 +65,9 @@ enum fa_status {
     FA_ERR_LAUNCH = -11,              /* the kernel launch failed (hipGetLastError)           */
     FA_ERR_INVALID_SPLITS = -12,      /* fa_fwd_splitkv: num_splits outside 0..256            */
     FA_ERR_WORKSPACE = -13,           /* fa_fwd_splitkv, fa_bwd: workspace_bytes too small    */
-    FA_ERR_INVALID_WINDOW = -14       /* window < 0, window > 0 without causal masking, or    */
+    FA_ERR_INVALID_WINDOW = -14,      /* window < 0, window > 0 without causal masking, or    */
                                       /* fa_fwd_window with window < 1                        */
+    FA_ERR_SCRATCH = -15              /* fa_fwd_splitkv_noalloc: partials exceed its scratch  */
 };
 
 /*
@@ -205,6 +206,31 @@ int fa_fwd_splitkv_fp8(const void* q, const void* k, const void* v, void* out, f
  * fa_splitkv_num_splits, with 3 bytes per K/V element), or a negative fa_status. */
 int fa_splitkv_num_splits_fp8(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
                               int input_pos, int window, int v_dtype, int config);
+
+/*
+ * fa_fwd_splitkv without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The split-KV partials live in a fixed scratch array inside the library, one
+ * copy per GPU, FA_NOALLOC_SCRATCH_BYTES bytes, held by each GPU the library runs on until
+ * the process ends.  The call itself allocates nothing: no hipMalloc, no hipFree.
+ *
+ *   q .. config, stream   as for fa_fwd_splitkv; the kernels run on the current device,
+ *                         which `stream` must belong to.
+ * Checks: those of fa_fwd_splitkv up to num_splits; then, only when more than one split
+ * runs and B*Hq*Sq > 0, fa_splitkv_workspace_size(B, Hq, Sq, D, splits) >
+ * FA_NOALLOC_SCRATCH_BYTES returns FA_ERR_SCRATCH.  The first call on a device that runs
+ * more than one split looks up that device's copy of the array (hipGetSymbolAddress; a
+ * failure returns FA_ERR_LAUNCH): make that first call outside graph capture.
+ * Every call on one GPU shares that GPU's array and leaves its partials there: calls that
+ * overlap in time on one GPU (two streams, two threads) race and may return wrong results;
+ * serialise them, or use fa_fwd_splitkv with a workspace each.  Nothing in the array needs
+ * to start at zero: every partial the merge reads is written by the same call.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                           int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+                           int causal, int input_pos, int window, int dtype, int num_splits,
+                           int config, void* stream);
 
 /* Workspace bytes fa_fwd_splitkv needs for num_splits ranges:
  * num_splits * B * Hq * Sq * (D + 1) * 4 (fp32 partial O, then fp32 partial LSE), 0 when

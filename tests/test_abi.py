@@ -210,6 +210,40 @@ def test_splitkv_validation_order_and_noops(lib):
     assert call_split(lib, ws_bytes=need - 1) == -13
 
 
+def call_noalloc(lib, num_splits=2, config=-1, window=0, **over):
+    a = dict(GOOD, **over)
+    return lib.fa_fwd_splitkv_noalloc(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"],
+                                      a["Hkv"], a["Sq"], a["Skv"], a["D"], a["scale"], a["causal"],
+                                      a["input_pos"], window, a["dtype"], num_splits, config, None)
+
+
+def test_noalloc_scratch_size_header_and_binding():
+    text = open(HEADER).read()
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_validation(lib):
+    """The workspace-free split-KV entry point checks what fa_fwd_splitkv checks, in the same
+    order, and then that the partials fit its fixed scratch -- all before any HIP call."""
+    assert call_noalloc(lib, q=0) == -1
+    assert call_noalloc(lib, Hq=3) == -3
+    assert call_noalloc(lib, D=96) == -4
+    assert call_noalloc(lib, scale=0.0) == -6
+    assert call_noalloc(lib, out=Q) == -9
+    assert call_noalloc(lib, config=10 ** 6) == -10
+    assert call_noalloc(lib, num_splits=-1) == -12 and call_noalloc(lib, num_splits=257) == -12
+    assert call_noalloc(lib, window=4, causal=0) == -14
+    assert call_noalloc(lib, Sq=0) == 0 and call_noalloc(lib, B=0, num_splits=0) == 0
+    # B=1, Hq=32, Sq=4096, D=128 at 2 splits needs 135 MB of partials: over the 64 MiB scratch
+    big = dict(B=1, Hq=32, Hkv=32, Sq=4096, Skv=4096, D=128)
+    need = fa.splitkv_workspace_size(1, 32, 4096, 128, 2)
+    assert need > fa.NOALLOC_SCRATCH_BYTES
+    assert call_noalloc(lib, num_splits=2, **big) == -15
+    assert call_noalloc(lib, num_splits=256, B=1, Hq=8, Hkv=8, Sq=64, Skv=4096, D=128) == -15
+    assert b"scratch" in lib.fa_strerror(-15)
+
+
 # --- sliding window ------------------------------------------------------------------
 
 def test_window_validation(lib):
