@@ -18,6 +18,8 @@ __all__ = ["fa_fwd", "fa_fwd_into", "fa_bwd", "fa_bwd_into", "bwd_workspace_size
            "fa_fwd_fp8_into", "select_config_fp8", "fa_fwd_splitkv_fp8", "fa_fwd_splitkv_fp8_into",
            "splitkv_num_splits_fp8", "fa_fwd_splitkv", "fa_fwd_splitkv_into", "splitkv_num_splits",
            "fa_fwd_splitkv_noalloc", "fa_fwd_splitkv_noalloc_into", "NOALLOC_SCRATCH_BYTES",
+           "fa_fwd_fp8qkv", "fa_fwd_fp8qkv_into", "fa_fwd_splitkv_fp8qkv", "fa_fwd_splitkv_fp8qkv_into",
+           "splitkv_num_splits_fp8qkv",
            "splitkv_workspace_size", "select_config", "config_names", "num_configs", "FaError",
            "load_library", "LIB_PATH"]
 
@@ -64,6 +66,13 @@ def _declare(lib):
     lib.fa_fwd_splitkv.argtypes = _FWD_ARGS[:14] + [_c_int, _c_int, _c_int, _c_int, _vp,
                                                     ctypes.c_size_t, _vp]
     lib.fa_fwd_splitkv.restype = _c_int
+    lib.fa_fwd_fp8qkv.argtypes = _FWD_ARGS[:12] + [_c_float] * 3 + [_c_int] * 4 + [_vp, _c_int]
+    lib.fa_fwd_fp8qkv.restype = _c_int
+    lib.fa_fwd_splitkv_fp8qkv.argtypes = _FWD_ARGS[:12] + [_c_float] * 3 + [_c_int] * 6 + [
+        _vp, ctypes.c_size_t, _vp]
+    lib.fa_fwd_splitkv_fp8qkv.restype = _c_int
+    lib.fa_splitkv_num_splits_fp8qkv.argtypes = [_c_int] * 11
+    lib.fa_splitkv_num_splits_fp8qkv.restype = _c_int
     lib.fa_fwd_splitkv_noalloc.argtypes = _FWD_ARGS[:14] + [_c_int, _c_int, _c_int, _c_int, _vp]
     lib.fa_fwd_splitkv_noalloc.restype = _c_int
     lib.fa_fwd_splitkv_fp8.argtypes = _FWD_ARGS[:12] + [_c_float, _c_float] + [_c_int] * 6 + [
@@ -443,6 +452,133 @@ def fa_fwd_splitkv_fp8(q8, k8, v, q_descale, k_descale, scale=None, causal=True,
     return fa_fwd_splitkv_fp8_into(q8, k8, v, out, lse, ws, q_descale, k_descale,
                                    num_splits=num_splits, scale=scale, causal=causal,
                                    input_pos=input_pos, window=window, config=config)
+
+
+def _check_fp8qkv_tensors(q8, k8, v8, out, lse):
+    """Checks of the fp8 Q/K/V entry points: q8, k8, v8 float8_e4m3fn; out fp16 / bf16;
+    lse fp32; all contiguous on one GPU.  Returns (B, Hq, Hkv, Sq, Skv, D)."""
+    import torch
+
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8), ("out", out), ("lse", lse)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != q8.device:
+            raise ValueError(f"{name} is on {t.device}, q8 on {q8.device}")
+    if any(t.dtype != torch.float8_e4m3fn for t in (q8, k8, v8)):
+        raise TypeError("q8, k8 and v8 must be torch.float8_e4m3fn")
+    if out.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("out must be float16 or bfloat16")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    B, Hq, Sq, D = q8.shape
+    Bk, Hkv, Skv, Dk = k8.shape
+    if tuple(v8.shape) != tuple(k8.shape) or Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch q{tuple(q8.shape)} k{tuple(k8.shape)} v{tuple(v8.shape)}")
+    if tuple(out.shape) != tuple(q8.shape) or tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("out must be [B, Hq, Sq, D] and lse [B, Hq, Sq]")
+    return B, Hq, Hkv, Sq, Skv, D
+
+
+def fa_fwd_fp8qkv_into(q8, k8, v8, out, lse, q_descale, k_descale, v_descale, scale=None,
+                       causal=True, input_pos=0, window=0, config=-1, stream=None):
+    """fp8 E4M3 q8, k8, v8 (torch.float8_e4m3fn) with per-tensor descale factors into
+    caller-provided out (fp16 / bf16) and lse fp32 (fa_fwd_fp8qkv)."""
+    import torch
+
+    lib = load_library()
+    B, Hq, Hkv, Sq, Skv, D = _check_fp8qkv_tensors(q8, k8, v8, out, lse)
+    _check_window(causal, window)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q8.device).cuda_stream
+    with torch.cuda.device(q8.device):
+        rc = lib.fa_fwd_fp8qkv(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), B, Hq, Hkv, Sq, Skv, D, float(scale),
+                               float(q_descale), float(k_descale), float(v_descale),
+                               1 if causal else 0, int(input_pos), int(window),
+                               _dtype_code(out.dtype), stream, int(config))
+    _check(rc)
+    return out, lse
+
+
+def fa_fwd_fp8qkv(q8, k8, v8, q_descale, k_descale, v_descale, out_dtype=None, scale=None,
+                  causal=True, input_pos=0, window=0, config=-1):
+    """Attention with fp8 E4M3 queries, keys and values (real values descale * codes):
+    returns (out in out_dtype, default bfloat16; lse fp32)."""
+    import torch
+
+    q8, k8, v8 = q8.contiguous(), k8.contiguous(), v8.contiguous()
+    out = torch.empty(q8.shape, dtype=out_dtype or torch.bfloat16, device=q8.device)
+    lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=q8.device)
+    return fa_fwd_fp8qkv_into(q8, k8, v8, out, lse, q_descale, k_descale, v_descale, scale=scale,
+                              causal=causal, input_pos=input_pos, window=window, config=config)
+
+
+def splitkv_num_splits_fp8qkv(B, Hq, Hkv, Sq, Skv, D, causal, input_pos, out_dtype, config=-1,
+                              window=0) -> int:
+    """Split count fa_fwd_splitkv_fp8qkv picks for num_splits=0."""
+    code = out_dtype if isinstance(out_dtype, int) else _dtype_code(out_dtype)
+    rc = load_library().fa_splitkv_num_splits_fp8qkv(B, Hq, Hkv, Sq, Skv, D, 1 if causal else 0,
+                                                     int(input_pos), int(window), code,
+                                                     int(config))
+    _check(rc if rc < 0 else 0)
+    return rc
+
+
+def fa_fwd_splitkv_fp8qkv_into(q8, k8, v8, out, lse, workspace, q_descale, k_descale, v_descale,
+                               num_splits=0, scale=None, causal=True, input_pos=0, window=0,
+                               config=-1, stream=None):
+    """Split-KV forward with fp8 E4M3 q8, k8, v8 into caller-provided out, lse and workspace
+    (``splitkv_workspace_size`` bytes; None when one split runs)."""
+    import torch
+
+    lib = load_library()
+    B, Hq, Hkv, Sq, Skv, D = _check_fp8qkv_tensors(q8, k8, v8, out, lse)
+    _check_window(causal, window)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q8.device).cuda_stream
+    if workspace is not None:
+        if not workspace.is_cuda or workspace.device != q8.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on q8's device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    else:
+        ws_ptr, ws_bytes = None, 0
+    with torch.cuda.device(q8.device):
+        rc = lib.fa_fwd_splitkv_fp8qkv(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(),
+                                       out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Sq, Skv, D,
+                                       float(scale), float(q_descale), float(k_descale),
+                                       float(v_descale), 1 if causal else 0, int(input_pos),
+                                       int(window), _dtype_code(out.dtype), int(num_splits),
+                                       int(config), ws_ptr, ws_bytes, stream)
+    _check(rc)
+    return out, lse
+
+
+def fa_fwd_splitkv_fp8qkv(q8, k8, v8, q_descale, k_descale, v_descale, out_dtype=None, scale=None,
+                          causal=True, input_pos=0, num_splits=0, window=0, config=-1):
+    """Split-KV attention with fp8 E4M3 queries, keys and values; allocates out, lse and the
+    workspace with torch."""
+    import torch
+
+    q8, k8, v8 = q8.contiguous(), k8.contiguous(), v8.contiguous()
+    B, Hq, Sq, D = q8.shape
+    Hkv, Skv = k8.shape[1], k8.shape[2]
+    dt = out_dtype or torch.bfloat16
+    if num_splits == 0:
+        num_splits = splitkv_num_splits_fp8qkv(B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dt,
+                                               config, window)
+    out = torch.empty(q8.shape, dtype=dt, device=q8.device)
+    lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=q8.device)
+    nbytes = splitkv_workspace_size(B, Hq, Sq, D, num_splits)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q8.device) if nbytes else None
+    return fa_fwd_splitkv_fp8qkv_into(q8, k8, v8, out, lse, ws, q_descale, k_descale, v_descale,
+                                      num_splits=num_splits, scale=scale, causal=causal,
+                                      input_pos=input_pos, window=window, config=config)
 
 
 def select_config_fp8(B, Hq, Hkv, Sq, D, causal, v_dtype) -> int:

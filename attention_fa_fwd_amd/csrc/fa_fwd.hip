@@ -32,16 +32,16 @@ typedef hipError_t (*LaunchFn)(const Params&, hipStream_t);
 
 struct ConfigEntry {
     const char* name;
-    int D, bf16, causal, qk8;
+    int D, bf16, causal, qk8, v8;
     int BN, QB, WPH, HPW;
     LaunchFn launch;
 };
 
-#define FA_TABLE_ENTRY(D, BN, QB, WPH, HPW, C, B, Q, CNAME, TNAME)                            \
+#define FA_TABLE_ENTRY(D, BN, QB, WPH, HPW, C, B, Q, V8, CNAME, TNAME)                        \
     ConfigEntry{"D" FA_STR(D) "_BN" FA_STR(BN) "_Mw" FA_STR(QB) "x32_WPH" FA_STR(WPH)        \
                 "_HPW" FA_STR(HPW) "_" CNAME "_" TNAME,                                        \
-                D, B, C, Q, BN, QB, WPH, HPW,                                                   \
-                &fa_host::launch_cfg<Cfg<D, BN, QB, WPH, HPW, C, B, Q>>},
+                D, B, C, Q, V8, BN, QB, WPH, HPW,                                               \
+                &fa_host::launch_cfg<Cfg<D, BN, QB, WPH, HPW, C, B, Q, V8>>},
 #define FA_STR2(x) #x
 #define FA_STR(x) FA_STR2(x)
 
@@ -73,8 +73,9 @@ bool overlaps(uintptr_t a, size_t na, uintptr_t b, size_t nb) {
     return a < b + nb && b < a + na;
 }
 
-// One call's arguments.  dtype is the element type of v and out (and of q, k unless
-// qk8); qk8: q and k are fp8 e4m3 with per-tensor dequantisation factors.
+// One call's arguments.  dtype is the element type of out (and of v unless v8, of q, k
+// unless qk8); qk8: q and k are fp8 e4m3 with per-tensor dequantisation factors; v8: v
+// too.
 struct Call {
     const void* q;
     const void* k;
@@ -84,8 +85,8 @@ struct Call {
     int B, Hq, Hkv, Sq, Skv, D;
     float scale;
     int causal, input_pos, window, dtype;
-    int qk8;
-    float q_descale, k_descale;
+    int qk8, v8;
+    float q_descale, k_descale, v_descale;
 };
 
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
@@ -111,6 +112,7 @@ int validate(const Call& a) {
     if (!finite_pos(a.scale)) return FA_ERR_INVALID_SCALE;
     if (a.qk8 && (!finite_pos(a.q_descale) || !finite_pos(a.k_descale))) return FA_ERR_INVALID_SCALE;
     if (a.qk8 && !finite_pos(a.scale * a.q_descale * a.k_descale)) return FA_ERR_INVALID_SCALE;
+    if (a.v8 && !finite_pos(a.v_descale)) return FA_ERR_INVALID_SCALE;
     if (a.input_pos < 0 || (long long)a.input_pos + Sq > INT_MAX) return FA_ERR_INVALID_INPUT_POS;
     if (a.window < 0 || (a.window > 0 && !a.causal)) return FA_ERR_INVALID_WINDOW;
     if (((uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.out) & 15u)
@@ -118,7 +120,7 @@ int validate(const Call& a) {
     if ((uintptr_t)a.lse & 3u) return FA_ERR_MISALIGNED;
     const size_t qke = a.qk8 ? 1 : 2;
     const size_t qb = (size_t)B * Hq * Sq * D * qke, kb = (size_t)B * Hkv * Skv * D * qke;
-    const size_t ob = (size_t)B * Hq * Sq * D * 2, vb = (size_t)B * Hkv * Skv * D * 2;
+    const size_t ob = (size_t)B * Hq * Sq * D * 2, vb = (size_t)B * Hkv * Skv * D * (a.v8 ? 1 : 2);
     const size_t lb = (size_t)B * Hq * Sq * 4;
     const uintptr_t o = (uintptr_t)a.out, l = (uintptr_t)a.lse;
     const uintptr_t q = (uintptr_t)a.q, k = (uintptr_t)a.k, v = (uintptr_t)a.v;
@@ -129,17 +131,18 @@ int validate(const Call& a) {
     return FA_OK;
 }
 
-bool applicable(const ConfigEntry& c, int Hq, int Hkv, int D, int causal, int dtype, int qk8) {
+bool applicable(const ConfigEntry& c, int Hq, int Hkv, int D, int causal, int dtype, int qk8,
+                int v8) {
     const int group = Hq / Hkv;
     return c.D == D && c.bf16 == (dtype == FA_DTYPE_BF16) && c.causal == (causal != 0) &&
-           c.qk8 == (qk8 != 0) && group % c.HPW == 0;
+           c.qk8 == (qk8 != 0) && c.v8 == (v8 != 0) && group % c.HPW == 0;
 }
 
-int find(int D, int bf16, int causal, int qk8, int BN, int QB, int WPH, int HPW) {
+int find(int D, int bf16, int causal, int qk8, int v8, int BN, int QB, int WPH, int HPW) {
     for (int i = 0; i < kNumConfigs; ++i) {
         const ConfigEntry& c = kConfigs[i];
-        if (c.D == D && c.bf16 == bf16 && c.causal == causal && c.qk8 == qk8 && c.BN == BN &&
-            c.QB == QB && c.WPH == WPH && c.HPW == HPW)
+        if (c.D == D && c.bf16 == bf16 && c.causal == causal && c.qk8 == qk8 && c.v8 == v8 &&
+            c.BN == BN && c.QB == QB && c.WPH == WPH && c.HPW == HPW)
             return i;
     }
     return -1;
@@ -158,27 +161,28 @@ long long grid_of(const ConfigEntry& c, int B, int Hq, int Hkv, int Sq) {
 // K/V tile is read once for all of them.  An 8-wave workgroup (a whole CU: its K/V tiles
 // shared by twice the waves) beats two 4-wave ones when it still forms at least one
 // workgroup per CU; smaller grids use 4-wave workgroups for more of them.
-int select(int B, int Hq, int Hkv, int Sq, int D, int causal, int dtype, int qk8) {
+int select(int B, int Hq, int Hkv, int Sq, int D, int causal, int dtype, int qk8, int v8 = 0) {
     const int bf16 = dtype == FA_DTYPE_BF16;
     const int cz = causal != 0;
     const int q8 = qk8 != 0;
+    const int x8 = v8 != 0;
     const int group = Hq / Hkv;
     const int bn = D == 128 ? 32 : 64;
     int big, small;
     if (group % 8 == 0 && D == 128) {
         // All eight heads of a group on one 32-row block: the K/V tile is shared by eight
         // waves as with 2 x 4, and the waves reach the causal diagonal together.
-        big = find(D, bf16, cz, q8, bn, 1, 1, 8);
-        small = find(D, bf16, cz, q8, bn, 1, 1, 4);
+        big = find(D, bf16, cz, q8, x8, bn, 1, 1, 8);
+        small = find(D, bf16, cz, q8, x8, bn, 1, 1, 4);
     } else if (group % 4 == 0) {
-        big = find(D, bf16, cz, q8, bn, 1, 2, 4);
-        small = find(D, bf16, cz, q8, bn, 1, 1, 4);
+        big = find(D, bf16, cz, q8, x8, bn, 1, 2, 4);
+        small = find(D, bf16, cz, q8, x8, bn, 1, 1, 4);
     } else if (group % 2 == 0) {
-        big = find(D, bf16, cz, q8, bn, 1, 4, 2);
-        small = find(D, bf16, cz, q8, bn, 1, 2, 2);
+        big = find(D, bf16, cz, q8, x8, bn, 1, 4, 2);
+        small = find(D, bf16, cz, q8, x8, bn, 1, 2, 2);
     } else {
-        big = find(D, bf16, cz, q8, bn, 1, 8, 1);
-        small = find(D, bf16, cz, q8, bn, 1, 4, 1);
+        big = find(D, bf16, cz, q8, x8, bn, 1, 8, 1);
+        small = find(D, bf16, cz, q8, x8, bn, 1, 4, 1);
     }
     if (big >= 0 && grid_of(kConfigs[big], B, Hq, Hkv, Sq) >= kNumCUs) return big;
     return small;
@@ -228,7 +232,7 @@ int auto_splits(const ConfigEntry& c, const Call& a) {
     const int tiles = max_key_tiles(c, a.Sq, a.Skv, a.causal, a.causal ? a.input_pos : 0,
                                     a.causal ? a.window : 0);
     const long long by_len = tiles / 8;
-    const double kv_elem_bytes = a.qk8 ? 3.0 : 4.0;   // K (1 or 2 bytes) + V (2 bytes)
+    const double kv_elem_bytes = (a.qk8 ? 1.0 : 2.0) + (a.v8 ? 1.0 : 2.0);   // K + V bytes
     const double kv_bytes = kv_elem_bytes * a.B * a.Hkv * std::min<double>(a.Skv, (double)tiles * c.BN) * c.D;
     const double part_bytes = 8.0 * a.B * a.Hq * (double)a.Sq * (c.D + 1);   // per range
     const long long by_traffic = (long long)(kv_bytes / part_bytes);
@@ -237,9 +241,9 @@ int auto_splits(const ConfigEntry& c, const Call& a) {
 
 int resolve_config(int config, const Call& a) {
     if (config < -1 || config >= kNumConfigs) return FA_ERR_INVALID_CONFIG;
-    if (config == -1) config = select(a.B, a.Hq, a.Hkv, a.Sq, a.D, a.causal, a.dtype, a.qk8);
+    if (config == -1) config = select(a.B, a.Hq, a.Hkv, a.Sq, a.D, a.causal, a.dtype, a.qk8, a.v8);
     if (config < 0) return FA_ERR_INVALID_CONFIG;
-    if (!applicable(kConfigs[config], a.Hq, a.Hkv, a.D, a.causal, a.dtype, a.qk8))
+    if (!applicable(kConfigs[config], a.Hq, a.Hkv, a.D, a.causal, a.dtype, a.qk8, a.v8))
         return FA_ERR_INVALID_CONFIG;
     return config;
 }
@@ -272,6 +276,7 @@ int launch(const Call& a, int config, int num_splits, void* workspace, void* str
     p.num_splits = num_splits;
     p.o_part = nullptr;
     p.lse_part = nullptr;
+    p.o_scale = a.v8 ? a.v_descale : 1.0f;
     if (num_splits > 1) {
         const size_t rows = (size_t)a.B * a.Hq * a.Sq;
         p.o_part = (float*)workspace;
@@ -314,7 +319,7 @@ int run_splitkv(const Call& a, int num_splits, int config, void* workspace,
         const size_t qb = (size_t)a.B * a.Hq * a.Sq * a.D * qke;
         const size_t kb = (size_t)a.B * a.Hkv * a.Skv * a.D * qke;
         const size_t ob = (size_t)a.B * a.Hq * a.Sq * a.D * 2;
-        const size_t vb = (size_t)a.B * a.Hkv * a.Skv * a.D * 2;
+        const size_t vb = (size_t)a.B * a.Hkv * a.Skv * a.D * (a.v8 ? 1 : 2);
         const size_t lb = (size_t)a.B * a.Hq * a.Sq * 4;
         const uintptr_t w = (uintptr_t)workspace;
         if (overlaps(w, need, (uintptr_t)a.q, qb) || overlaps(w, need, (uintptr_t)a.k, kb) ||
@@ -401,8 +406,24 @@ Call make_call(const void* q, const void* k, const void* v, void* out, float* ls
     a.window = window;
     a.dtype = dtype;
     a.qk8 = 0;
+    a.v8 = 0;
     a.q_descale = 1.0f;
     a.k_descale = 1.0f;
+    a.v_descale = 1.0f;
+    return a;
+}
+
+Call make_call_fp8qkv(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                      int Hq, int Hkv, int Sq, int Skv, int D, float scale, float q_descale,
+                      float k_descale, float v_descale, int causal, int input_pos, int window,
+                      int out_dtype) {
+    Call a = make_call(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, causal, input_pos,
+                       window, out_dtype);
+    a.qk8 = 1;
+    a.v8 = 1;
+    a.q_descale = q_descale;
+    a.k_descale = k_descale;
+    a.v_descale = v_descale;
     return a;
 }
 
@@ -492,6 +513,42 @@ int fa_splitkv_num_splits_fp8(int B, int Hq, int Hkv, int Sq, int Skv, int D, in
     if (config < 0) return config;
     return auto_splits(kConfigs[config], a);
 }
+int fa_fwd_fp8qkv(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                  int Hq, int Hkv, int Sq, int Skv, int D, float scale, float q_descale,
+                  float k_descale, float v_descale, int causal, int input_pos, int window,
+                  int out_dtype, void* stream, int config) {
+    return run(make_call_fp8qkv(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale, q_descale,
+                                k_descale, v_descale, causal, input_pos, window, out_dtype),
+               stream, config);
+}
+
+int fa_fwd_splitkv_fp8qkv(const void* q, const void* k, const void* v, void* out, float* lse,
+                          int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+                          float q_descale, float k_descale, float v_descale, int causal,
+                          int input_pos, int window, int out_dtype, int num_splits, int config,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    return run_splitkv(make_call_fp8qkv(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, scale,
+                                        q_descale, k_descale, v_descale, causal, input_pos,
+                                        window, out_dtype),
+                       num_splits, config, workspace, workspace_bytes, stream);
+}
+
+int fa_splitkv_num_splits_fp8qkv(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                                 int input_pos, int window, int out_dtype, int config) {
+    if (B < 0 || Hq < 0 || Sq < 0 || Hkv < 1 || Skv < 1) return FA_ERR_INVALID_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_HEAD_GROUP;
+    if (D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (out_dtype != FA_DTYPE_FP16 && out_dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
+    if (input_pos < 0 || (long long)input_pos + Sq > INT_MAX) return FA_ERR_INVALID_INPUT_POS;
+    if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_WINDOW;
+    const Call a = make_call_fp8qkv(nullptr, nullptr, nullptr, nullptr, nullptr, B, Hq, Hkv, Sq,
+                                    Skv, D, 1.0f, 1.0f, 1.0f, 1.0f, causal, input_pos, window,
+                                    out_dtype);
+    config = resolve_config(config, a);
+    if (config < 0) return config;
+    return auto_splits(kConfigs[config], a);
+}
+
 int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
                           int input_pos, int window, int dtype, int config) {
     if (B < 0 || Hq < 0 || Sq < 0 || Hkv < 1 || Skv < 1) return FA_ERR_INVALID_SHAPE;

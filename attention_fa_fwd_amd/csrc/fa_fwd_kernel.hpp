@@ -99,10 +99,12 @@ struct Params {
     int num_splits;  // key ranges per query tile; > 1 writes partials for the merge kernel
     float* o_part;   // num_splits > 1: normalised partial O, fp32 [num_splits][B*Hq*Sq][D]
     float* lse_part; // num_splits > 1: partial LSE, fp32 [num_splits][B*Hq*Sq]
+    float o_scale;   // fp8 V: its dequantisation factor, applied to O; 1 otherwise
 };
 
 // Compile-time configuration of one kernel instance.
-template <int D_, int BN_, int QB_, int WPH_, int HPW_, bool CAUSAL_, bool BF16_, bool QK8_ = false>
+template <int D_, int BN_, int QB_, int WPH_, int HPW_, bool CAUSAL_, bool BF16_, bool QK8_ = false,
+          bool V8_ = false>
 struct Cfg {
     static constexpr int D = D_;        // head dim
     static constexpr int BN = BN_;      // keys per K/V tile
@@ -112,6 +114,7 @@ struct Cfg {
     static constexpr bool CAUSAL = CAUSAL_;
     static constexpr bool BF16 = BF16_;    // V / O element type: bf16, else fp16
     static constexpr bool QK8 = QK8_;      // Q and K in fp8 e4m3 (S = K Q^T on the fp8 MFMA)
+    static constexpr bool V8 = V8_;        // V in fp8 e4m3 too (widened to BF16 ? bf16 : fp16)
     static constexpr int NW = WPH * HPW;
     static constexpr int NT = 64 * NW;
     static constexpr int BMP = 32 * QB * WPH;   // query positions per workgroup
@@ -121,6 +124,7 @@ struct Cfg {
     static_assert(QB == 1 || QB == 2, "query blocks per wave");
     static_assert(NW == 4 || NW == 8, "waves per workgroup");
     static_assert(!QK8 || (D == 128 && BN == 32 && QB == 1), "fp8 Q/K: head dim 128, 32-key tiles");
+    static_assert(!V8 || QK8, "fp8 V comes with fp8 Q and K");
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -171,6 +175,26 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* p) {
     const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s16x4*)(p));
     return __builtin_bit_cast(u32x2, r);
+}
+
+// 8 bytes of an 8-bit transposed LDS read.  Measured lane rule: in each group of 16 lanes,
+// lane i receives byte (i mod 8) of the 8-byte pieces addressed by lanes 2j + i/8,
+// j = 0..7, in that order.
+__device__ __forceinline__ u32x2 lds_read_tr8(const unsigned char* p) {
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+// Two fp8 e4m3 codes (bytes 0, 1 of x, or 2, 3 when HI) widened exactly to bf16 / fp16:
+// low half from the lower byte.
+template <bool BF16, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_widen(uint32_t x) {
+    if constexpr (BF16) {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, HI));
+    } else {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, HI));
+    }
 }
 
 // Balanced reductions of N floats held in registers: a max tree of v_max3 and a pairwise
@@ -238,20 +262,33 @@ template <int D>
 __device__ __forceinline__ int v_swz(int row) {
     return v_swz_of<D>(row & 3);
 }
+// fp8 V rows (128 bytes, 8 chunks), read 8 bytes at a time by the 8-bit transposed read:
+// one read covers, for each half of the wave, 8 keys (rows r with r mod 16 in {0..3, 8..11}
+// or {4..7, 12..15}) x 2 chunks x 16 bytes.  Chunk XOR 2 * (bit 1 of r | bit 3 of r << 1)
+// gives the four even and the four odd rows of each half distinct 32-byte bank windows,
+// so the 256 bytes of a half land on the 64 banks once.
+__device__ __forceinline__ int v8_swz(int row) {
+    return 2 * (((row >> 1) & 1) | (((row >> 3) & 1) << 1));
+}
 
 template <class C>
 __global__ __attribute__((amdgpu_flat_work_group_size(C::NT, C::NT), amdgpu_waves_per_eu(C::WAVES_PER_SIMD, C::WAVES_PER_SIMD)))
 void fa_fwd_kernel(Params p) {
-    constexpr int D = C::D, BN = C::BN, QB = C::QB, NT = C::NT, WPH = C::WPH, HPW = C::HPW;
+    constexpr int D = C::D, BN = C::BN, QB = C::QB, WPH = C::WPH, HPW = C::HPW;
     constexpr bool CAUSAL = C::CAUSAL, BF16 = C::BF16;
     constexpr int KB = BN / 32;          // 32-key blocks per tile
     constexpr int DK = D / 16;           // k-steps of Q K^T
     constexpr int DB = D / 32;           // 32-wide d blocks of O
     constexpr bool QK8 = C::QK8;
-    constexpr int ROWB = D * 2;          // bytes per V row (and K row unless fp8)
-    constexpr int TILE = BN * ROWB;      // bytes per V tile
-    constexpr int CPR = D / 8;           // 16-byte chunks per V row
-    constexpr int LD = BN * CPR / NT;    // 16-byte chunks of each V tile per thread
+    constexpr bool V8 = C::V8;
+    constexpr int ROWB = D * 2;          // bytes per fp16 / bf16 row
+    constexpr int ROWV = V8 ? D : ROWB;  // bytes per V row
+    constexpr int TILE = BN * ROWV;      // bytes per V tile
+    constexpr int CPR = ROWV / 16;       // 16-byte chunks per V row
+    constexpr int NLV = BN * CPR / 64;   // 64-lane loads per V tile
+    constexpr int NWV = NLV < C::NW ? NLV : C::NW;   // waves that load V (the last NWV)
+    constexpr int LD = NLV / NWV;        // V loads per loading thread
+    static_assert(NLV % NWV == 0, "V tile loads per wave");
     constexpr int ROWK = QK8 ? D : ROWB; // bytes per K row
     constexpr int TILEK = BN * ROWK;     // bytes per K tile
     constexpr int CPRK = ROWK / 16;      // 16-byte chunks per K row
@@ -261,8 +298,7 @@ void fa_fwd_kernel(Params p) {
     static_assert(NLK % NWK == 0, "K tile loads per wave");
     constexpr float P_LIMIT = 32768.0f;  // lazy max: largest partial row sum of p allowed
     constexpr float LN2 = 0.69314718055994530942f;
-    static_assert(BN * CPR % NT == 0, "tile chunks per thread");
-    static_assert(TILE % (NT * 16) == 0, "each load fills whole 1 KiB wave slots");
+    static_assert(TILE % (NWV * 1024) == 0, "each load fills whole 1 KiB wave slots");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -304,7 +340,7 @@ void fa_fwd_kernel(Params p) {
     constexpr int QE = QK8 ? 1 : 2;   // bytes per Q / K element
     const unsigned char* qp = (const unsigned char*)p.q + (size_t)(b * p.Hq + hq) * p.Sq * D * QE;
     const unsigned char* kp = (const unsigned char*)p.k + (size_t)(b * p.Hkv + kvh) * p.Skv * D * QE;
-    const T* vp = (const T*)p.v + (size_t)(b * p.Hkv + kvh) * p.Skv * D;
+    const unsigned char* vp = (const unsigned char*)p.v + (size_t)(b * p.Hkv + kvh) * p.Skv * ROWV;
 
     // Queries of this wave, as the B operand of S^T = K Q^T: lane l holds row l%32 of
     // query block qb, elements dk*16 + 8*(l/32) .. +8.  Rows past Sq read row Sq-1; their
@@ -391,36 +427,44 @@ void fa_fwd_kernel(Params p) {
     // rows past Skv, and whole tiles past the end, are out of range and land as zeros.
     // The row of a slot advances by 64*NW/CPR rows per load i; that is a multiple of 16, so
     // the swizzles (row mod 16) do not depend on i: one per-lane offset plus i * stride.
-    static_assert((64 * C::NW / CPR) % 16 == 0, "load stride keeps the swizzle");
+    static_assert((64 * NWV / CPR) % 16 == 0, "load stride keeps the swizzle");
     static_assert((64 * NWK / CPRK) % 16 == 0, "K load stride keeps the swizzle");
-    constexpr int LOAD_STRIDE = 64 * C::NW * 16;   // bytes of V tile per load i
+    constexpr int LOAD_STRIDE = 64 * NWV * 16;     // bytes of V tile per load i
     constexpr int LOAD_STRIDE_K = 64 * NWK * 16;   // bytes of K tile per load i
     // K rows of 128 bytes (fp8) use the 8-chunk swizzle of the head-dim-64 bf16 layout.
     constexpr int KSWZ_D = QK8 ? 64 : D;
     auto kswz = [&](int row) { return k_swz<KSWZ_D>(row); };
+    // Waves that load V tiles are the last NWV; those that load K the first NWK.
+    const int vw = w - (C::NW - NWV);
+    const bool ld_v = NWV == C::NW || vw >= 0;
+    const bool ld_k = NWK == C::NW || w < NWK;
     int ksrc, vsrc;
     {
-        const int slot = w * 64 + lane;
+        const int slot = (ld_v ? vw : 0) * 64 + lane;
         const int row = slot / CPR, pc = slot % CPR;
-        vsrc = row * ROWB + ((pc ^ v_swz<D>(row)) << 4);
-        const int rowk = slot / CPRK, pck = slot % CPRK;
+        if constexpr (V8) vsrc = row * ROWV + ((pc ^ v8_swz(row)) << 4);
+        else vsrc = row * ROWV + ((pc ^ v_swz<D>(row)) << 4);
+        const int slotk = w * 64 + lane;
+        const int rowk = slotk / CPRK, pck = slotk % CPRK;
         ksrc = rowk * ROWK + ((pck ^ kswz(rowk)) << 4);
     }
     // One buffer resource per tile, ending at the tile's last valid key; load i adds
     // i * LOAD_STRIDE as the scalar offset (gfx950's range check covers voffset + soffset,
     // so every load past the end of the range reads zero).
-    auto fetch = [&](const T* base, int j, unsigned char* dst, int src) FA_INLINE {
+    auto fetch = [&](const unsigned char* base, int j, unsigned char* dst, int src) FA_INLINE {
         const int j0 = min(j * BN, kend);
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (size_t)j0 * D, min(kend - j0, BN) * ROWB);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (size_t)j0 * ROWV, min(kend - j0, BN) * ROWV);
+        if (ld_v) {
 #pragma unroll
-        for (int i = 0; i < LD; ++i)
-            buffer_load_lds16(r, dst + (i * C::NW + w) * 1024, src, i * LOAD_STRIDE);
+            for (int i = 0; i < LD; ++i)
+                buffer_load_lds16(r, dst + (i * NWV + vw) * 1024, src, i * LOAD_STRIDE);
+        }
     };
     // K tiles: waves w < NWK load LDK chunks per lane (all waves unless fp8).
     auto fetch_k = [&](int j, unsigned char* dst) FA_INLINE {
         const int j0 = min(j * BN, kend);
         const __amdgpu_buffer_rsrc_t r = make_rsrc(kp + (size_t)j0 * ROWK, min(kend - j0, BN) * ROWK);
-        if (NWK == C::NW || w < NWK) {
+        if (ld_k) {
 #pragma unroll
             for (int i = 0; i < LDK; ++i)
                 buffer_load_lds16(r, dst + (i * NWK + w) * 1024, ksrc, i * LOAD_STRIDE_K);
@@ -447,6 +491,21 @@ void fa_fwd_kernel(Params p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
         voff[db] = v_lane_row * ROWB + (vq >> 1) * 8 + (((4 * db) ^ vu) << 4);
+    // fp8 V^T operand (one 8-bit transposed read per MFMA): the A operand of lane l holds,
+    // for d = l mod 32 of its 32-wide block (so, unlike the 16-bit path, accumulator row m
+    // is d = m and the epilogue stores accordingly), the same 8 keys as P^T's lane: keys
+    // 4h + e and 8 + 4h + e, e = 0..3 (h = l / 32) of the 16-key half.  By the read's lane
+    // rule, the lanes 2j + p of each 16-lane group g address key j of that list (d bytes
+    // 16 (g mod 2) + 8p of the block), so lane i receives key j's byte for its own d as
+    // element j.
+    int voff8[DB];
+    {
+        const int g8 = lane >> 4, a8 = lane & 15, j8 = a8 >> 1, p8 = a8 & 1;
+        const int key = 4 * (g8 >> 1) + j8 + (j8 >= 4 ? 4 : 0);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            voff8[db] = key * ROWV + (((2 * db + (g8 & 1)) ^ v8_swz(key)) << 4) + 8 * p8;
+    }
 
     // S^T = K Q^T of the tile in K buffer `kb`.
     auto qk = [&](const unsigned char* kb, f32x16 (&s)[KB][QB]) FA_INLINE {
@@ -477,6 +536,22 @@ void fa_fwd_kernel(Params p) {
 
     // O^T += V^T P^T for the tile whose V sits in `vb` and whose packed P is `pk`.
     auto pv = [&](const unsigned char* vb, const u32x4 (&pk)[KB][QB][2]) FA_INLINE {
+        if constexpr (V8) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int k2 = 0; k2 < KB; ++k2)
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf) {
+                            const u32x2 x = lds_read_tr8(vb + voff8[db] + (k2 * 32 + 16 * hf) * ROWV);
+                            const u32x4 a = {fp8x2_widen<BF16, false>(x[0]), fp8x2_widen<BF16, true>(x[0]),
+                                             fp8x2_widen<BF16, false>(x[1]), fp8x2_widen<BF16, true>(x[1])};
+                            acc[db][qb] = mfma32<BF16>(a, pk[k2][qb][hf], acc[db][qb]);
+                        }
+            return;
+        }
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -513,10 +588,18 @@ void fa_fwd_kernel(Params p) {
         constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
         asm volatile("s_waitcnt %0\n\ts_barrier" ::"n"(imm) : "memory");
     };
-    // A wave issues LDK K loads (if it loads K) and LD V loads per step.
+    // Wait until at most KN (for a wave that loads K) plus VN (for a wave that loads V) of
+    // this wave's loads are in flight, then the barrier.
+    auto wait_loads = [&](auto kn, auto vn) FA_INLINE {
+        constexpr int KN = decltype(kn)::value, VN = decltype(vn)::value;
+        if (ld_k && ld_v) wait_barrier(std::integral_constant<int, KN + VN>{});
+        else if (ld_k) wait_barrier(std::integral_constant<int, KN>{});
+        else if (ld_v) wait_barrier(std::integral_constant<int, VN>{});
+        else wait_barrier(std::integral_constant<int, 0>{});
+    };
+    // A wave issues LDK K loads (if it loads K) and LD V loads (if it loads V) per step.
     auto end_step = [&]() FA_INLINE {
-        if (NWK == C::NW || w < NWK) wait_barrier(std::integral_constant<int, LDK + LD>{});
-        else wait_barrier(std::integral_constant<int, LD>{});
+        wait_loads(std::integral_constant<int, LDK>{}, std::integral_constant<int, LD>{});
     };
 
     // One K-loop step for tile j (phase PH = (j - t0) % 3), a three-stage software
@@ -641,8 +724,7 @@ void fa_fwd_kernel(Params p) {
         fetch_k(t0 + 2, k_lds2);
         fetch(vp, t0, v_lds0, vsrc);
         // K(t0) landed; K(t0+1), K(t0+2) and V(t0) may be in flight.
-        if (NWK == C::NW || w < NWK) wait_barrier(std::integral_constant<int, 2 * LDK + LD>{});
-        else wait_barrier(std::integral_constant<int, LD>{});
+        wait_loads(std::integral_constant<int, 2 * LDK>{}, std::integral_constant<int, LD>{});
         qk(k_lds0, s0);
         end_step();   // K(t0+1) and K(t0+2) landed
 
@@ -687,9 +769,37 @@ void fa_fwd_kernel(Params p) {
         const int row = qw0 + qb * 32 + l32;
         if (row < p.Sq) {
             const float l = l_run[qb];
-            const float inv = l > 0.0f ? __builtin_amdgcn_rcpf(l) : 0.0f;
+            float inv = l > 0.0f ? __builtin_amdgcn_rcpf(l) : 0.0f;
+            if constexpr (V8) inv *= p.o_scale;   // V's dequantisation factor
             const float lse = l > 0.0f ? (m_run[qb] + __builtin_amdgcn_logf(l)) * LN2 : -__builtin_inff();
-            if (p.num_splits == 1) {
+            if constexpr (V8) {
+                // fp8 V: accumulator row m is d = 32 db + m, so the lane holds, for t = 0..3,
+                // the four consecutive d = 32 db + 8t + 4h + 0..3 in slots 4t .. 4t+3.
+                if (p.num_splits == 1) {
+                    T* orow = (T*)p.o + (head_row0 + row) * D;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        const f32x16 a = acc[db][qb] * inv;
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            *(u32x2*)(orow + db * 32 + 8 * t + 4 * h) =
+                                (u32x2){pack2<BF16>(a[4 * t], a[4 * t + 1]), pack2<BF16>(a[4 * t + 2], a[4 * t + 3])};
+                    }
+                    if (h == 0) p.lse[head_row0 + row] = lse;
+                } else {
+                    const size_t rows = (size_t)p.B * p.Hq * p.Sq;
+                    float* orow = p.o_part + ((size_t)split * rows + head_row0 + row) * D;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        const f32x16 a = acc[db][qb] * inv;
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            *(f32x4*)(orow + db * 32 + 8 * t + 4 * h) =
+                                (f32x4){a[4 * t], a[4 * t + 1], a[4 * t + 2], a[4 * t + 3]};
+                    }
+                    if (h == 0) p.lse_part[(size_t)split * rows + head_row0 + row] = lse;
+                }
+            } else if (p.num_splits == 1) {
                 T* orow = (T*)p.o + (head_row0 + row) * D;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {

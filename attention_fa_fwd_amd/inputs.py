@@ -51,8 +51,6 @@ WORKLOADS = {
 }
 
 
-# Workloads with fp8 E4M3 queries and keys (per-tensor descale factors) and fp16 / bf16
-# values: the headline and the causal multi-head shapes.
 # A sequence-length sweep of causal MHA at B=4, H=32, D=128, fp16: the shape of the length
 # sweep in "Tuning Flash Attention for peak performance in NVIDIA CUDA Tile" (Tables 1-6),
 # timed for context only.
@@ -62,6 +60,8 @@ SWEEP_WORKLOADS = {
     for S in (1024, 2048, 4096, 8192, 16384)
 }
 
+# Workloads with fp8 E4M3 queries and keys (per-tensor descale factors) and fp16 / bf16
+# values -- or fp8 values too ("fp8v") -- the headline, causal multi-head and decoding shapes.
 FP8_WORKLOADS = {
     "gqa8_causal_s8192_d128_fp8qk_bf16": dict(B=1, Hq=32, Hkv=4, Sq=8192, Skv=8192, D=128,
                                               dtype="bf16", causal=True, input_pos=0),
@@ -70,6 +70,13 @@ FP8_WORKLOADS = {
     # Decoding against an fp8 key cache (the bf16 decode workload's shape).
     "gqa4_decode_b4_kv16384_d128_fp8qk_bf16": dict(B=4, Hq=32, Hkv=8, Sq=1, Skv=16384, D=128,
                                                    dtype="bf16", causal=True, input_pos=16383),
+    # fp8 queries, keys and values (bf16 output): decoding against an fp8 K/V cache, and
+    # the headline prefill shape.
+    "gqa4_decode_b4_kv16384_d128_fp8qkv_bf16": dict(B=4, Hq=32, Hkv=8, Sq=1, Skv=16384, D=128,
+                                                    dtype="bf16", causal=True, input_pos=16383,
+                                                    fp8v=True),
+    "gqa8_causal_s8192_d128_fp8qkv_bf16": dict(B=1, Hq=32, Hkv=4, Sq=8192, Skv=8192, D=128,
+                                               dtype="bf16", causal=True, input_pos=0, fp8v=True),
 }
 
 
@@ -118,6 +125,16 @@ def make_qkv_fp8(B, Hq, Hkv, Sq, Skv, D, v_dtype, seed=0):
     return q8, k8, v.to(v_dtype).contiguous(), qd, kd
 
 
+def make_qkv_fp8qkv(B, Hq, Hkv, Sq, Skv, D, seed=0):
+    """The same seeded draws as ``make_qkv``, with q, k and v each quantised to fp8 E4M3 per
+    tensor.  Returns (q8, k8, v8, q_descale, k_descale, v_descale)."""
+    q, k, v = _randn_qkv(B, Hq, Hkv, Sq, Skv, D, seed)
+    q8, qd = quantize_fp8(q)
+    k8, kd = quantize_fp8(k)
+    v8, vd = quantize_fp8(v)
+    return q8, k8, v8, qd, kd, vd
+
+
 def make_workload(name, seed=0):
     """Inputs and call arguments for a named workload: (q, k, v, kwargs)."""
     w = dict(WORKLOADS[name] if name in WORKLOADS else SWEEP_WORKLOADS[name])
@@ -128,10 +145,18 @@ def make_workload(name, seed=0):
 
 
 def make_fp8_workload(name, seed=0):
-    """Inputs and call arguments for a named fp8 workload: (q8, k8, v, kwargs)."""
+    """Inputs and call arguments for a named fp8 workload: (q8, k8, v, kwargs).  For an
+    fp8 Q/K/V workload v is fp8 codes too and kwargs holds v_descale; its "dtype" is the
+    output's."""
     w = dict(FP8_WORKLOADS[name])
-    q8, k8, v, qd, kd = make_qkv_fp8(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"],
-                                     w["dtype"], seed)
     kw = dict(scale=default_scale(w["D"]), causal=w["causal"], input_pos=w["input_pos"],
-              window=w.get("window", 0), q_descale=qd, k_descale=kd)
+              window=w.get("window", 0))
+    if w.get("fp8v"):
+        q8, k8, v, qd, kd, vd = make_qkv_fp8qkv(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"],
+                                                w["D"], seed)
+        kw["v_descale"] = vd
+    else:
+        q8, k8, v, qd, kd = make_qkv_fp8(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"],
+                                         w["dtype"], seed)
+    kw.update(q_descale=qd, k_descale=kd)
     return q8, k8, v, kw

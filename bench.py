@@ -49,6 +49,8 @@ PEAK_FP8_TFLOPS = 2 * PEAK_TFLOPS
 PEAK_FP8QK_TFLOPS = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_TFLOPS)
 METRIC_BWD = "attention bwd TFLOP/s (2.5x the forward FLOPs: five matrix products), bf16/fp16"
 METRIC_FP8 = "attention fwd TFLOP/s, fp8 E4M3 Q/K (Q K^T on the fp8 MFMA), fp16/bf16 P V"
+METRIC_FP8QKV = ("attention fwd TFLOP/s, fp8 E4M3 Q/K/V (Q K^T on the fp8 MFMA; V widened to "
+                 "bf16/fp16 for P V)")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.json")
 MIN_WARMUP_S = 0.3
 COLD_FLUSH_BYTES = 512 << 20
@@ -117,10 +119,12 @@ def traffic_bytes(workload):
 
 
 def algorithmic_bytes(w, fp8=False):
-    """q, k, v read once; out and lse written once (q and k one byte per element with fp8)."""
+    """q, k, v read once; out and lse written once (q and k one byte per element with fp8,
+    v too for an fp8 Q/K/V workload)."""
     qk = 1 if fp8 else 2
+    vb = 1 if w.get("fp8v") else 2
     q_o = w["B"] * w["Hq"] * w["Sq"] * w["D"] * (qk + 2)
-    k_v = w["B"] * w["Hkv"] * w["Skv"] * w["D"] * (qk + 2)
+    k_v = w["B"] * w["Hkv"] * w["Skv"] * w["D"] * (qk + vb)
     return q_o + k_v + w["B"] * w["Hq"] * w["Sq"] * 4
 
 
@@ -142,6 +146,7 @@ def time_gpu(name, steps, warmup, config=-1, splitkv=False, backward=False, cold
     from attention_fa_fwd_amd.inputs import make_fp8_workload, make_workload
 
     w, fp8 = workload(name)
+    fp8v = fp8 and w.get("fp8v", False)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if fp8:
@@ -149,7 +154,8 @@ def time_gpu(name, steps, warmup, config=-1, splitkv=False, backward=False, cold
     else:
         q, k, v, kw = make_workload(name, seed=0)
     q, k, v = q.to(dev), k.to(dev), v.to(dev)
-    out = torch.empty(q.shape, dtype=v.dtype, device=dev)
+    out_dtype = {"bf16": torch.bfloat16, "fp16": torch.float16}[w["dtype"]]
+    out = torch.empty(q.shape, dtype=out_dtype, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
@@ -169,6 +175,24 @@ def time_gpu(name, steps, warmup, config=-1, splitkv=False, backward=False, cold
             fa.fa_bwd_into(q, k, v, out, lse, dout, dq, dk, dv, ws, scale=kw["scale"],
                            causal=kw["causal"], input_pos=kw["input_pos"], window=kw["window"],
                            stream=sp)
+    elif fp8v and splitkv:
+        splits = fa.splitkv_num_splits_fp8qkv(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"],
+                                              w["causal"], w["input_pos"], out_dtype, config,
+                                              kw["window"])
+        nbytes = fa.splitkv_workspace_size(w["B"], w["Hq"], w["Sq"], w["D"], splits)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+
+        def step():
+            fa.fa_fwd_splitkv_fp8qkv_into(q, k, v, out, lse, ws, kw["q_descale"], kw["k_descale"],
+                                          kw["v_descale"], num_splits=splits, scale=kw["scale"],
+                                          causal=kw["causal"], input_pos=kw["input_pos"],
+                                          window=kw["window"], config=config, stream=sp)
+    elif fp8v:
+        def step():
+            fa.fa_fwd_fp8qkv_into(q, k, v, out, lse, kw["q_descale"], kw["k_descale"],
+                                  kw["v_descale"], scale=kw["scale"], causal=kw["causal"],
+                                  input_pos=kw["input_pos"], window=kw["window"], config=config,
+                                  stream=sp)
     elif fp8 and splitkv:
         splits = fa.splitkv_num_splits_fp8(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"],
                                            w["causal"], w["input_pos"], v.dtype, config,
@@ -245,7 +269,9 @@ def time_gpu(name, steps, warmup, config=-1, splitkv=False, backward=False, cold
     if config >= 0:
         cfg = config
     elif fp8:
-        cfg = fa.select_config_fp8(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["D"], w["causal"], v.dtype)
+        cfg = fa.select_config_fp8(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["D"], w["causal"], out_dtype)
+        if fp8v:   # the fp8 Q/K/V table entry of the same shape
+            cfg = fa.config_names().index(fa.config_names()[cfg].replace("_fp8qk_", "_fp8qkv_"))
     else:
         cfg = fa.select_config(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"], w["causal"],
                                w["input_pos"], q.dtype)
@@ -254,41 +280,91 @@ def time_gpu(name, steps, warmup, config=-1, splitkv=False, backward=False, cold
                 warmup_extra=extra, splits=splits)
 
 
-def cpu_baseline(name, min_s=10.0):
-    """The fp64 oracle on whole GQA groups (one K/V head and its query heads) of the
-    workload, one group after another until at least ``min_s`` seconds of CPU work have
-    run or the workload is exhausted (a bounded sample; every group has the same shape)."""
-    import numpy as np
-
-    import oracle
-    from attention_fa_fwd_amd.inputs import WORKLOADS, make_workload
-
+def _blas_threads():
+    """Threads of the BLAS pool NumPy's matmul runs on (threadpoolctl), or None."""
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else None
     except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = len(os.sched_getaffinity(0))
-    w = dict(WORKLOADS[name])
-    q, k, v, kw = make_workload(name, seed=0)
+        return None
+
+
+def cpu_baseline(name, min_s=10.0, backward=False):
+    """The fp64 oracle of the timed path (forward, fp8 forward or backward) on whole GQA
+    groups (one K/V head and its query heads) of the workload, one group after another until
+    at least ``min_s`` seconds of CPU work have run or the workload is exhausted (a bounded
+    sample; every group has the same shape).  BLAS runs on every core the process may use
+    (os.sched_getaffinity); ``cores`` is the size of the BLAS pool that ran, next to that
+    count.  The smallest workload also gets the single-core pure-Python form."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from attention_fa_fwd_amd.inputs import make_fp8_workload, make_workload
+
+    affinity = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=affinity, user_api="blas")
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        limiter = None
+    threads = _blas_threads() or affinity
+    w, fp8 = workload(name)
+    fp8v = fp8 and w.get("fp8v", False)
+    if fp8:
+        q, k, v, kw = make_fp8_workload(name, seed=0)
+    else:
+        q, k, v, kw = make_workload(name, seed=0)
+    codes = lambda t: t.view(torch.uint8).numpy()
     G = w["Hq"] // w["Hkv"]
     groups = [(b, g) for b in range(w["B"]) for g in range(w["Hkv"])]
+    if backward:
+        gen = torch.Generator(device="cpu")
+        gen.manual_seed(1)
+        dout = torch.randn(q.shape, generator=gen, dtype=torch.float32).to(q.dtype)
     done, dt = 0, 0.0
     for b, g in groups:
-        qs = q[b:b + 1, g * G:(g + 1) * G].double().numpy()
-        ks = k[b:b + 1, g:g + 1].double().numpy()
-        vs = v[b:b + 1, g:g + 1].double().numpy()
+        sl_q, sl_k = (slice(b, b + 1), slice(g * G, (g + 1) * G)), (slice(b, b + 1), slice(g, g + 1))
         t0 = time.perf_counter()
-        oracle.attention_blocked(qs, ks, vs, kw["scale"], kw["causal"], kw["input_pos"], window=kw["window"])
+        if fp8:
+            oracle.attention_fp8_blocked(codes(q[sl_q]), codes(k[sl_k]),
+                                         codes(v[sl_k]) if fp8v else v[sl_k].double().numpy(),
+                                         kw["scale"], kw["q_descale"], kw["k_descale"], kw["causal"],
+                                         kw["input_pos"], window=kw["window"],
+                                         v_descale=kw.get("v_descale"))
+        elif backward:
+            oracle.attention_backward_blocked(q[sl_q].double().numpy(), k[sl_k].double().numpy(),
+                                              v[sl_k].double().numpy(), dout[sl_q].double().numpy(),
+                                              kw["scale"], kw["causal"], kw["input_pos"],
+                                              window=kw["window"])
+        else:
+            oracle.attention_blocked(q[sl_q].double().numpy(), k[sl_k].double().numpy(),
+                                     v[sl_k].double().numpy(), kw["scale"], kw["causal"],
+                                     kw["input_pos"], window=kw["window"])
         dt += time.perf_counter() - t0
         done += 1
         if dt >= min_s:
             break
+    if limiter is not None:
+        limiter.restore_original_limits()
     ws = dict(w, B=1, Hq=G, Hkv=1)
-    return dict(value=done * literal_flops(ws) / dt / 1e12, unit="TFLOP/s", cores=int(threads),
-                kind="oracle",
-                sample=f"{done} of the {len(groups)} GQA groups (one K/V head and its {G} query "
-                       f"heads each) of {name}; {dt:.1f} s wall; same FLOP count rule",
-                wall_s=round(dt, 3))
+    flops = literal_flops(ws) * (2.5 if backward else 1.0)
+    form = ("fp8 forward" if fp8 else "backward" if backward else "forward") + " oracle (NumPy, fp64)"
+    out = dict(value=done * flops / dt / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+               sample=f"{form}: {done} of the {len(groups)} GQA groups (one K/V head and its {G} "
+                      f"query heads each) of {name}; {dt:.1f} s wall; same FLOP count rule",
+               wall_s=round(dt, 3), affinity_cores=affinity)
+    if w["B"] * w["Hq"] * w["Sq"] * w["Skv"] <= 1 << 16 and not fp8 and not backward:
+        # the pure-Python loops, one core, on the whole (tiny) workload
+        t0 = time.perf_counter()
+        oracle.attention_naive(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                               kw["scale"], kw["causal"], kw["input_pos"], window=kw["window"])
+        t1 = time.perf_counter() - t0
+        out["naive_single_core"] = dict(value=literal_flops(w) / t1 / 1e12, unit="TFLOP/s",
+                                        cores=1, wall_s=round(t1, 3),
+                                        sample=f"pure-Python loops over all of {name}")
+    return out
 
 
 def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False, backward=False,
@@ -302,7 +378,10 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False, bac
     mean_kernel_ms = sum(r["per_ms"]) / len(r["per_ms"])
     med = r["per_ms"][len(r["per_ms"]) // 2]
     p95 = r["per_ms"][min(len(r["per_ms"]) - 1, int(math.ceil(0.95 * len(r["per_ms"]))) - 1)]
+    fp8v = fp8 and w.get("fp8v", False)
     path = ("fa_bwd" if backward else
+            f"fa_fwd_splitkv_fp8qkv ({r['splits']} splits)" if fp8v and splitkv else
+            "fa_fwd_fp8qkv" if fp8v else
             f"fa_fwd_splitkv_fp8 ({r['splits']} splits)" if fp8 and splitkv else
             "fa_fwd_fp8" if fp8 else
             f"fa_fwd_splitkv ({r['splits']} splits)" if splitkv else "fa_fwd")
@@ -320,7 +399,8 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False, bac
                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
     else:
         achieved = flops / (mean_kernel_ms * 1e-3) / 1e12
-        metric, unit = (METRIC_BWD if backward else METRIC_FP8 if fp8 else METRIC), "TFLOP/s"
+        metric, unit = (METRIC_BWD if backward else METRIC_FP8QKV if fp8v else
+                        METRIC_FP8 if fp8 else METRIC), "TFLOP/s"
         peak = PEAK_FP8QK_TFLOPS if fp8 else PEAK_TFLOPS
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
@@ -333,12 +413,18 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False, bac
         "steps": steps,
         "warmup": warmup,
         "warmup_extra_steps": r["warmup_extra"],
+        "warmup_total_steps": warmup + r["warmup_extra"],
+        "warmup_rule": f"{warmup} steps, then more until {MIN_WARMUP_S} s of warm-up (clock ramp)",
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"fp8e4m3 q/k, {w['dtype']} v" if fp8 else w["dtype"],
-        "data": "synthetic: seeded N(0,1) q, k, v rounded to the storage dtype",
+        "dtype": (f"fp8e4m3 q/k/v, {w['dtype']} out" if fp8v else
+                  f"fp8e4m3 q/k, {w['dtype']} v" if fp8 else w["dtype"]),
+        "data": ("synthetic: seeded N(0,1) q, k, v quantised per tensor to fp8 e4m3" if fp8v else
+                 "synthetic: seeded N(0,1) q, k quantised per tensor to fp8 e4m3, v rounded to "
+                 "the storage dtype" if fp8 else
+                 "synthetic: seeded N(0,1) q, k, v rounded to the storage dtype"),
         "config": {"workload": name, "B": w["B"], "Hq": w["Hq"], "Hkv": w["Hkv"], "Sq": w["Sq"],
                    "Skv": w["Skv"], "D": w["D"], "causal": w["causal"],
                    "input_pos": w["input_pos"], "window": w.get("window", 0),
@@ -354,9 +440,9 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False, bac
         line["pct_of_peak"] = round(100.0 * value / (PEAK_FP8QK_TFLOPS if fp8 else PEAK_TFLOPS), 2)
         line["tflops_exact_pairs"] = round(exact_flops(w) * (2.5 if backward else 1.0)
                                            / (ms_step * 1e-3) / 1e12, 2)
-    if with_cpu and not fp8 and not backward:
+    if with_cpu:
         log("timing the fp64 CPU oracle on a bounded sample ...")
-        line["cpu_baseline"] = cpu_baseline(name)
+        line["cpu_baseline"] = cpu_baseline(name, backward=backward)
     return line
 
 
@@ -459,11 +545,12 @@ def main(argv=None):
             for split in runs:
                 if name == a.workload and split == a.splitkv:
                     continue
-                extra = bench_line(name, a.steps, a.warmup, -1, with_cpu=False, splitkv=split)
+                extra = bench_line(name, a.steps, a.warmup, -1, with_cpu=not a.no_cpu_baseline,
+                                   splitkv=split)
                 print("[bench-extra] " + json.dumps(extra), file=sys.stderr, flush=True)
         for name in (HEADLINE, "mha_causal_s4096_d128_fp16"):
-            extra = bench_line(name, max(1, a.steps // 4), a.warmup, -1, with_cpu=False,
-                               backward=True)
+            extra = bench_line(name, max(1, a.steps // 4), a.warmup, -1,
+                               with_cpu=not a.no_cpu_baseline, backward=True)
             print("[bench-extra] " + json.dumps(extra), file=sys.stderr, flush=True)
     if a.sweep:
         from attention_fa_fwd_amd.inputs import SWEEP_WORKLOADS

@@ -232,6 +232,45 @@ int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* ou
                            int causal, int input_pos, int window, int dtype, int num_splits,
                            int config, void* stream);
 
+/*
+ * Attention forward pass with fp8 E4M3 queries, keys and values (OCP "E4M3FN": 1 sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits; largest finite value 448), each with one
+ * per-tensor dequantisation factor: the attention of q = q_descale * q_codes, k =
+ * k_descale * k_codes, v = v_descale * v_codes.  "How I Beat PyTorch's Flash Attention"
+ * names FP8 tensor cores as its next step ("What's Next"); no page gives a format or a
+ * scaling rule, so this is the plainest one.  Q K^T runs on the fp8 MFMA; each V fragment
+ * is widened exactly to bf16 / fp16 (every E4M3 value is representable there) and P V runs
+ * on the bf16 / fp16 MFMA with P in that type; v_descale is applied to the fp32 result
+ * before it is rounded.  K and V together move 2 bytes per element instead of 4.
+ *
+ *   q, k, v      fp8 E4M3 codes, one byte per element, layouts as for fa_fwd.
+ *   out          [B, Hq, Sq, D] of out_dtype (an fa_dtype); lse as for fa_fwd.
+ *   q_descale, k_descale, v_descale   finite and > 0 (FA_ERR_INVALID_SCALE), checked
+ *                after scale, in this order.
+ *   D            128 only (FA_ERR_UNSUPPORTED_HEAD_DIM otherwise).
+ *   other arguments as for fa_fwd_fp8 (config: an "fp8qkv" configuration or -1).
+ * Checks and errors as for fa_fwd_fp8.
+ */
+int fa_fwd_fp8qkv(const void* q, const void* k, const void* v, void* out, float* lse,
+                  int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+                  float q_descale, float k_descale, float v_descale, int causal,
+                  int input_pos, int window, int out_dtype, void* stream, int config);
+
+/* Split-KV form of fa_fwd_fp8qkv (decoding against an fp8 K/V cache): arguments as for
+ * fa_fwd_fp8qkv, then num_splits, config, workspace and workspace_bytes as for
+ * fa_fwd_splitkv (fa_splitkv_workspace_size gives the size).  Checks: those of
+ * fa_fwd_fp8qkv, then those of fa_fwd_splitkv's split and workspace arguments. */
+int fa_fwd_splitkv_fp8qkv(const void* q, const void* k, const void* v, void* out, float* lse,
+                          int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
+                          float q_descale, float k_descale, float v_descale, int causal,
+                          int input_pos, int window, int out_dtype, int num_splits,
+                          int config, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Split count fa_fwd_splitkv_fp8qkv uses for num_splits = 0 (the rule of
+ * fa_splitkv_num_splits, with 2 bytes per K/V element), or a negative fa_status. */
+int fa_splitkv_num_splits_fp8qkv(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                                 int input_pos, int window, int out_dtype, int config);
+
 /* Workspace bytes fa_fwd_splitkv needs for num_splits ranges:
  * num_splits * B * Hq * Sq * (D + 1) * 4 (fp32 partial O, then fp32 partial LSE), 0 when
  * num_splits <= 1, the problem is empty or D is unsupported. */

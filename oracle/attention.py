@@ -50,7 +50,7 @@ Several forms are provided, written independently of one another:
                                into one result (split-KV).
 * ``fp8_e4m3_decode`` and ``attention_fp8_blocked``: fp8 E4M3 codes decoded
                                from the format's definition, and the definition over
-                               dequantised fp8 queries and keys.
+                               dequantised fp8 queries and keys (and values).
 * ``attention_backward_blocked``: the gradients dQ, dK, dV from the softmax
                                derivative (the backward pass); ``attention_backward_sampled``
                                evaluates them at sampled rows of full-size problems.
@@ -537,16 +537,18 @@ def fp8_e4m3_decode(codes):
 
 
 def attention_fp8_blocked(q_codes, k_codes, v, scale, q_descale, k_descale, causal=False,
-                          input_pos=0, window=0):
+                          input_pos=0, window=0, v_descale=None):
     """Attention of fp8-coded queries and keys: the module-docstring definition applied
     to q = q_descale * decode(q_codes), k = k_descale * decode(k_codes) and v, in
-    float64 (``attention_blocked``).  Returns (O, LSE)."""
-    if not (math.isfinite(q_descale) and q_descale > 0 and math.isfinite(k_descale) and k_descale > 0):
+    float64 (``attention_blocked``).  With ``v_descale`` given, v holds fp8 codes as well
+    and the values are v_descale * decode(v).  Returns (O, LSE)."""
+    factors = [q_descale, k_descale] + ([] if v_descale is None else [v_descale])
+    if not all(math.isfinite(f) and f > 0 for f in factors):
         raise ValueError("descale factors must be finite and > 0")
     q = q_descale * fp8_e4m3_decode(q_codes)
     k = k_descale * fp8_e4m3_decode(k_codes)
-    return attention_blocked(q, k, np.asarray(v, np.float64), scale, causal, input_pos,
-                             window=window)
+    vv = np.asarray(v, np.float64) if v_descale is None else v_descale * fp8_e4m3_decode(v)
+    return attention_blocked(q, k, vv, scale, causal, input_pos, window=window)
 
 
 # ----------------------------------------------------------------------------

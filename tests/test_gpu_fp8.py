@@ -1,5 +1,6 @@
 """GPU parity of fa_fwd_fp8 (fp8 E4M3 queries and keys, fp16 / bf16 values) against the
-fp64 oracle over the dequantised inputs.
+fp64 oracle over the dequantised inputs; the named fp8 workloads include fp8 values too
+(fa_fwd_fp8qkv, whose own tests are in test_gpu_fp8qkv.py).
 
 The scores come from exact products of fp8 values accumulated in fp32, so the output
 error has the same sources as the fp16 / bf16 path (P and O rounded to the value type) and
@@ -111,25 +112,28 @@ def test_fp8_descale_invariance():
 
 @pytest.mark.parametrize("name", sorted(FP8_WORKLOADS))
 def test_fp8_named_workload(name):
+    """Full-size fp8 workloads (fp8 queries and keys; with "fp8v", fp8 values too) in the
+    dispatch table's configuration: every element of O and LSE against the oracle."""
     w = FP8_WORKLOADS[name]
     _say("workload", name)
     q8, k8, v, kw = make_fp8_workload(name, seed=0)
-    out, lse = run(q8, k8, v, kw["q_descale"], kw["k_descale"], kw["scale"], kw["causal"],
-                   kw["input_pos"], kw["window"])
-    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
-    rng = np.random.default_rng(3)
-    B, Hq, Sq = w["B"], w["Hq"], w["Sq"]
-    rows = [r for r in (0, 1, 31, 32, 63, 64, 127, 128, Sq // 2, Sq - 1) if r < Sq]
-    samples = [(0, int(rng.integers(Hq)), i) for i in rows]
-    samples += [(0, int(rng.integers(Hq)), int(rng.integers(Sq))) for _ in range(40)]
-    qf = oracle.fp8_e4m3_decode(_codes(q8)) * kw["q_descale"]
-    kf = oracle.fp8_e4m3_decode(_codes(k8)) * kw["k_descale"]
-    O, L = oracle.attention_rows(qf, kf, v.double().numpy(), kw["scale"], kw["causal"],
-                                 kw["input_pos"], samples)
-    o = np.stack([out[b, h, i].double().numpy() for b, h, i in samples])
-    l = np.array([float(lse[b, h, i]) for b, h, i in samples])
-    assert float(np.max(np.abs(o - O))) <= TOL_O[v.dtype]
-    assert float(np.max(np.abs(l - L))) <= TOL_LSE
+    if w.get("fp8v"):
+        out, lse = fa.fa_fwd_fp8qkv(q8.to(DEV), k8.to(DEV), v.to(DEV), kw["q_descale"], kw["k_descale"],
+                                    kw["v_descale"], out_dtype=torch.bfloat16, scale=kw["scale"],
+                                    causal=kw["causal"], input_pos=kw["input_pos"])
+        torch.cuda.synchronize()
+        out, lse = out.cpu(), lse.cpu()
+        O, L = oracle.attention_fp8_blocked(_codes(q8), _codes(k8), _codes(v), kw["scale"],
+                                            kw["q_descale"], kw["k_descale"], kw["causal"],
+                                            kw["input_pos"], v_descale=kw["v_descale"])
+        dt = torch.bfloat16
+    else:
+        out, lse = run(q8, k8, v, kw["q_descale"], kw["k_descale"], kw["scale"], kw["causal"],
+                       kw["input_pos"], kw["window"])
+        O, L = oracle_fp8(q8, k8, v, kw["scale"], kw["q_descale"], kw["k_descale"], kw["causal"],
+                          kw["input_pos"])
+        dt = v.dtype
+    check(O, L, out, lse, dt, name)
 
 
 FP8_SPLIT_CASES = [

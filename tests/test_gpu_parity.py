@@ -92,7 +92,7 @@ def forced_configs(D, dtype, causal):
     causality (the fp8 ones have their own tests)."""
     out = []
     for cid, name in enumerate(fa.config_names()):
-        if not name.startswith(f"D{D}_") or "_fp8qk_" in name:
+        if not name.startswith(f"D{D}_") or "fp8" in name:
             continue
         if ("_causal_" in name) != causal or (("_bf16" in name) != (dtype == "bf16")):
             continue

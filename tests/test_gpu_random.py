@@ -21,7 +21,7 @@ import torch
 
 import attention_fa_fwd_amd as fa
 import oracle
-from attention_fa_fwd_amd.inputs import DTYPES, make_qkv, make_qkv_fp8
+from attention_fa_fwd_amd.inputs import DTYPES, make_qkv, make_qkv_fp8, make_qkv_fp8qkv
 
 pytestmark = pytest.mark.gpu
 
@@ -120,6 +120,31 @@ def test_random_fp8(i):
                                      causal=causal, input_pos=pos, num_splits=splits, window=W)
     torch.cuda.synchronize()
     check_fwd(O, L, out, lse, v.dtype, what + (splits,))
+
+
+@pytest.mark.parametrize("i", range(N_CASES // 2))
+def test_random_fp8qkv(i):
+    """fa_fwd_fp8qkv and fa_fwd_splitkv_fp8qkv (fp8 queries, keys and values) on random
+    problems (head dim 128); the drawn dtype is the output's."""
+    rng = np.random.default_rng(5000 + i)
+    B, Hq, Hkv, Sq, Skv, D, dt, causal, pos, W = draw(rng, fp8=True)
+    what = (B, Hq, Hkv, Sq, Skv, D, dt, causal, pos, W)
+    _say("fp8qkv", what)
+    q8, k8, v8, qd, kd, vd = make_qkv_fp8qkv(B, Hq, Hkv, Sq, Skv, D, seed=300 + i)
+    u8 = lambda t: t.view(torch.uint8).numpy()
+    O, L = oracle.attention_fp8_blocked(u8(q8), u8(k8), u8(v8), 0.09, qd, kd, causal, pos,
+                                        window=W, v_descale=vd)
+    odt = DTYPES[dt]
+    out, lse = fa.fa_fwd_fp8qkv(q8.to(DEV), k8.to(DEV), v8.to(DEV), qd, kd, vd, out_dtype=odt,
+                                scale=0.09, causal=causal, input_pos=pos, window=W)
+    torch.cuda.synchronize()
+    check_fwd(O, L, out, lse, odt, what)
+    splits = int(rng.choice([0, 2, 5]))
+    out, lse = fa.fa_fwd_splitkv_fp8qkv(q8.to(DEV), k8.to(DEV), v8.to(DEV), qd, kd, vd, out_dtype=odt,
+                                        scale=0.09, causal=causal, input_pos=pos,
+                                        num_splits=splits, window=W)
+    torch.cuda.synchronize()
+    check_fwd(O, L, out, lse, odt, what + (splits,))
 
 
 @pytest.mark.parametrize("i", range(N_CASES // 2))

@@ -88,7 +88,7 @@ def test_window_every_config(D, dtype):
     q, k, v = make_qkv(1, 16, 2, 333, 400, D, dtype, seed=12)   # GQA 8: every shape applies
     tested = 0
     for cid, name in enumerate(fa.config_names()):
-        if not name.startswith(f"D{D}_") or "_fp8qk_" in name or "_causal_" not in name or \
+        if not name.startswith(f"D{D}_") or "fp8" in name or "_causal_" not in name or \
                 (("_bf16" in name) != (dtype == "bf16")):
             continue
         _say("config", name)

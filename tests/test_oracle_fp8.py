@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from attention_fa_fwd_amd.inputs import make_qkv_fp8, quantize_fp8
+from attention_fa_fwd_amd.inputs import make_qkv_fp8, make_qkv_fp8qkv, quantize_fp8
 from tests import oracle_pins as pins
 
 ALL = np.arange(256, dtype=np.uint8)
@@ -128,3 +128,36 @@ def test_fp8_rejects_bad_descale():
         with pytest.raises(ValueError):
             oracle.attention_fp8_blocked(q8.view(torch.uint8).numpy(), k8.view(torch.uint8).numpy(),
                                          v.double().numpy(), 0.1, bad, kd)
+
+
+# --- fp8 values --------------------------------------------------------------------
+
+def test_fp8v_attention_matches_torch_decoded_inputs():
+    """fp8 values: the oracle decodes v's codes and applies v_descale; decoding all three
+    inputs with PyTorch's float8_e4m3fn conversion instead gives the same result."""
+    q8, k8, v8, qd, kd, vd = make_qkv_fp8qkv(2, 4, 2, 33, 70, 128, seed=6)
+    u8 = lambda t: t.view(torch.uint8).numpy()
+    O, L = oracle.attention_fp8_blocked(u8(q8), u8(k8), u8(v8), 0.09, qd, kd, True, 37,
+                                        v_descale=vd)
+    qf = q8.to(torch.float64).numpy() * qd
+    kf = k8.to(torch.float64).numpy() * kd
+    vf = v8.to(torch.float64).numpy() * vd
+    O2, L2 = oracle.attention_blocked(qf, kf, vf, 0.09, True, 37)
+    assert np.max(np.abs(O - O2)) < 1e-12 and np.max(np.abs(L - L2)) < 1e-12
+
+
+def test_fp8v_descale_scales_output_only():
+    """O is linear in the values, so doubling v_descale doubles O and leaves LSE as it is."""
+    q8, k8, v8, qd, kd, vd = make_qkv_fp8qkv(1, 2, 1, 30, 45, 128, seed=7)
+    u8 = lambda t: t.view(torch.uint8).numpy()
+    O1, L1 = oracle.attention_fp8_blocked(u8(q8), u8(k8), u8(v8), 0.1, qd, kd, False, v_descale=vd)
+    O2, L2 = oracle.attention_fp8_blocked(u8(q8), u8(k8), u8(v8), 0.1, qd, kd, False, v_descale=2 * vd)
+    assert np.max(np.abs(O2 - 2 * O1)) < 1e-12 and np.max(np.abs(L2 - L1)) == 0.0
+
+
+def test_fp8v_rejects_bad_descale():
+    q8, k8, v8, qd, kd, vd = make_qkv_fp8qkv(1, 1, 1, 4, 4, 128, seed=0)
+    u8 = lambda t: t.view(torch.uint8).numpy()
+    for bad in (0.0, -1.0, math.inf, math.nan):
+        with pytest.raises(ValueError):
+            oracle.attention_fp8_blocked(u8(q8), u8(k8), u8(v8), 0.1, qd, kd, v_descale=bad)
