@@ -58,11 +58,22 @@ def bench_of_run(path):
     if line is None:
         return ["", "# bench.py line of the same run: not found in " + os.path.basename(path)]
     k = line.get("kernel_us", {})
-    return ["", "# bench.py line of the same run (HIP events on the launch stream):",
-            f"#   workload {line['config']['workload']}, path {line['config'].get('path')}, "
-            f"kernel {line['config'].get('kernel')}",
-            f"#   value {line['value']} {line['unit']}, kernel_us mean {k.get('mean')} "
-            f"median {k.get('median')} min {k.get('min')}"]
+    out = ["", "# bench.py line of the same run (HIP events on the launch stream):",
+           f"#   workload {line['config']['workload']}, path {line['config'].get('path')}, "
+           f"kernel {line['config'].get('kernel')}",
+           f"#   value {line['value']} {line['unit']}, kernel_us mean {k.get('mean')} "
+           f"median {k.get('median')} min {k.get('min')}"]
+    if "ms_per_step" in line:
+        out.append(f"#   ms_per_step {line['ms_per_step']}")
+    pc = line.get("peak_check") or {}
+    if "mfma_loop_tflops" in pc:
+        # The box's own real-data MFMA rate: box-to-box clock spread shows here.
+        frac = (f", the run's value is {line['value'] / pc['mfma_loop_tflops']:.3f} of it"
+                if line.get("unit") == "TFLOP/s" else "")
+        out.append(f"#   peak_check: bf16 MFMA loop on random operands {pc['mfma_loop_tflops']} "
+                   f"TFLOP/s at {pc.get('mfma_loop_clock_ghz')} GHz (derived peak "
+                   f"{pc.get('derived_peak_tflops')}){frac}")
+    return out
 
 
 def trace(db, command, bench_out=None):
@@ -107,6 +118,10 @@ def pmc(db, command):
             conf = cs["SQ_LDS_BANK_CONFLICT"]
             out.append(f"  {'derived LDS conflict cycles %':<32} {100 * conf / act if act else 0:>18.2f}"
                        f"   (bank-conflict stall cycles / LDS indexed-active cycles)")
+        if "TCC_HIT_sum" in cs and "TCC_MISS_sum" in cs:
+            tot = cs["TCC_HIT_sum"] + cs["TCC_MISS_sum"]
+            out.append(f"  {'derived L2 hit %':<32} {100 * cs['TCC_HIT_sum'] / tot if tot else 0:>18.2f}"
+                       f"   (TCC hits / (hits + misses))")
         if "SQ_INSTS_VALU" in cs and "SQ_INSTS_MFMA" in cs:
             out.append(f"  {'derived VALU / MFMA insts':<32} {cs['SQ_INSTS_VALU'] / max(1, cs['SQ_INSTS_MFMA']):>18.2f}")
         out.append("")

@@ -44,6 +44,20 @@ def test_trace_table_and_bench_quote(tmp_path):
     assert "#   value 12.5 TFLOP/s, kernel_us mean 301.0 median 200.5 min 99.0" in lines
 
 
+def test_bench_quote_with_peak_check(tmp_path):
+    line = {"metric": "m", "value": 900.0, "unit": "TFLOP/s", "ms_per_step": 0.5,
+            "config": {"workload": "w1", "path": "fa_fwd", "kernel": "K"},
+            "kernel_us": {"mean": 499.0, "median": 498.0, "min": 490.0},
+            "peak_check": {"mfma_loop_tflops": 1800.0, "mfma_loop_clock_ghz": 1.8,
+                           "derived_peak_tflops": 2516.6}}
+    f = tmp_path / "bench.out"
+    f.write_text(json.dumps(line) + "\n")
+    q = rocprof_summary.bench_of_run(str(f))
+    assert "#   ms_per_step 0.5" in q
+    assert q[-1] == ("#   peak_check: bf16 MFMA loop on random operands 1800.0 TFLOP/s at 1.8 GHz "
+                     "(derived peak 2516.6), the run's value is 0.500 of it")
+
+
 def test_bench_quote_missing_line(tmp_path):
     f = tmp_path / "bench.out"
     f.write_text("no json here\n")
