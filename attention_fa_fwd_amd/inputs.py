@@ -135,6 +135,29 @@ def make_qkv_fp8qkv(B, Hq, Hkv, Sq, Skv, D, seed=0):
     return q8, k8, v8, qd, kd, vd
 
 
+def make_rising_scores(dtype, B=1, Hq=4, Hkv=2, S=320, D=128, seed=5):
+    """Queries and keys built so that scores rise steadily along the keys, plus one outlier.
+
+    With a random unit direction u: q = 3 u + 0.1 N(0,1) noise; key j = r_j u + 0.1 noise with
+    r_j rising linearly from 0 to 80 over the S keys, except key 250 (when S > 250), set to
+    100 u; v is N(0,1).  At scale 0.5 the scores reach about 150, so a row's maximum grows
+    from one key block to the next and the outlier dominates every row that sees it.
+    Returns (q, k, v) rounded to ``dtype``."""
+    if isinstance(dtype, str):
+        dtype = DTYPES[dtype]
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    u = torch.randn(D, generator=g)
+    u = u / u.norm()
+    q = 3.0 * u + 0.1 * torch.randn((B, Hq, S, D), generator=g)
+    ramp = torch.linspace(0.0, 80.0, S)
+    k = ramp[None, None, :, None] * u + 0.1 * torch.randn((B, Hkv, S, D), generator=g)
+    if S > 250:
+        k[:, :, 250, :] = 100.0 * u
+    v = torch.randn((B, Hkv, S, D), generator=g)
+    return tuple(t.to(dtype).contiguous() for t in (q, k, v))
+
+
 def make_workload(name, seed=0):
     """Inputs and call arguments for a named workload: (q, k, v, kwargs)."""
     w = dict(WORKLOADS[name] if name in WORKLOADS else SWEEP_WORKLOADS[name])

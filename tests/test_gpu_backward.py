@@ -5,8 +5,9 @@ TOL_REL * max(max |g_oracle|, 0.05 * the largest of the three gradients' maxima)
 TOL_REL = 4e-3 (fp16) and 1.6e-2 (bf16).  A CPU simulation
 of the kernels' arithmetic (P and dS rounded to the input type before their products, fp32
 accumulation, outputs rounded, D from the rounded forward output) stays below 40% of that
-(tests/test_tolerance_backward.py).  The forward pass that provides out and lse is the
-library's own fa_fwd on the same inputs.
+(tests/test_tolerance_backward.py).  On the rising-score input, far from N(0,1), the bound
+is instead derived elementwise from the same rounding steps (tests/bwd_bound.py).  The
+forward pass that provides out and lse is the library's own fa_fwd on the same inputs.
 """
 
 from __future__ import annotations
@@ -20,7 +21,8 @@ import torch
 
 import attention_fa_fwd_amd as fa
 import oracle
-from attention_fa_fwd_amd.inputs import DTYPES, make_qkv
+from attention_fa_fwd_amd.inputs import DTYPES, make_qkv, make_rising_scores
+from tests.bwd_bound import check_within, rounding_bound, rounding_model
 
 pytestmark = pytest.mark.gpu
 
@@ -155,6 +157,34 @@ def test_backward_headline_sampled():
         bound = TOL_REL[q.dtype] * max(float(np.max(np.abs(r))), 0.05 * top)
         _say(nm, f"err {err:.3e} bound {bound:.3e}")
         assert err <= bound, f"{nm} err {err:.3e} > {bound:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 64)])
+def test_backward_rising_scores(dtype, causal, window):
+    """Scores rising along the keys up to about 150, with one outlier key (the forward's
+    rising-score input, GQA 2): rows whose softmax is nearly one-hot make dS = P (dP - D) a
+    difference of nearly equal numbers, so the gradients' error is set by where the kernels
+    round (the stored O that D comes from, P and dS rounded before their products), not by a
+    fixed fraction of the gradient.  Every element must lie within the bound derived from those
+    rounding steps (tests/bwd_bound.py), and each gradient's largest error within 3x that of a
+    CPU model of the same steps (plus 1% of the relative tolerance at the largest gradient)."""
+    q, k, v = make_rising_scores(dtype)
+    do = make_dout(q.shape, DTYPES[dtype], 77)
+    _say("rising scores backward", dtype, "causal", causal, "window", window)
+    got = run_bwd(q, k, v, do, 0.5, causal, 0, window)
+    ref = oracle.attention_backward_blocked(q.double().numpy(), k.double().numpy(),
+                                            v.double().numpy(), do.double().numpy(),
+                                            0.5, causal, 0, window)
+    bounds = rounding_bound(q, k, v, do, 0.5, causal, 0, window)
+    model = rounding_model(q, k, v, do, 0.5, causal, 0, window)
+    top = max(float(np.max(np.abs(r))) for r in ref)
+    floor = 0.01 * TOL_REL[q.dtype] * top
+    for name, err, ratio, lim in check_within(got, ref, bounds, model, factor=3.0, floor=floor):
+        m = float(np.max(np.abs(ref[("dq", "dk", "dv").index(name)])))
+        _say(name, f"err {err:.3e} (max |g| {m:.3e}), worst err/bound {ratio:.3f}, measured limit {lim:.3e}")
+        assert ratio <= 1.0, f"{name}: error {ratio:.2f}x the derived bound"
+        assert err <= lim, f"{name}: err {err:.3e} > 3x the rounding model's + floor = {lim:.3e}"
 
 
 def test_backward_deterministic():

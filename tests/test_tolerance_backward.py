@@ -1,11 +1,17 @@
-"""The backward tolerance is reachable by the kernels' arithmetic.
+"""The backward tolerances are reachable by the kernels' arithmetic, and the derived bound holds.
 
-A CPU simulation of fa_bwd's arithmetic -- fp32 scores from the rounded inputs, P from the
-forward's fp32 LSE, D from the forward output rounded to the input type, P and dS rounded
-to the input type (round to nearest even) before their products, fp32 accumulation,
-gradients rounded to the input type -- is compared with the fp64 oracle.  Its error (worst
-4.3e-3 of max |g| for bf16, 7e-4 for fp16) must stay below 40% of the tolerance the GPU
-parity tests use, so that a failing GPU test points at the kernels rather than at the bound.
+A CPU model of fa_bwd's rounding steps (tests/bwd_bound.py: fp32 scores from the rounded
+inputs, P from an accurate LSE, the forward output as fl(fl(P) V), D from it, P and dS
+rounded to the input type before their products, fp32 accumulation, gradients rounded) is
+compared with the fp64 oracle:
+
+* on N(0,1) inputs its error must stay below 40% of the relative tolerance the GPU parity
+  tests use, so that a failing GPU test points at the kernels rather than at the bound;
+* on every input, including the rising-score input whose near one-hot rows make dS a
+  difference of nearly equal numbers, it must stay below half of the elementwise bound
+  derived from the same rounding steps (``rounding_bound``);
+* each of five planted mistakes in the model (D dropped, D's sign flipped, dK without the
+  scale, dQ from the wrong key, dV from dS) must exceed that bound somewhere.
 """
 
 from __future__ import annotations
@@ -17,30 +23,10 @@ import pytest
 import torch
 
 import oracle
-from attention_fa_fwd_amd.inputs import make_qkv
+from attention_fa_fwd_amd.inputs import make_qkv, make_rising_scores
+from tests.bwd_bound import check_within, rounding_bound, rounding_model
 
 TOL_REL = {"fp16": 4e-3, "bf16": 1.6e-2}
-
-
-def _simulate(q, k, v, do, scale, dt):
-    qf, kf, vf, dof = q.float(), k.float(), v.float(), do.float()
-    O, L = oracle.attention_blocked(q.double().numpy(), k.double().numpy(), v.double().numpy(),
-                                    scale, True, 0)
-    Ob = torch.from_numpy(O).to(dt).float()
-    Lf = torch.from_numpy(L).float()
-    s = torch.matmul(qf, kf.transpose(-1, -2).contiguous())
-    Sq, Skv = s.shape[-2:]
-    mask = torch.arange(Skv)[None, :] <= torch.arange(Sq)[:, None]
-    c = scale / math.log(2.0)
-    p = torch.exp2(s * c - Lf[..., None] / math.log(2.0)).masked_fill(~mask, 0.0)
-    Dr = (dof * Ob).sum(-1, keepdim=True)
-    dp = torch.matmul(dof, vf.transpose(-1, -2).contiguous())
-    ds = p * (dp - Dr)
-    pb, dsb = p.to(dt).float(), ds.to(dt).float()
-    dv = torch.matmul(pb.transpose(-1, -2).contiguous(), dof).to(dt)
-    dq = (scale * torch.matmul(dsb, kf)).to(dt)
-    dk = (scale * torch.matmul(dsb.transpose(-1, -2).contiguous(), qf)).to(dt)
-    return dq, dk, dv
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
@@ -51,10 +37,56 @@ def test_backward_tolerance_headroom(dtype):
         q, k, v = make_qkv(1, 4, 4, 192, 192, 128, dtype, seed)
         g = torch.Generator().manual_seed(500 + seed)
         do = torch.randn(q.shape, generator=g).to(dt)
-        sim = _simulate(q, k, v, do, 1 / math.sqrt(128), dt)
+        sim = rounding_model(q, k, v, do, 1 / math.sqrt(128), True)
         ref = oracle.attention_backward_blocked(q.double().numpy(), k.double().numpy(),
                                                 v.double().numpy(), do.double().numpy(),
                                                 1 / math.sqrt(128), True, 0)
         for a, r in zip(sim, ref):
             worst = max(worst, float(np.max(np.abs(a.double().numpy() - r)) / np.max(np.abs(r))))
     assert worst < 0.4 * TOL_REL[dtype], worst
+
+
+def _cases(dtype):
+    dt = {"fp16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    out = []
+    for causal in (True, False):
+        q, k, v = make_rising_scores(dtype)
+        do = torch.randn(q.shape, generator=torch.Generator().manual_seed(7)).to(dt)
+        out.append((f"rising causal={causal}", q, k, v, do, 0.5, causal, 0, 0))
+    q, k, v = make_qkv(1, 8, 2, 200, 300, 128, dtype, 11)
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(8)).to(dt)
+    out.append(("N(0,1) GQA 4, input_pos 40", q, k, v, do, 1 / math.sqrt(128), True, 40, 0))
+    q, k, v = make_qkv(1, 4, 4, 150, 150, 64, dtype, 12)
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(9)).to(dt)
+    out.append(("N(0,1) window 33", q, k, v, do, 0.125, True, 0, 33))
+    return out
+
+
+def _oracle(q, k, v, do, scale, causal, pos, window):
+    return oracle.attention_backward_blocked(q.double().numpy(), k.double().numpy(),
+                                             v.double().numpy(), do.double().numpy(),
+                                             scale, causal, pos, window)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_derived_bound_holds_for_the_rounding_model(dtype):
+    for what, q, k, v, do, scale, causal, pos, window in _cases(dtype):
+        ref = _oracle(q, k, v, do, scale, causal, pos, window)
+        bounds = rounding_bound(q, k, v, do, scale, causal, pos, window)
+        model = rounding_model(q, k, v, do, scale, causal, pos, window)
+        for name, err, ratio, _ in check_within(model, ref, bounds):
+            assert ratio < 0.5, f"{what} {name}: model error reaches {ratio:.2f} of the bound"
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("mistake", ["no_d", "d_sign", "dk_no_scale", "dq_keys_shifted",
+                                     "dv_from_ds"])
+def test_derived_bound_catches_planted_mistakes(dtype, mistake):
+    caught = []
+    for what, q, k, v, do, scale, causal, pos, window in _cases(dtype):
+        ref = _oracle(q, k, v, do, scale, causal, pos, window)
+        bounds = rounding_bound(q, k, v, do, scale, causal, pos, window)
+        bad = rounding_model(q, k, v, do, scale, causal, pos, window, mistake=mistake)
+        caught.append(max(r[2] for r in check_within(bad, ref, bounds)) > 1.0)
+    # the rising-score causal case and both N(0,1) cases must each catch it
+    assert caught[0] and caught[2] and caught[3], caught
