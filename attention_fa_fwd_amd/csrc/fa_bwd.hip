@@ -59,8 +59,8 @@ hipError_t launch_all(const BwdParams& p, int causal, hipStream_t s) {
     pq.n_tiles = (p.Sq + 127) / 128;
     const dim3 gk((unsigned)((long long)pk.n_tiles * p.B * p.Hkv * p.gsplit));
     const dim3 gq((unsigned)((long long)pq.n_tiles * p.B * p.Hq));
-    if (causal) hipLaunchKernelGGL((fa::fa_bwd_kernel<D, true, BF16, fa::BWD_DKDV>), gk, dim3(256), 0, s, pk);
-    else hipLaunchKernelGGL((fa::fa_bwd_kernel<D, false, BF16, fa::BWD_DKDV>), gk, dim3(256), 0, s, pk);
+    if (causal) hipLaunchKernelGGL((fa::fa_bwd_dkdv_pair_kernel<D, true, BF16>), gk, dim3(512), 0, s, pk);
+    else hipLaunchKernelGGL((fa::fa_bwd_dkdv_pair_kernel<D, false, BF16>), gk, dim3(512), 0, s, pk);
     if (p.gsplit > 1) {
         const size_t n = (size_t)p.B * p.Hkv * p.Skv * D;
         const size_t threads = n / 4;   // 2 tensors x n / 8
@@ -68,8 +68,8 @@ hipError_t launch_all(const BwdParams& p, int causal, hipStream_t s) {
         hipLaunchKernelGGL((fa::fa_bwd_reduce_kernel<BF16>), gr, dim3(256), 0, s, (const float*)p.part, p.dk,
                            p.dv, n, p.gsplit, p.scale);
     }
-    if (causal) hipLaunchKernelGGL((fa::fa_bwd_kernel<D, true, BF16, fa::BWD_DQ>), gq, dim3(256), 0, s, pq);
-    else hipLaunchKernelGGL((fa::fa_bwd_kernel<D, false, BF16, fa::BWD_DQ>), gq, dim3(256), 0, s, pq);
+    if (causal) hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<D, true, BF16>), gq, dim3(256), 0, s, pq);
+    else hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<D, false, BF16>), gq, dim3(256), 0, s, pq);
     return hipGetLastError();
 }
 
