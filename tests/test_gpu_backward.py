@@ -82,6 +82,10 @@ BWD_CASES = [
     (1, 6, 2, 200, 300, 128, True, 40, 0),     # GQA 3: odd group
     (1, 12, 2, 150, 150, 64, True, 0, 0),      # GQA 6
     (1, 21, 3, 96, 200, 128, False, 0, 0),     # GQA 7, non-causal
+    # GQA 8 at head dim 128, larger grids
+    (2, 32, 4, 1000, 1000, 128, True, 0, 0),   # ragged query tail
+    (2, 64, 8, 520, 700, 128, True, 180, 96),  # offset and sliding window
+    (4, 64, 8, 300, 200, 128, False, 0, 0),    # non-causal, Sq > Skv
 ]
 
 
