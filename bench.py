@@ -290,13 +290,15 @@ def _blas_threads():
         return None
 
 
-def cpu_baseline(name, min_s=10.0, backward=False):
+def cpu_baseline(name, min_s=10.0, backward=False, unit="TFLOP/s"):
     """The fp64 oracle of the timed path (forward, fp8 forward or backward) on whole GQA
     groups (one K/V head and its query heads) of the workload, one group after another until
     at least ``min_s`` seconds of CPU work have run or the workload is exhausted (a bounded
     sample; every group has the same shape).  BLAS runs on every core the process may use
     (os.sched_getaffinity); ``cores`` is the size of the BLAS pool that ran, next to that
-    count.  The smallest workload also gets the single-core pure-Python form."""
+    count.  The rate is in the bench line's own unit: TFLOP/s under the same FLOP rule, or
+    for a decoding line GB/s of the same algorithmic bytes.  The smallest workload also gets
+    the single-core pure-Python form."""
     import numpy as np
     import torch
 
@@ -349,11 +351,15 @@ def cpu_baseline(name, min_s=10.0, backward=False):
     if limiter is not None:
         limiter.restore_original_limits()
     ws = dict(w, B=1, Hq=G, Hkv=1)
-    flops = literal_flops(ws) * (2.5 if backward else 1.0)
     form = ("fp8 forward" if fp8 else "backward" if backward else "forward") + " oracle (NumPy, fp64)"
-    out = dict(value=done * flops / dt / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+    if unit == "GB/s":
+        value, rule = done * algorithmic_bytes(ws, fp8) / dt / 1e9, "same algorithmic byte count"
+    else:
+        value = done * literal_flops(ws) * (2.5 if backward else 1.0) / dt / 1e12
+        rule = "same FLOP count rule"
+    out = dict(value=value, unit=unit, cores=int(threads), kind="oracle",
                sample=f"{form}: {done} of the {len(groups)} GQA groups (one K/V head and its {G} "
-                      f"query heads each) of {name}; {dt:.1f} s wall; same FLOP count rule",
+                      f"query heads each) of {name}; {dt:.1f} s wall; {rule}",
                wall_s=round(dt, 3), affinity_cores=affinity)
     if w["B"] * w["Hq"] * w["Sq"] * w["Skv"] <= 1 << 16 and not fp8 and not backward:
         # the pure-Python loops, one core, on the whole (tiny) workload
@@ -442,7 +448,7 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False, bac
                                            / (ms_step * 1e-3) / 1e12, 2)
     if with_cpu:
         log("timing the fp64 CPU oracle on a bounded sample ...")
-        line["cpu_baseline"] = cpu_baseline(name, backward=backward)
+        line["cpu_baseline"] = cpu_baseline(name, backward=backward, unit=unit)
     return line
 
 

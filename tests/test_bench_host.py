@@ -172,3 +172,22 @@ def test_every_named_workload_resolves(monkeypatch):
     for S, w in zip((1024, 2048, 4096, 8192, 16384), by_len):
         assert (w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"], w["causal"]) == (4, 32, 32, S, S, 128, True)
         assert bench.literal_flops(w) == 4.0 * 4 * 32 * S * S * 128 / 2
+
+
+def test_cpu_baseline_units(monkeypatch):
+    """The CPU oracle's rate is reported in the bench line's unit: GB/s of the algorithmic
+    bytes for a decoding line, TFLOP/s under the FLOP rule otherwise (here on a tiny
+    decoding-like workload registered for the test)."""
+    from attention_fa_fwd_amd import inputs
+
+    shape = dict(B=2, Hq=4, Hkv=2, Sq=1, Skv=96, D=64, dtype="fp16", causal=True, input_pos=95)
+    monkeypatch.setitem(inputs.WORKLOADS, "tiny_decode_test", shape)
+    gb = bench.cpu_baseline("tiny_decode_test", min_s=0.0, unit="GB/s")
+    assert gb["unit"] == "GB/s" and gb["kind"] == "oracle" and gb["value"] > 0
+    assert "algorithmic byte" in gb["sample"]
+    one_group = dict(shape, B=1, Hq=2, Hkv=1)
+    # min_s = 0: exactly one group ran
+    assert gb["value"] == pytest.approx(bench.algorithmic_bytes(one_group) / 1e9 / gb["wall_s"], rel=0.05) \
+        or gb["wall_s"] < 0.01
+    tf = bench.cpu_baseline("tiny_decode_test", min_s=0.0)
+    assert tf["unit"] == "TFLOP/s" and "FLOP count rule" in tf["sample"]
