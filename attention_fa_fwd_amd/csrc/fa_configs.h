@@ -7,10 +7,11 @@
 #pragma once
 
 // Head dim 64: 64-key tiles; 4 or 8 waves (WPH position blocks x HPW query heads).
-#define FA_SHAPES_BN64(X, D, C, B, CN, TN)                                                  \
-    X(D, 64, 1, 1, 4, C, B, false, false, CN, TN) X(D, 64, 1, 2, 4, C, B, false, false, CN, TN) \
-    X(D, 64, 1, 2, 2, C, B, false, false, CN, TN) X(D, 64, 1, 4, 2, C, B, false, false, CN, TN) \
-    X(D, 64, 1, 4, 1, C, B, false, false, CN, TN) X(D, 64, 1, 8, 1, C, B, false, false, CN, TN)
+#define FA_SHAPES_BN64Q(X, D, C, B, Q, V8, CN, TN)                                          \
+    X(D, 64, 1, 1, 4, C, B, Q, V8, CN, TN) X(D, 64, 1, 2, 4, C, B, Q, V8, CN, TN)             \
+    X(D, 64, 1, 2, 2, C, B, Q, V8, CN, TN) X(D, 64, 1, 4, 2, C, B, Q, V8, CN, TN)             \
+    X(D, 64, 1, 4, 1, C, B, Q, V8, CN, TN) X(D, 64, 1, 8, 1, C, B, Q, V8, CN, TN)
+#define FA_SHAPES_BN64(X, D, C, B, CN, TN) FA_SHAPES_BN64Q(X, D, C, B, false, false, CN, TN)
 
 // Head dim 128: 32-key tiles (a 32 x 64 tile is too small to split over 512 threads, and
 // with three LDS buffers and three register sets a 64-key tile does not fit two waves per
@@ -48,6 +49,19 @@
     FA_SHAPES_BN32(X, true, false, true, true, "causal", "fp8qkv_fp16")                     \
     FA_SHAPES_BN32(X, false, false, true, true, "full", "fp8qkv_fp16")
 
+// fp8 at head dim 64 (64-key tiles): "fp8qk" and "fp8qkv", bf16 and fp16 output.
+#define FA_LIST_FP8_D64(X)                                                                  \
+    FA_SHAPES_BN64Q(X, 64, true, true, true, false, "causal", "fp8qk_bf16")                 \
+    FA_SHAPES_BN64Q(X, 64, false, true, true, false, "full", "fp8qk_bf16")                  \
+    FA_SHAPES_BN64Q(X, 64, true, false, true, false, "causal", "fp8qk_fp16")                \
+    FA_SHAPES_BN64Q(X, 64, false, false, true, false, "full", "fp8qk_fp16")
+#define FA_LIST_FP8QKV_D64(X)                                                               \
+    FA_SHAPES_BN64Q(X, 64, true, true, true, true, "causal", "fp8qkv_bf16")                 \
+    FA_SHAPES_BN64Q(X, 64, false, true, true, true, "full", "fp8qkv_bf16")                  \
+    FA_SHAPES_BN64Q(X, 64, true, false, true, true, "causal", "fp8qkv_fp16")                \
+    FA_SHAPES_BN64Q(X, 64, false, false, true, true, "full", "fp8qkv_fp16")
+
 #define FA_LIST_ALL(X)                                                                      \
     FA_LIST_D64(X) FA_LIST_D128_BF16(X) FA_LIST_D128_FP16(X) FA_LIST_FP8_BF16(X)            \
-    FA_LIST_FP8_FP16(X) FA_LIST_FP8QKV_BF16(X) FA_LIST_FP8QKV_FP16(X)
+    FA_LIST_FP8_FP16(X) FA_LIST_FP8QKV_BF16(X) FA_LIST_FP8QKV_FP16(X) FA_LIST_FP8_D64(X)    \
+    FA_LIST_FP8QKV_D64(X)

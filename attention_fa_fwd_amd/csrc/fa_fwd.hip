@@ -107,7 +107,6 @@ int validate(const Call& a) {
     if (qe > 1125899906842624.0 || ke > 1125899906842624.0) return FA_ERR_INVALID_SHAPE;
     if (Hq % Hkv != 0) return FA_ERR_HEAD_GROUP;
     if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
-    if (a.qk8 && D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
     if (a.dtype != FA_DTYPE_FP16 && a.dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
     if (!finite_pos(a.scale)) return FA_ERR_INVALID_SCALE;
     if (a.qk8 && (!finite_pos(a.q_descale) || !finite_pos(a.k_descale))) return FA_ERR_INVALID_SCALE;
@@ -502,7 +501,7 @@ int fa_splitkv_num_splits_fp8(int B, int Hq, int Hkv, int Sq, int Skv, int D, in
                               int input_pos, int window, int v_dtype, int config) {
     if (B < 0 || Hq < 0 || Sq < 0 || Hkv < 1 || Skv < 1) return FA_ERR_INVALID_SHAPE;
     if (Hq % Hkv != 0) return FA_ERR_HEAD_GROUP;
-    if (D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
     if (v_dtype != FA_DTYPE_FP16 && v_dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
     if (input_pos < 0 || (long long)input_pos + Sq > INT_MAX) return FA_ERR_INVALID_INPUT_POS;
     if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_WINDOW;
@@ -537,7 +536,7 @@ int fa_splitkv_num_splits_fp8qkv(int B, int Hq, int Hkv, int Sq, int Skv, int D,
                                  int input_pos, int window, int out_dtype, int config) {
     if (B < 0 || Hq < 0 || Sq < 0 || Hkv < 1 || Skv < 1) return FA_ERR_INVALID_SHAPE;
     if (Hq % Hkv != 0) return FA_ERR_HEAD_GROUP;
-    if (D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
     if (out_dtype != FA_DTYPE_FP16 && out_dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
     if (input_pos < 0 || (long long)input_pos + Sq > INT_MAX) return FA_ERR_INVALID_INPUT_POS;
     if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_WINDOW;
@@ -584,7 +583,7 @@ int fa_select_config(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
 int fa_select_config_fp8(int B, int Hq, int Hkv, int Sq, int D, int causal, int v_dtype) {
     if (B < 0 || Hq < 0 || Sq < 0 || Hkv < 1) return FA_ERR_INVALID_SHAPE;
     if (Hq % Hkv != 0) return FA_ERR_HEAD_GROUP;
-    if (D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
     if (v_dtype != FA_DTYPE_FP16 && v_dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED_DTYPE;
     const int c = select(B, Hq, Hkv, Sq, D, causal, v_dtype, 1);
     return c < 0 ? FA_ERR_INVALID_CONFIG : c;

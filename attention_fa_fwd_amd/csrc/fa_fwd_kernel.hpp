@@ -123,7 +123,8 @@ struct Cfg {
     static_assert(BN == 32 || BN == 64, "key tile");
     static_assert(QB == 1 || QB == 2, "query blocks per wave");
     static_assert(NW == 4 || NW == 8, "waves per workgroup");
-    static_assert(!QK8 || (D == 128 && BN == 32 && QB == 1), "fp8 Q/K: head dim 128, 32-key tiles");
+    static_assert(!QK8 || ((D == 128 && BN == 32) || (D == 64 && BN == 64)) && QB == 1,
+                  "fp8 Q/K: head dim 128 with 32-key tiles or head dim 64 with 64-key tiles");
     static_assert(!V8 || QK8, "fp8 V comes with fp8 Q and K");
 };
 
@@ -243,7 +244,8 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, unsi
 template <int D>
 __device__ __forceinline__ int k_swz(int row) {
     if constexpr (D == 128) return row & 15;
-    else return (row & 7) ^ ((row >> 3) & 1);
+    else if constexpr (D == 64) return (row & 7) ^ ((row >> 3) & 1);
+    else return (row >> 2) & 3;   // 64-byte rows (fp8, head dim 64): 16 rows on 16 bank groups
 }
 // V rows: a swizzle taken from key mod 4.  A transposed read serves 32 lanes per pass: 4
 // consecutive keys x 4 chunks x 16 bytes = 256 bytes, which must fall on the 64 distinct
@@ -267,8 +269,13 @@ __device__ __forceinline__ int v_swz(int row) {
 // or {4..7, 12..15}) x 2 chunks x 16 bytes.  Chunk XOR 2 * (bit 1 of r | bit 3 of r << 1)
 // gives the four even and the four odd rows of each half distinct 32-byte bank windows,
 // so the 256 bytes of a half land on the 64 banks once.
+// fp8 V rows of 64 bytes (head dim 64, 4 chunks): rows r and r + 8 share banks, so chunk XOR
+// 2 * (bit 3 of r) puts them on opposite chunk pairs; the other rows of a half already fall
+// on distinct banks.
+template <int D>
 __device__ __forceinline__ int v8_swz(int row) {
-    return 2 * (((row >> 1) & 1) | (((row >> 3) & 1) << 1));
+    if constexpr (D == 128) return 2 * (((row >> 1) & 1) | (((row >> 3) & 1) << 1));
+    else return 2 * ((row >> 3) & 1);
 }
 
 template <class C>
@@ -431,8 +438,9 @@ void fa_fwd_kernel(Params p) {
     static_assert((64 * NWK / CPRK) % 16 == 0, "K load stride keeps the swizzle");
     constexpr int LOAD_STRIDE = 64 * NWV * 16;     // bytes of V tile per load i
     constexpr int LOAD_STRIDE_K = 64 * NWK * 16;   // bytes of K tile per load i
-    // K rows of 128 bytes (fp8) use the 8-chunk swizzle of the head-dim-64 bf16 layout.
-    constexpr int KSWZ_D = QK8 ? 64 : D;
+    // fp8 K rows (D bytes) use the swizzle of a bf16 row of the same length: head dim 128
+    // takes the 8-chunk map of the head-dim-64 layout, head dim 64 a 4-chunk map.
+    constexpr int KSWZ_D = QK8 ? D / 2 : D;
     auto kswz = [&](int row) { return k_swz<KSWZ_D>(row); };
     // Waves that load V tiles are the last NWV; those that load K the first NWK.
     const int vw = w - (C::NW - NWV);
@@ -442,7 +450,7 @@ void fa_fwd_kernel(Params p) {
     {
         const int slot = (ld_v ? vw : 0) * 64 + lane;
         const int row = slot / CPR, pc = slot % CPR;
-        if constexpr (V8) vsrc = row * ROWV + ((pc ^ v8_swz(row)) << 4);
+        if constexpr (V8) vsrc = row * ROWV + ((pc ^ v8_swz<D>(row)) << 4);
         else vsrc = row * ROWV + ((pc ^ v_swz<D>(row)) << 4);
         const int slotk = w * 64 + lane;
         const int rowk = slotk / CPRK, pck = slotk % CPRK;
@@ -504,7 +512,7 @@ void fa_fwd_kernel(Params p) {
         const int key = 4 * (g8 >> 1) + j8 + (j8 >= 4 ? 4 : 0);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-            voff8[db] = key * ROWV + (((2 * db + (g8 & 1)) ^ v8_swz(key)) << 4) + 8 * p8;
+            voff8[db] = key * ROWV + (((2 * db + (g8 & 1)) ^ v8_swz<D>(key)) << 4) + 8 * p8;
     }
 
     // S^T = K Q^T of the tile in K buffer `kb`.

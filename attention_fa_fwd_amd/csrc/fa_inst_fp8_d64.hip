@@ -1,0 +1,7 @@
+// fa_inst_fp8_d64.hip -- compiles the forward-kernel configurations of FA_LIST_FP8_D64
+// (fa_configs.h): fp8 E4M3 queries and keys at head dim 64, bf16 / fp16 values; the dispatch table in fa_fwd.hip refers to them.
+#define FA_LAUNCH_DEFINE
+#include "fa_launch.hpp"
+#include "fa_configs.h"
+
+FA_LIST_FP8_D64(FA_INSTANTIATE)

@@ -77,6 +77,11 @@ FP8_WORKLOADS = {
                                                     fp8v=True),
     "gqa8_causal_s8192_d128_fp8qkv_bf16": dict(B=1, Hq=32, Hkv=4, Sq=8192, Skv=8192, D=128,
                                                dtype="bf16", causal=True, input_pos=0, fp8v=True),
+    # Head dim 64 in fp8: the GQA-4 causal shape of the head-dim-64 bf16 workload.
+    "gqa4_causal_s4096_d64_fp8qk_bf16": dict(B=1, Hq=32, Hkv=8, Sq=4096, Skv=4096, D=64,
+                                             dtype="bf16", causal=True, input_pos=0),
+    "gqa4_causal_s4096_d64_fp8qkv_bf16": dict(B=1, Hq=32, Hkv=8, Sq=4096, Skv=4096, D=64,
+                                              dtype="bf16", causal=True, input_pos=0, fp8v=True),
 }
 
 

@@ -129,7 +129,7 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* out, float*
  * with fp32 accumulation, so the scores are the exact products of the fp8 values up to
  * fp32 rounding; P V stays on the fp16 / bf16 MFMA.
  *
- *   D          128 only (FA_ERR_UNSUPPORTED_HEAD_DIM otherwise).
+ *   D          64 or 128 (FA_ERR_UNSUPPORTED_HEAD_DIM otherwise).
  *   q_descale, k_descale   finite and > 0 (FA_ERR_INVALID_SCALE), checked after scale.
  *   window     0 = none, >= 1 = sliding window (needs causal), as for fa_fwd_splitkv.
  *   config     -1 = the dispatch table (fa_select_config_fp8), else an fp8 configuration.
@@ -247,7 +247,7 @@ int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* ou
  *   out          [B, Hq, Sq, D] of out_dtype (an fa_dtype); lse as for fa_fwd.
  *   q_descale, k_descale, v_descale   finite and > 0 (FA_ERR_INVALID_SCALE), checked
  *                after scale, in this order.
- *   D            128 only (FA_ERR_UNSUPPORTED_HEAD_DIM otherwise).
+ *   D            64 or 128 (FA_ERR_UNSUPPORTED_HEAD_DIM otherwise).
  *   other arguments as for fa_fwd_fp8 (config: an "fp8qkv" configuration or -1).
  * Checks and errors as for fa_fwd_fp8.
  */

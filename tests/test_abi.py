@@ -282,7 +282,7 @@ def call_fp8(lib, qd=0.01, kd=0.02, window=0, config=-1, **over):
 
 
 def test_fp8_validation(lib):
-    assert call_fp8(lib, D=64) == -4                      # head dim 128 only
+    assert call_fp8(lib, D=96) == -4                      # head dim 64 or 128
     for bad in (0.0, -1.0, float("inf"), float("nan")):
         assert call_fp8(lib, qd=bad) == -6
         assert call_fp8(lib, kd=bad) == -6
@@ -309,7 +309,7 @@ def call_split_fp8(lib, num_splits=2, ws=W, ws_bytes=1 << 28, qd=0.01, kd=0.02, 
 def test_fp8_splitkv_validation(lib):
     """fa_fwd_splitkv_fp8 runs fa_fwd_fp8's checks, then the split and workspace checks
     (no call here reaches a launch)."""
-    assert call_split_fp8(lib, D=64) == -4
+    assert call_split_fp8(lib, D=96) == -4
     assert call_split_fp8(lib, qd=float("nan")) == -6
     assert call_split_fp8(lib, kd=0.0) == -6
     assert call_split_fp8(lib, window=5, causal=0) == -14
@@ -332,7 +332,8 @@ def test_fp8_splitkv_num_splits(lib):
     f = lib.fa_splitkv_num_splits_fp8
     assert f(4, 32, 8, 1, 16384, 128, 1, 16383, 0, 1, -1) == 16
     assert f(1, 32, 4, 8192, 8192, 128, 1, 0, 0, 1, -1) == 1
-    assert f(4, 32, 8, 1, 16384, 64, 1, 16383, 0, 1, -1) == -4
+    assert f(4, 32, 8, 1, 16384, 64, 1, 16383, 0, 1, -1) == 16
+    assert f(4, 32, 8, 1, 16384, 96, 1, 16383, 0, 1, -1) == -4
     assert f(4, 32, 8, 1, 16384, 128, 1, 16383, 0, 3, -1) == -5
     assert fa.splitkv_num_splits_fp8(4, 32, 8, 1, 16384, 128, True, 16383, 1) == 16
 
@@ -340,7 +341,9 @@ def test_fp8_splitkv_num_splits(lib):
 def test_fp8_configs(lib):
     names = fa.config_names()
     fp8 = [i for i, nm in enumerate(names) if "_fp8qk_" in nm]
-    assert len(fp8) == 28 and all(names[i].startswith("D128_BN32_") for i in fp8)
+    assert len(fp8) == 52
+    assert sum(names[i].startswith("D128_BN32_") for i in fp8) == 28
+    assert sum(names[i].startswith("D64_BN64_") for i in fp8) == 24
     c = fa.select_config_fp8(1, 32, 4, 8192, 128, True, 1)
     assert names[c] == "D128_BN32_Mw1x32_WPH1_HPW8_causal_fp8qk_bf16"
     c = fa.select_config_fp8(1, 32, 32, 4096, 128, True, 0)
@@ -351,8 +354,10 @@ def test_fp8_configs(lib):
     args = [GOOD[x] for x in ("q", "k", "v", "out", "lse", "B", "Hq", "Hkv", "Sq", "Skv")] + \
         [128, GOOD["scale"], 1, 0, 1, None]
     assert lib.fa_fwd_config(*args, fp8[0]) == -10
+    c = fa.select_config_fp8(1, 32, 4, 8192, 64, True, 1)
+    assert names[c] == "D64_BN64_Mw1x32_WPH2_HPW4_causal_fp8qk_bf16"
     with pytest.raises(fa.FaError):
-        fa.select_config_fp8(1, 32, 4, 8192, 64, True, 1)
+        fa.select_config_fp8(1, 32, 4, 8192, 96, True, 1)
 
 
 def test_header_compiles_as_c99():

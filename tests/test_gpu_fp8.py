@@ -72,33 +72,39 @@ FP8_CASES = [
 ]
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("vdt", ["fp16", "bf16"])
 @pytest.mark.parametrize("case", FP8_CASES, ids=lambda c: "x".join(map(str, c)))
-def test_fp8_shapes(case, vdt):
+def test_fp8_shapes(case, vdt, D):
     B, Hq, Hkv, Sq, Skv, causal, pos, W = case
-    _say(case, vdt)
-    q8, k8, v, qd, kd = make_qkv_fp8(B, Hq, Hkv, Sq, Skv, 128, vdt, seed=sum(case) + 7)
-    scale = 1.0 / math.sqrt(128)
+    _say(case, vdt, D)
+    q8, k8, v, qd, kd = make_qkv_fp8(B, Hq, Hkv, Sq, Skv, D, vdt, seed=sum(case) + 7 + D)
+    scale = 1.0 / math.sqrt(D)
     out, lse = run(q8, k8, v, qd, kd, scale, causal, pos, W)
     O, L = oracle_fp8(q8, k8, v, scale, qd, kd, causal, pos, W)
-    check(O, L, out, lse, v.dtype, f"{case} {vdt}")
+    check(O, L, out, lse, v.dtype, f"{case} {vdt} D{D}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("vdt", ["fp16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_every_config(vdt, causal):
-    q8, k8, v, qd, kd = make_qkv_fp8(1, 16, 2, 333, 333, 128, vdt, seed=21)   # GQA 8: every shape applies
+def test_fp8_every_config(vdt, causal, D):
+    """Every compiled fp8 configuration of the head dim (seven shapes at 128, six at 64),
+    forced on one GQA-8 input."""
+    q8, k8, v, qd, kd = make_qkv_fp8(1, 16, 2, 333, 333, D, vdt, seed=21)   # GQA 8: every shape applies
     pos = 7 if causal else 0
     O, L = oracle_fp8(q8, k8, v, 0.09, qd, kd, causal, pos)
     tested = 0
     for cid, name in enumerate(fa.config_names()):
         if "_fp8qk_" not in name or (("_causal_" in name) != causal) or not name.endswith(vdt):
             continue
+        if not name.startswith(f"D{D}_"):
+            continue
         _say("config", name)
         out, lse = run(q8, k8, v, qd, kd, 0.09, causal, pos, config=cid)
         check(O, L, out, lse, v.dtype, name)
         tested += 1
-    assert tested == 7
+    assert tested == (7 if D == 128 else 6)
 
 
 def test_fp8_descale_invariance():
@@ -153,17 +159,18 @@ def run_split(q8, k8, v, qd, kd, scale, pos, W, splits):
     return out.cpu(), lse.cpu()
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("vdt", ["fp16", "bf16"])
 @pytest.mark.parametrize("case", FP8_SPLIT_CASES, ids=lambda c: "x".join(map(str, c)))
-def test_fp8_splitkv_shapes(case, vdt):
+def test_fp8_splitkv_shapes(case, vdt, D):
     """fa_fwd_splitkv_fp8: fp8 queries and keys over split key ranges, merged."""
     B, Hq, Hkv, Sq, Skv, pos, W, splits = case
-    _say("splitkv", case, vdt)
-    q8, k8, v, qd, kd = make_qkv_fp8(B, Hq, Hkv, Sq, Skv, 128, vdt, seed=sum(case) % 97)
-    scale = 1.0 / math.sqrt(128)
+    _say("splitkv", case, vdt, D)
+    q8, k8, v, qd, kd = make_qkv_fp8(B, Hq, Hkv, Sq, Skv, D, vdt, seed=(sum(case) + D) % 97)
+    scale = 1.0 / math.sqrt(D)
     out, lse = run_split(q8, k8, v, qd, kd, scale, pos, W, splits)
     O, L = oracle_fp8(q8, k8, v, scale, qd, kd, True, pos, W)
-    check(O, L, out, lse, v.dtype, f"{case} {vdt}")
+    check(O, L, out, lse, v.dtype, f"{case} {vdt} D{D}")
 
 
 def test_fp8_splitkv_one_split_is_fa_fwd_fp8():

@@ -84,33 +84,39 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("odt", ["fp16", "bf16"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
-def test_fp8qkv_shapes(case, odt):
+def test_fp8qkv_shapes(case, odt, D):
     B, Hq, Hkv, Sq, Skv, causal, pos, W = case
-    q8, k8, v8, qd, kd, vd = make_qkv_fp8qkv(B, Hq, Hkv, Sq, Skv, 128, seed=sum(case) + 11)
-    scale = 1.0 / math.sqrt(128)
+    _say(case, odt, D)
+    q8, k8, v8, qd, kd, vd = make_qkv_fp8qkv(B, Hq, Hkv, Sq, Skv, D, seed=sum(case) + 11 + D)
+    scale = 1.0 / math.sqrt(D)
     out, lse = run(q8, k8, v8, qd, kd, vd, DT[odt], scale, causal, pos, W)
     O, L = oracle_qkv(q8, k8, v8, scale, qd, kd, vd, causal, pos, W)
-    check(O, L, out, lse, DT[odt], f"{case} {odt}")
+    check(O, L, out, lse, DT[odt], f"{case} {odt} D{D}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("odt", ["fp16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8qkv_every_config(odt, causal):
-    """Every compiled fp8 Q/K/V configuration (seven shapes per output type and causality),
-    forced on one GQA-8 input."""
-    q8, k8, v8, qd, kd, vd = make_qkv_fp8qkv(1, 16, 2, 333, 333, 128, seed=31)
+def test_fp8qkv_every_config(odt, causal, D):
+    """Every compiled fp8 Q/K/V configuration of the head dim (seven shapes at 128, six at
+    64, per output type and causality), forced on one GQA-8 input."""
+    q8, k8, v8, qd, kd, vd = make_qkv_fp8qkv(1, 16, 2, 333, 333, D, seed=31)
     pos = 7 if causal else 0
     O, L = oracle_qkv(q8, k8, v8, 0.09, qd, kd, vd, causal, pos)
     tested = 0
     for cid, name in enumerate(fa.config_names()):
         if "_fp8qkv_" not in name or (("_causal_" in name) != causal) or not name.endswith(odt):
             continue
+        if not name.startswith(f"D{D}_"):
+            continue
+        _say("config", name)
         out, lse = run(q8, k8, v8, qd, kd, vd, DT[odt], 0.09, causal, pos, config=cid)
         check(O, L, out, lse, DT[odt], name)
         tested += 1
-    assert tested == 7
+    assert tested == (7 if D == 128 else 6)
 
 
 def test_fp8qkv_v_descale_doubles_output_exactly():
@@ -132,15 +138,17 @@ SPLIT_CASES = [
 ]
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("odt", ["fp16", "bf16"])
 @pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "x".join(map(str, c)))
-def test_fp8qkv_splitkv_shapes(case, odt):
+def test_fp8qkv_splitkv_shapes(case, odt, D):
     B, Hq, Hkv, Sq, Skv, pos, W, splits = case
-    q8, k8, v8, qd, kd, vd = make_qkv_fp8qkv(B, Hq, Hkv, Sq, Skv, 128, seed=sum(case) % 89)
-    scale = 1.0 / math.sqrt(128)
+    _say("split", case, odt, D)
+    q8, k8, v8, qd, kd, vd = make_qkv_fp8qkv(B, Hq, Hkv, Sq, Skv, D, seed=(sum(case) + D) % 89)
+    scale = 1.0 / math.sqrt(D)
     out, lse = run_split(q8, k8, v8, qd, kd, vd, DT[odt], scale, pos, W, splits)
     O, L = oracle_qkv(q8, k8, v8, scale, qd, kd, vd, True, pos, W)
-    check(O, L, out, lse, DT[odt], f"split {case} {odt}")
+    check(O, L, out, lse, DT[odt], f"split {case} {odt} D{D}")
 
 
 def test_fp8qkv_splitkv_one_split_is_fa_fwd_fp8qkv():
@@ -173,7 +181,7 @@ def test_fp8qkv_rejects_bad_arguments():
         with pytest.raises(fa.FaError) as e:
             fa.fa_fwd_fp8qkv(q8, k8, v8, qd, kd, bad)
         assert e.value.code == -6
-    q64 = torch.zeros(1, 2, 8, 64, dtype=torch.float8_e4m3fn, device=DEV)
+    q96 = torch.zeros(1, 2, 8, 96, dtype=torch.float8_e4m3fn, device=DEV)
     with pytest.raises(fa.FaError) as e:
-        fa.fa_fwd_fp8qkv(q64, q64, q64, 1.0, 1.0, 1.0)
+        fa.fa_fwd_fp8qkv(q96, q96, q96, 1.0, 1.0, 1.0)
     assert e.value.code == -4

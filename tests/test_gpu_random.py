@@ -35,9 +35,9 @@ def _say(*a):
     print("[random]", *a, file=sys.stderr, flush=True)
 
 
-def draw(rng, fp8=False, backward=False):
+def draw(rng, backward=False):
     """One random problem: (B, Hq, Hkv, Sq, Skv, D, dtype, causal, input_pos, window)."""
-    D = 128 if fp8 else int(rng.choice([64, 128]))
+    D = int(rng.choice([64, 128]))
     dtype = str(rng.choice(["fp16", "bf16"]))
     Hkv = int(rng.choice([1, 2, 4]))
     Hq = Hkv * int(rng.choice([1, 2, 3, 4, 6, 8]))
@@ -103,9 +103,9 @@ def test_random_splitkv(i):
 
 @pytest.mark.parametrize("i", range(N_CASES // 2))
 def test_random_fp8(i):
-    """fa_fwd_fp8 and fa_fwd_splitkv_fp8 on random problems (head dim 128)."""
+    """fa_fwd_fp8 and fa_fwd_splitkv_fp8 on random problems."""
     rng = np.random.default_rng(3000 + i)
-    B, Hq, Hkv, Sq, Skv, D, dt, causal, pos, W = draw(rng, fp8=True)
+    B, Hq, Hkv, Sq, Skv, D, dt, causal, pos, W = draw(rng)
     what = (B, Hq, Hkv, Sq, Skv, D, dt, causal, pos, W)
     _say("fp8", what)
     q8, k8, v, qd, kd = make_qkv_fp8(B, Hq, Hkv, Sq, Skv, D, dt, seed=200 + i)
@@ -125,9 +125,9 @@ def test_random_fp8(i):
 @pytest.mark.parametrize("i", range(N_CASES // 2))
 def test_random_fp8qkv(i):
     """fa_fwd_fp8qkv and fa_fwd_splitkv_fp8qkv (fp8 queries, keys and values) on random
-    problems (head dim 128); the drawn dtype is the output's."""
+    problems; the drawn dtype is the output's."""
     rng = np.random.default_rng(5000 + i)
-    B, Hq, Hkv, Sq, Skv, D, dt, causal, pos, W = draw(rng, fp8=True)
+    B, Hq, Hkv, Sq, Skv, D, dt, causal, pos, W = draw(rng)
     what = (B, Hq, Hkv, Sq, Skv, D, dt, causal, pos, W)
     _say("fp8qkv", what)
     q8, k8, v8, qd, kd, vd = make_qkv_fp8qkv(B, Hq, Hkv, Sq, Skv, D, seed=300 + i)
