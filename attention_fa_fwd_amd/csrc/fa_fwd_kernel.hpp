@@ -635,6 +635,11 @@ void fa_fwd_kernel(Params p) {
         if (do_sm) {
             if constexpr (MASKED) {
                 const int j0 = j * BN;
+                // A band tile that every row of this wave sees whole (below its diagonal, above
+                // its window edge, before the key tail) needs no mask: skip it for the wave.
+                const bool whole = j0 + BN - 1 <= (CAUSAL ? min(p.input_pos + qw0, p.Skv - 1) : p.Skv - 1) &&
+                                   (!win || j0 >= p.input_pos + qw0 + 32 * QB - p.window);
+                if (!whole)
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
                     const int qpos = p.input_pos + qw0 + qb * 32 + l32;
