@@ -104,7 +104,7 @@ struct Params {
 
 // Compile-time configuration of one kernel instance.
 template <int D_, int BN_, int QB_, int WPH_, int HPW_, bool CAUSAL_, bool BF16_, bool QK8_ = false,
-          bool V8_ = false>
+          bool V8_ = false, int KS_ = 1>
 struct Cfg {
     static constexpr int D = D_;        // head dim
     static constexpr int BN = BN_;      // keys per K/V tile
@@ -115,7 +115,10 @@ struct Cfg {
     static constexpr bool BF16 = BF16_;    // V / O element type: bf16, else fp16
     static constexpr bool QK8 = QK8_;      // Q and K in fp8 e4m3 (S = K Q^T on the fp8 MFMA)
     static constexpr bool V8 = V8_;        // V in fp8 e4m3 too (widened to BF16 ? bf16 : fp16)
-    static constexpr int NW = WPH * HPW;
+    static constexpr int KS = KS_;         // key parts: KS sets of WPH x HPW waves, each taking
+                                           // 1/KS of the key tiles, merged at the end
+    static constexpr int NWQ = WPH * HPW;  // waves per key part
+    static constexpr int NW = NWQ * KS;
     static constexpr int NT = 64 * NW;
     static constexpr int BMP = 32 * QB * WPH;   // query positions per workgroup
     static constexpr int WAVES_PER_SIMD = QB == 1 ? 2 : 1;  // register budget 256 / 512
@@ -126,6 +129,8 @@ struct Cfg {
     static_assert(!QK8 || ((D == 128 && BN == 32) || (D == 64 && BN == 64)) && QB == 1,
                   "fp8 Q/K: head dim 128 with 32-key tiles or head dim 64 with 64-key tiles");
     static_assert(!V8 || QK8, "fp8 V comes with fp8 Q and K");
+    static_assert(KS == 1 || (KS == 2 && !CAUSAL && !QK8 && QB == 1),
+                  "key parts: non-causal fp16 / bf16, one query block per wave");
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -293,14 +298,14 @@ void fa_fwd_kernel(Params p) {
     constexpr int TILE = BN * ROWV;      // bytes per V tile
     constexpr int CPR = ROWV / 16;       // 16-byte chunks per V row
     constexpr int NLV = BN * CPR / 64;   // 64-lane loads per V tile
-    constexpr int NWV = NLV < C::NW ? NLV : C::NW;   // waves that load V (the last NWV)
+    constexpr int NWV = NLV < C::NWQ ? NLV : C::NWQ; // waves of a key part that load V (its last NWV)
     constexpr int LD = NLV / NWV;        // V loads per loading thread
     static_assert(NLV % NWV == 0, "V tile loads per wave");
     constexpr int ROWK = QK8 ? D : ROWB; // bytes per K row
     constexpr int TILEK = BN * ROWK;     // bytes per K tile
     constexpr int CPRK = ROWK / 16;      // 16-byte chunks per K row
     constexpr int NLK = BN * CPRK / 64;  // 64-lane loads per K tile
-    constexpr int NWK = NLK < C::NW ? NLK : C::NW;   // waves that load K
+    constexpr int NWK = NLK < C::NWQ ? NLK : C::NWQ; // waves of a key part that load K
     constexpr int LDK = NLK / NWK;       // K loads per loading thread
     static_assert(NLK % NWK == 0, "K tile loads per wave");
     constexpr float P_LIMIT = 32768.0f;  // lazy max: largest partial row sum of p allowed
@@ -310,6 +315,8 @@ void fa_fwd_kernel(Params p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+    const int kpart = C::KS == 1 ? 0 : w / C::NWQ;   // key part of the wave (0 unless KS > 1)
+    const int wq = C::KS == 1 ? w : w % C::NWQ;      // its place among the part's query blocks
     const int l32 = lane & 31;
     const int h = lane >> 5;
 
@@ -339,9 +346,9 @@ void fa_fwd_kernel(Params p) {
     const int trank = item / p.hsub;
     const int hs = item - trank * p.hsub;
     const int tile = CAUSAL ? p.n_tiles - 1 - trank : trank;
-    const int hq = kvh * p.group + hs * HPW + w / WPH;
+    const int hq = kvh * p.group + hs * HPW + wq / WPH;
     const int q0 = tile * C::BMP;
-    const int qw0 = q0 + (w % WPH) * (32 * QB);
+    const int qw0 = q0 + (wq % WPH) * (32 * QB);
 
     typedef uint16_t T;
     constexpr int QE = QK8 ? 1 : 2;   // bytes per Q / K element
@@ -395,8 +402,16 @@ void fa_fwd_kernel(Params p) {
     // This workgroup's key split: tiles [t0, t1) of [tb, Tc), tile-aligned, so no mask is
     // needed at split boundaries.  Loads stop at key kend.  An empty range (more splits than
     // tiles) leaves the state empty: the partial is O = 0, LSE = -inf.
-    const int t0 = tb + (int)((long long)(Tc - tb) * split / p.num_splits);
-    const int t1 = tb + (int)((long long)(Tc - tb) * (split + 1) / p.num_splits);
+    int t0 = tb + (int)((long long)(Tc - tb) * split / p.num_splits);
+    int t1 = tb + (int)((long long)(Tc - tb) * (split + 1) / p.num_splits);
+    if constexpr (C::KS > 1) {
+        // Key parts: consecutive, equal runs of the range's tiles (the host launches key parts
+        // only for even tile counts), so every wave of the workgroup runs the same number of
+        // steps, and of barriers.
+        const int part = (t1 - t0) / C::KS;
+        t0 += kpart * part;
+        t1 = t0 + part;
+    }
     const int nt = t1 - t0;                    // tiles in this range
     // Local step bands: [0, ua) masked, [ua, ub) unmasked, [ub, nt) masked.
     const int ua = min(max(f0 - t0, 0), nt);
@@ -417,15 +432,18 @@ void fa_fwd_kernel(Params p) {
     // LDS: K(t0+i) lives in k_lds[i%3] and V(t0+i) in v_lds[i%3].  Six separate arrays, so
     // the compiler can tell a direct-to-LDS load into one from reads of another and does
     // not wait for the load before those reads; the step-end barrier publishes it.
-    __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILEK], k_lds1[TILEK], k_lds2[TILEK];
-    __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TILE], v_lds1[TILE], v_lds2[TILE];
+    // With key parts, part k uses bytes [k TILE, (k+1) TILE) of each array.
+    __shared__ __attribute__((aligned(16))) unsigned char k_lds0[TILEK * C::KS], k_lds1[TILEK * C::KS],
+        k_lds2[TILEK * C::KS];
+    __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TILE * C::KS], v_lds1[TILE * C::KS],
+        v_lds2[TILE * C::KS];
     auto kl = [&](auto ph) -> unsigned char* {
         constexpr int P = decltype(ph)::value;
-        return P == 0 ? k_lds0 : P == 1 ? k_lds1 : k_lds2;
+        return (P == 0 ? k_lds0 : P == 1 ? k_lds1 : k_lds2) + kpart * TILEK;
     };
     auto vl = [&](auto ph) -> unsigned char* {
         constexpr int P = decltype(ph)::value;
-        return P == 0 ? v_lds0 : P == 1 ? v_lds1 : v_lds2;
+        return (P == 0 ? v_lds0 : P == 1 ? v_lds1 : v_lds2) + kpart * TILE;
     };
 
     // Tiles move from HBM straight into LDS (buffer_load_dwordx4 ... lds): in load i, wave
@@ -442,17 +460,18 @@ void fa_fwd_kernel(Params p) {
     // takes the 8-chunk map of the head-dim-64 layout, head dim 64 a 4-chunk map.
     constexpr int KSWZ_D = QK8 ? D / 2 : D;
     auto kswz = [&](int row) { return k_swz<KSWZ_D>(row); };
-    // Waves that load V tiles are the last NWV; those that load K the first NWK.
-    const int vw = w - (C::NW - NWV);
-    const bool ld_v = NWV == C::NW || vw >= 0;
-    const bool ld_k = NWK == C::NW || w < NWK;
+    // Waves that load V tiles are the last NWV of their key part; those that load K the first
+    // NWK.  Each key part streams its own tiles into its own half of the buffers.
+    const int vw = wq - (C::NWQ - NWV);
+    const bool ld_v = NWV == C::NWQ || vw >= 0;
+    const bool ld_k = NWK == C::NWQ || wq < NWK;
     int ksrc, vsrc;
     {
         const int slot = (ld_v ? vw : 0) * 64 + lane;
         const int row = slot / CPR, pc = slot % CPR;
         if constexpr (V8) vsrc = row * ROWV + ((pc ^ v8_swz<D>(row)) << 4);
         else vsrc = row * ROWV + ((pc ^ v_swz<D>(row)) << 4);
-        const int slotk = w * 64 + lane;
+        const int slotk = wq * 64 + lane;
         const int rowk = slotk / CPRK, pck = slotk % CPRK;
         ksrc = rowk * ROWK + ((pck ^ kswz(rowk)) << 4);
     }
@@ -468,14 +487,14 @@ void fa_fwd_kernel(Params p) {
                 buffer_load_lds16(r, dst + (i * NWV + vw) * 1024, src, i * LOAD_STRIDE);
         }
     };
-    // K tiles: waves w < NWK load LDK chunks per lane (all waves unless fp8).
+    // K tiles: waves wq < NWK load LDK chunks per lane (all waves unless fp8).
     auto fetch_k = [&](int j, unsigned char* dst) FA_INLINE {
         const int j0 = min(j * BN, kend);
         const __amdgpu_buffer_rsrc_t r = make_rsrc(kp + (size_t)j0 * ROWK, min(kend - j0, BN) * ROWK);
         if (ld_k) {
 #pragma unroll
             for (int i = 0; i < LDK; ++i)
-                buffer_load_lds16(r, dst + (i * NWK + w) * 1024, ksrc, i * LOAD_STRIDE_K);
+                buffer_load_lds16(r, dst + (i * NWK + wq) * 1024, ksrc, i * LOAD_STRIDE_K);
         }
     };
 
@@ -732,13 +751,13 @@ void fa_fwd_kernel(Params p) {
     using F = std::false_type;
     using TT = std::true_type;
     if (nt > 0) {
-        fetch_k(t0, k_lds0);
-        fetch_k(t0 + 1, k_lds1);
-        fetch_k(t0 + 2, k_lds2);
-        fetch(vp, t0, v_lds0, vsrc);
+        fetch_k(t0, kl(Q0{}));
+        fetch_k(t0 + 1, kl(Q1{}));
+        fetch_k(t0 + 2, kl(Q2{}));
+        fetch(vp, t0, vl(Q0{}), vsrc);
         // K(t0) landed; K(t0+1), K(t0+2) and V(t0) may be in flight.
         wait_loads(std::integral_constant<int, 2 * LDK>{}, std::integral_constant<int, LD>{});
-        qk(k_lds0, s0);
+        qk(kl(Q0{}), s0);
         end_step();   // K(t0+1) and K(t0+2) landed
 
         // The K loop in bands (K-loop split): window-edge tiles, tiles needing no mask,
@@ -767,10 +786,41 @@ void fa_fwd_kernel(Params p) {
         // Drain: P V of the last tile (its V landed by the end of the last step).
         if (t1 - 1 >= wave_lo && t1 - 1 < wave_tc) {
             const int ph = (nt - 1) % 3;
-            if (ph == 0) pv(v_lds0, pk0);
-            else if (ph == 1) pv(v_lds1, pk1);
-            else pv(v_lds2, pk2);
+            if (ph == 0) pv(vl(Q0{}), pk0);
+            else if (ph == 1) pv(vl(Q1{}), pk1);
+            else pv(vl(Q2{}), pk2);
         }
+    }
+
+    if constexpr (C::KS > 1) {
+        // Merge the two key parts' states through LDS, whose tile buffers are free once every
+        // wave has done its last P V: part 1 stores (m, l, acc); part 0 folds them into its
+        // own with the online-softmax rescale (both m in the same exp2 units) and goes on to
+        // the epilogue; part 1 ends here.
+        static_assert(C::KS == 2 && C::NWQ <= 4, "two key parts of at most four waves");
+        static_assert(DB * 16 * 64 * 4 <= TILEK * C::KS && DB * 16 * 64 * 4 <= TILE * C::KS &&
+                          C::NWQ * 64 * 8 <= TILE * C::KS,
+                      "a wave's state fits one buffer array");
+        __syncthreads();
+        unsigned char* xa = wq == 0 ? k_lds0 : wq == 1 ? k_lds1 : wq == 2 ? k_lds2 : v_lds0;
+        float* xml = (float*)v_lds1 + 2 * (wq * 64 + lane);
+        if (kpart == 1) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) *(f32x16*)(xa + (db * 64 + lane) * 64) = acc[db][0];
+            xml[0] = m_run[0];
+            xml[1] = l_run[0];
+        }
+        __syncthreads();
+        if (kpart == 1) return;
+        const float m1 = xml[0], l1 = xml[1], m0 = m_run[0];
+        const float m = fmaxf(m0, m1);
+        const float a0 = m0 == -__builtin_inff() ? 0.0f : fast_exp2(m0 - m);
+        const float a1 = m1 == -__builtin_inff() ? 0.0f : fast_exp2(m1 - m);
+        m_run[0] = m;
+        l_run[0] = a0 * l_run[0] + a1 * l1;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            acc[db][0] = acc[db][0] * a0 + *(const f32x16*)(xa + (db * 64 + lane) * 64) * a1;
     }
 
     // Epilogue: O = acc / l (v_rcp_f32); LSE = ln2 (m + log2 l), -inf for a row with no

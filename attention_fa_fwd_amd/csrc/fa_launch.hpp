@@ -24,6 +24,6 @@ hipError_t launch_cfg(const fa::Params& p, hipStream_t s) {
 
 }  // namespace fa_host
 
-#define FA_INSTANTIATE(D, BN, QB, WPH, HPW, C, B, Q, V8, CN, TN)                             \
-    template hipError_t fa_host::launch_cfg<fa::Cfg<D, BN, QB, WPH, HPW, C, B, Q, V8>>(      \
+#define FA_INSTANTIATE(D, BN, QB, WPH, HPW, C, B, Q, V8, KS, CN, TN)                         \
+    template hipError_t fa_host::launch_cfg<fa::Cfg<D, BN, QB, WPH, HPW, C, B, Q, V8, KS>>(  \
         const fa::Params&, hipStream_t);

@@ -93,7 +93,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
  * Same as fa_fwd, but runs kernel configuration `config` (0 <= config < fa_num_configs())
  * instead of the one the dispatch table picks; config = -1 uses the table.  A configuration
  * whose head dim, dtype, causality or head grouping does not fit the call returns
- * FA_ERR_INVALID_CONFIG.  Meant for tests and tile sweeps.
+ * FA_ERR_INVALID_CONFIG, and so does a two-key-part one ("_KS2_" in its name: non-causal,
+ * the key tiles split between two sets of waves) when ceil(Skv / its key tile) is odd.
+ * Meant for tests and tile sweeps.
  */
 int fa_fwd_config(const void* q, const void* k, const void* v, void* out, float* lse,
                   int B, int Hq, int Hkv, int Sq, int Skv, int D, float scale,
@@ -165,7 +167,10 @@ int fa_select_config_fp8(int B, int Hq, int Hkv, int Sq, int D, int causal, int 
  *   num_splits       0 = choose (fa_splitkv_num_splits), 1 = no split (same kernels as
  *                    fa_fwd; workspace unused, may be NULL), 2..256 = that many ranges.
  *                    Ranges beyond the number of key tiles are empty and harmless.
- *   config           as for fa_fwd_config; -1 = the dispatch table.
+ *   config           as for fa_fwd_config; -1 = the dispatch table (whose two-key-part
+ *                    choices give way to their one-part twins when more than one range
+ *                    runs).  A forced two-key-part configuration runs one range only:
+ *                    more is FA_ERR_INVALID_CONFIG.
  *   workspace        device memory of >= fa_splitkv_workspace_size(B, Hq, Sq, D, splits)
  *                    bytes, 16-byte aligned, owned by the caller, overlapping no tensor.
  *                    Its contents on entry do not matter; on return it holds the partials.

@@ -101,8 +101,14 @@ def forced_configs(D, dtype, causal):
 
 
 # Compiled shapes per head dim: 7 for head dim 128 (32-key tiles), 6 for head dim 64
-# (64-key tiles), among them the eight-wave ones the dispatch takes for large grids.
+# (64-key tiles), among them the eight-wave ones the dispatch takes for large grids; the
+# non-causal lists add the three two-key-part ("KS2") shapes.
 N_SHAPES = {128: 7, 64: 6}
+N_KS2 = 3
+
+# Key lengths with a ragged last tile and an even number of tiles (32-key tiles for head dim
+# 128, 64-key tiles for head dim 64), so the two-key-part configurations apply.
+SKV_EVEN_TILES = {128: 300, 64: 333}
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -110,10 +116,11 @@ N_SHAPES = {128: 7, 64: 6}
 @pytest.mark.parametrize("causal", [False, True])
 def test_every_config_on_same_input(D, dtype, causal):
     """Every compiled configuration that fits the call agrees with the oracle."""
-    q, k, v = make_qkv(1, 16, 2, 333, 333, D, dtype, seed=5)   # GQA 8: every shape applies
+    skv = 333 if causal else SKV_EVEN_TILES[D]
+    q, k, v = make_qkv(1, 16, 2, 333, skv, D, dtype, seed=5)   # GQA 8: every shape applies
     pos = 7 if causal else 0
     configs = forced_configs(D, dtype, causal)
-    assert len(configs) == N_SHAPES[D]
+    assert len(configs) == N_SHAPES[D] + (0 if causal else N_KS2)
     for cid, name in configs:
         _say("config", name)
         out, lse = run_gpu(q, k, v, 0.09, causal, pos, config=cid)
