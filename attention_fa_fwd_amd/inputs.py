@@ -44,6 +44,13 @@ WORKLOADS = {
                                        dtype="bf16", causal=True, input_pos=0),
     "gqa2_s2048_d64_fp16": dict(B=1, Hq=32, Hkv=16, Sq=2048, Skv=2048, D=64, dtype="fp16",
                                 causal=False, input_pos=0),
+    # Non-causal attention of 256 queries over 16K keys (a cross-attention shape, GQA 4): 64
+    # four-wave workgroups, one wave per SIMD on the CUs they use, so fa_fwd's dispatch takes
+    # two key parts per workgroup; fa_fwd_splitkv splits the keys across workgroups instead
+    # (both are timed: "splitkv_line").
+    "gqa4_xattn_q256_kv16384_d128_bf16": dict(B=1, Hq=32, Hkv=8, Sq=256, Skv=16384, D=128,
+                                              dtype="bf16", causal=False, input_pos=0,
+                                              splitkv_line=True),
     # One new token per sequence against a 16K-token cache: the under-filled grid that
     # split-KV is for (32 workgroups unsplit).
     "gqa4_decode_b4_kv16384_d128_bf16": dict(B=4, Hq=32, Hkv=8, Sq=1, Skv=16384, D=128,

@@ -276,6 +276,8 @@ def time_gpu(name, steps, warmup, config=-1, splitkv=False, backward=False, cold
         cfg = fa.select_config(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"], w["causal"],
                                w["input_pos"], q.dtype)
     kernel = "fa_bwd (dot, dK/dV, dQ)" if backward else fa.config_names()[cfg]
+    if splitkv and splits > 1 and "_KS2_" in kernel:
+        kernel = kernel.replace("_KS2_", "_")   # split-KV runs the one-key-part twin
     return dict(total_ms=total_ms, wall_s=wall, per_ms=per, kernel=kernel,
                 warmup_extra=extra, splits=splits)
 
@@ -547,7 +549,7 @@ def main(argv=None):
 
         for name in list(WORKLOADS) + list(FP8_WORKLOADS):
             shape = WORKLOADS.get(name) or FP8_WORKLOADS[name]
-            runs = [False, True] if shape["Sq"] <= 16 else [False]
+            runs = [False, True] if shape["Sq"] <= 16 or shape.get("splitkv_line") else [False]
             for split in runs:
                 if name == a.workload and split == a.splitkv:
                     continue

@@ -149,6 +149,23 @@ def test_decode_workload_auto_split():
     check_full(q, k, v, kw["scale"], kw["causal"], kw["input_pos"], out, lse, name)
 
 
+def test_cross_attention_workload_auto_split():
+    """The non-causal cross-attention workload (256 queries, 16K keys; fa_fwd runs it with two
+    key parts per workgroup) through fa_fwd_splitkv with the library's split choice, which
+    runs the one-part twin over several key ranges: every element against the oracle."""
+    name = "gqa4_xattn_q256_kv16384_d128_bf16"
+    w = WORKLOADS[name]
+    q, k, v, kw = make_workload(name, seed=0)
+    names = fa.config_names()
+    assert "_KS2_" in names[fa.select_config(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"],
+                                             False, 0, q.dtype)]
+    s = fa.splitkv_num_splits(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Skv"], w["D"], False, 0, q.dtype)
+    _say(name, "auto splits", s)
+    assert s > 1
+    out, lse = run_split(q, k, v, kw["scale"], False, 0, 0)
+    check_full(q, k, v, kw["scale"], False, 0, out, lse, name)
+
+
 def test_split_workspace_errors():
     q, k, v = make_qkv(1, 4, 2, 64, 256, 128, "bf16", seed=2)
     q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
