@@ -399,19 +399,20 @@ void fa_fwd_kernel(Params p) {
                         : CAUSAL ? (min(p.input_pos + qw_last + 1, p.Skv) + BN - 1) / BN
                                  : Tc;
     const int wave_lo = win ? max(0, p.input_pos + qw0 - p.window + 1) / BN : 0;
-    // This workgroup's key split: tiles [t0, t1) of [tb, Tc), tile-aligned, so no mask is
-    // needed at split boundaries.  Loads stop at key kend.  An empty range (more splits than
-    // tiles) leaves the state empty: the partial is O = 0, LSE = -inf.
-    int t0 = tb + (int)((long long)(Tc - tb) * split / p.num_splits);
-    int t1 = tb + (int)((long long)(Tc - tb) * (split + 1) / p.num_splits);
+    // This workgroup's key split: tiles [r0, r1) of [tb, Tc), tile-aligned, so no mask is
+    // needed at split boundaries.  An empty range (more splits than tiles) leaves the state
+    // empty: the partial is O = 0, LSE = -inf.
+    int r0 = tb + (int)((long long)(Tc - tb) * split / p.num_splits);
+    int r1 = tb + (int)((long long)(Tc - tb) * (split + 1) / p.num_splits);
     if constexpr (C::KS > 1) {
         // Key parts: consecutive, equal runs of the range's tiles (the host launches key parts
         // only for even tile counts), so every wave of the workgroup runs the same number of
         // steps, and of barriers.
-        const int part = (t1 - t0) / C::KS;
-        t0 += kpart * part;
-        t1 = t0 + part;
+        const int part = (r1 - r0) / C::KS;
+        r0 += kpart * part;
+        r1 = r0 + part;
     }
+    const int t0 = r0, t1 = r1;
     const int nt = t1 - t0;                    // tiles in this range
     // Local step bands: [0, ua) masked, [ua, ub) unmasked, [ub, nt) masked.
     const int ua = min(max(f0 - t0, 0), nt);
@@ -421,8 +422,13 @@ void fa_fwd_kernel(Params p) {
     // Running state: m (exp2 domain, possibly stale), l, acc (= O^T blocks).
     float m_run[QB], l_run[QB];
     f32x16 acc[DB][QB];
+    // Each S block starts from -m/c (0 while m = -inf) instead of 0, so that the MFMAs
+    // deliver s - m/c and p = exp2(c (s - m/c)) costs one multiply before the exp2.
+    f32x16 negm[QB];
+    const float inv_c = 1.0f / p.c;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+        negm[qb] = (f32x16){};
         m_run[qb] = -__builtin_inff();
         l_run[qb] = 0.0f;
 #pragma unroll
@@ -475,26 +481,35 @@ void fa_fwd_kernel(Params p) {
         const int rowk = slotk / CPRK, pck = slotk % CPRK;
         ksrc = rowk * ROWK + ((pck ^ kswz(rowk)) << 4);
     }
-    // One buffer resource per tile, ending at the tile's last valid key; load i adds
-    // i * LOAD_STRIDE as the scalar offset (gfx950's range check covers voffset + soffset,
-    // so every load past the end of the range reads zero).
-    auto fetch = [&](const unsigned char* base, int j, unsigned char* dst, int src) FA_INLINE {
-        const int j0 = min(j * BN, kend);
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (size_t)j0 * ROWV, min(kend - j0, BN) * ROWV);
+    // One buffer resource for K and one for V from tile jb to the range's last valid key
+    // kend; a load adds the tile's byte offset from jb plus i * stride as the scalar offset.
+    // gfx950's range check covers voffset + soffset, so every load past the end of the range
+    // -- the ragged key tail, tiles past the end, keys of the next split -- reads zero.  jb
+    // moves up (rebase) only once a range has run RB tiles past it, which keeps offsets and
+    // record counts below 2^31: never, unless the range holds more than 2^30 bytes of K or V.
+    constexpr int RB = (1 << 30) / (TILEK > TILE ? TILEK : TILE);
+    int jb = t0;
+    __amdgpu_buffer_rsrc_t rk = make_rsrc(kp, 0), rv = make_rsrc(vp, 0);
+    auto rebase = [&](int j) FA_INLINE {
+        jb = j;
+        const int k0 = min(j * BN, kend);
+        const int n = min(kend - k0, (RB + 16) * BN);
+        rk = make_rsrc(kp + (size_t)k0 * ROWK, n * ROWK);
+        rv = make_rsrc(vp + (size_t)k0 * ROWV, n * ROWV);
+    };
+    auto fetch = [&](int j, unsigned char* dst) FA_INLINE {
         if (ld_v) {
 #pragma unroll
             for (int i = 0; i < LD; ++i)
-                buffer_load_lds16(r, dst + (i * NWV + vw) * 1024, src, i * LOAD_STRIDE);
+                buffer_load_lds16(rv, dst + (i * NWV + vw) * 1024, vsrc, (j - jb) * TILE + i * LOAD_STRIDE);
         }
     };
     // K tiles: waves wq < NWK load LDK chunks per lane (all waves unless fp8).
     auto fetch_k = [&](int j, unsigned char* dst) FA_INLINE {
-        const int j0 = min(j * BN, kend);
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(kp + (size_t)j0 * ROWK, min(kend - j0, BN) * ROWK);
         if (ld_k) {
 #pragma unroll
             for (int i = 0; i < LDK; ++i)
-                buffer_load_lds16(r, dst + (i * NWK + wq) * 1024, ksrc, i * LOAD_STRIDE_K);
+                buffer_load_lds16(rk, dst + (i * NWK + wq) * 1024, ksrc, (j - jb) * TILEK + i * LOAD_STRIDE_K);
         }
     };
 
@@ -539,7 +554,7 @@ void fa_fwd_kernel(Params p) {
 #pragma unroll
         for (int k2 = 0; k2 < KB; ++k2) {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[k2][qb] = (f32x16){};
+            for (int qb = 0; qb < QB; ++qb) s[k2][qb] = negm[qb];
             if constexpr (QK8) {
 #pragma unroll
                 for (int dk = 0; dk < DK8; ++dk) {
@@ -648,7 +663,7 @@ void fa_fwd_kernel(Params p) {
         auto& pk_cur = pick(ph_tag, pk0, pk1, pk2);
         auto& pk_prev = pick(N2{}, pk0, pk1, pk2);
         fetch_k(j + 3, kl(ph_tag));
-        fetch(vp, j + 1, vl(N1{}), vsrc);
+        fetch(j + 1, vl(N1{}));
         const bool do_sm = !MASKED || (j >= wave_lo && j < wave_tc);   // softmax of tile j
         const bool do_pv = !FIRST && (!MASKED || (j - 1 >= wave_lo && j - 1 < wave_tc));   // P V of tile j-1
         if (do_sm) {
@@ -688,16 +703,13 @@ void fa_fwd_kernel(Params p) {
             auto make_p = [&]() FA_INLINE {
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
-                    // m = -inf until the row's first visible key; meanwhile use 0, so masked
-                    // keys give p = 0, and take the slow path below.
-                    const float neg_m = m_run[qb] == -__builtin_inff() ? 0.0f : -m_run[qb];
                     float psum[KB];
 #pragma unroll
                     for (int k2 = 0; k2 < KB; ++k2) {
                         float t[16];
 #pragma unroll
                         for (int i = 0; i < 16; ++i)
-                            t[i] = fast_exp2(__builtin_fmaf(s_cur[k2][qb][i], p.c, neg_m));
+                            t[i] = fast_exp2(s_cur[k2][qb][i] * p.c);
 #pragma unroll
                         for (int hf = 0; hf < 2; ++hf) {
                             const float* e = t + 8 * hf;
@@ -718,7 +730,8 @@ void fa_fwd_kernel(Params p) {
             // the common path.
             bool bad = false;
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) bad |= !(ts[qb] <= P_LIMIT) || m_run[qb] == -__builtin_inff();
+            for (int qb = 0; qb < QB; ++qb)
+                bad |= !(ts[qb] <= P_LIMIT) || ((MASKED || FIRST) && m_run[qb] == -__builtin_inff());
             if (__builtin_amdgcn_ballot_w64(bad) != 0) {
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
@@ -727,18 +740,29 @@ void fa_fwd_kernel(Params p) {
                     for (int k2 = 0; k2 < KB; ++k2)
 #pragma unroll
                         for (int i = 0; i < 16; ++i) t[k2 * 16 + i] = s_cur[k2][qb][i];
-                    const float m_new = fmaxf(m_run[qb], xhalf_max(Tree<KB * 16>::max(t)) * p.c);
+                    // S holds s - m_used/c, m_used = m (0 while m = -inf).
+                    const float m_used = m_run[qb] == -__builtin_inff() ? 0.0f : m_run[qb];
+                    const float m_new = fmaxf(m_run[qb], m_used + xhalf_max(Tree<KB * 16>::max(t)) * p.c);
                     // A row with no visible key yet keeps m = -inf and its (zero) state.
                     const float alpha = m_new == -__builtin_inff() ? 1.0f : fast_exp2(m_run[qb] - m_new);
                     m_run[qb] = m_new;
                     l_run[qb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
+                    // S(j) and S(j+1) started from -m_used/c: move both to the new m.
+                    const float nm = (m_new == -__builtin_inff() ? 0.0f : -m_new) * inv_c;
+                    const float delta = m_used * inv_c + nm;
+#pragma unroll
+                    for (int k2 = 0; k2 < KB; ++k2) {
+                        s_cur[k2][qb] += delta;
+                        s_nxt[k2][qb] += delta;
+                    }
+                    negm[qb] = nm;
                 }
                 make_p();
             }
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) l_run[qb] += xhalf_sum(ts[qb]);
+            for (int qb = 0; qb < QB; ++qb) l_run[qb] += ts[qb];
         }
         end_step();
     };
@@ -751,10 +775,11 @@ void fa_fwd_kernel(Params p) {
     using F = std::false_type;
     using TT = std::true_type;
     if (nt > 0) {
+        rebase(t0);
         fetch_k(t0, kl(Q0{}));
         fetch_k(t0 + 1, kl(Q1{}));
         fetch_k(t0 + 2, kl(Q2{}));
-        fetch(vp, t0, vl(Q0{}), vsrc);
+        fetch(t0, vl(Q0{}));
         // K(t0) landed; K(t0+1), K(t0+2) and V(t0) may be in flight.
         wait_loads(std::integral_constant<int, 2 * LDK>{}, std::integral_constant<int, LD>{});
         qk(kl(Q0{}), s0);
@@ -770,6 +795,9 @@ void fa_fwd_kernel(Params p) {
             if (i < end && i % 3 == 1) { step(t0 + i, Q1{}, masked, F{}); ++i; }
             if (i < end && i % 3 == 2) { step(t0 + i, Q2{}, masked, F{}); ++i; }
             for (; i + 2 < end; i += 3) {
+                // At most RB + 8 tiles past jb before the next check: the rest of this
+                // iteration, up to four peeled steps, and the loads three tiles ahead.
+                if (t0 + i - jb >= RB) rebase(t0 + i);
                 step(t0 + i, Q0{}, masked, F{});
                 step(t0 + i + 1, Q1{}, masked, F{});
                 step(t0 + i + 2, Q2{}, masked, F{});
@@ -791,6 +819,10 @@ void fa_fwd_kernel(Params p) {
             else pv(vl(Q2{}), pk2);
         }
     }
+
+    // l_run holds each lane's half of its row's keys: add the two halves.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] = xhalf_sum(l_run[qb]);
 
     if constexpr (C::KS > 1) {
         // Merge the two key parts' states through LDS, whose tile buffers are free once every
