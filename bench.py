@@ -7,7 +7,9 @@ MFMA peak, and the fp64 CPU oracle timed on a bounded sample of the same workloa
 
 FLOPs are counted as 4*B*Hq*Sq*Skv*D, halved when causal.  Inputs are resident in HBM
 before the timed region; each step is one call of the library's fa_fwd on torch's
-current stream, timed with HIP events recorded on that stream.
+current stream, timed with HIP events recorded on that stream: the K timed steps run back
+to back between two events (value, ms_per_step), then K more with an event pair around each
+launch give the per-launch durations (kernel_us, roofline.achieved).
 
 Warm-up: W untimed steps, then more untimed steps until at least MIN_WARMUP_S seconds of
 warm-up have passed.  Coming out of idle the GPU needs some tens of milliseconds to reach
@@ -255,17 +257,27 @@ def time_gpu(name, steps, warmup, config=-1, splitkv=False, backward=False, cold
         per = sorted(ev0[i].elapsed_time(ev1[i]) for i in range(steps))
         total_ms = sum(per)
     else:
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        # Throughput: K steps back to back between two events (nothing else on the stream).
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        total_ms = e0.elapsed_time(e1)
+        # Per-launch durations: K more steps with an event between every two launches (the
+        # events add a gap of a few microseconds per launch, which the throughput run has not).
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
         evs[0].record(stream)
         for i in range(steps):
             step()
             evs[i + 1].record(stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
         per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))  # ms per launch
-        total_ms = evs[0].elapsed_time(evs[-1])
     if config >= 0:
         cfg = config
     elif fp8:
@@ -398,9 +410,12 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False, bac
         f"{r['warmup_extra']} extra warm-up steps")
     decode = w["Sq"] <= 16 and not backward
     if decode:
-        # Reading K and V bounds a decoding step: GB/s of algorithmic bytes per call.
-        gbs = algorithmic_bytes(w, fp8) / (mean_kernel_ms * 1e-3) / 1e9
-        metric, value, unit = "attention decode GB/s of algorithmic HBM bytes", gbs, "GB/s"
+        # Reading K and V bounds a decoding step: GB/s of algorithmic bytes per call, over the
+        # throughput run (value) and over the mean per-call duration (roofline).
+        nbytes = algorithmic_bytes(w, fp8)
+        gbs = nbytes / (mean_kernel_ms * 1e-3) / 1e9
+        metric, value, unit = ("attention decode GB/s of algorithmic HBM bytes",
+                               nbytes / (ms_step * 1e-3) / 1e9, "GB/s")
         # Counted bytes of the attention kernel (the merge kernel's are not included).
         traffic = None if cold else traffic_bytes(name + ("/splitkv" if splitkv else ""))
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -439,6 +454,10 @@ def bench_line(name, steps, warmup, config=-1, with_cpu=True, splitkv=False, bac
                    "kernel": r["kernel"], "path": path,
                    "caches": (f"cold: {COLD_FLUSH_BYTES >> 20} MiB written before each launch, "
                               "outside its events") if cold else "warm: launches back to back",
+                   "timing": ("each launch between its own events (value and kernel_us)" if cold else
+                              "value and ms_per_step: the K steps back to back between two events; "
+                              "kernel_us and roofline.achieved: K more steps, an event pair around "
+                              "each launch"),
                    "parallelism": "single GPU"},
         "kernel_us": {"mean": round(mean_kernel_ms * 1e3, 2), "median": round(med * 1e3, 2),
                       "p95": round(p95 * 1e3, 2), "min": round(r["per_ms"][0] * 1e3, 2)},
