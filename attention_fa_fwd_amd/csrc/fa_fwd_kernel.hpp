@@ -689,6 +689,10 @@ void fa_fwd_kernel(Params p) {
                 }
             }
         }
+        // Scheduling: the backend's MFMA / LDS-read interleave (one fragment read between
+        // MFMAs) for this step's block.  Same instructions; measured 0.5% faster on the causal
+        // GQA shapes and 5-10% on the grids with one or two waves per SIMD and long key loops.
+        __builtin_amdgcn_iglp_opt(0);
         // Matrix work of this step: S(j+1), and P V of tile j-1.
         qk(kl(N1{}), s_nxt);
         if constexpr (!FIRST) {
