@@ -75,6 +75,27 @@ def test_long_query_tensor():
         _check(out[:, h:h + 1, r0:r0 + n], lse[:, h:h + 1, r0:r0 + n], O, L, (h, r0, n))
 
 
+def test_key_range_past_1gib_of_one_workgroup():
+    """A query tile whose key range holds more than 2^30 bytes of K and of V: 40 rows of two
+    query heads against (2^22 + 12345) keys (1.08 GB of K, as much of V), non-causal and causal
+    with the last row on the last key (input_pos = Skv - Sq).  The kernel addresses a range's
+    tiles from one buffer resource and moves it up once 2^30 bytes of the range have been
+    streamed (here after 131073 of its 131458 key tiles); every element is compared with the
+    oracle."""
+    Hq, Sq, Skv, scale = 2, 40, (1 << 22) + 12345, 1.0 / math.sqrt(D)
+    assert Skv * D * 2 > (1 << 30)
+    _say("fa_fwd long key range", (1, Hq, 1, Sq, Skv, D), "bf16")
+    q = _randn((1, Hq, Sq, D), 41)
+    k = _randn((1, 1, Skv, D), 42)
+    v = _randn((1, 1, Skv, D), 43)
+    qd, kd, vd = _f64(q), _f64(k), _f64(v)
+    for causal, pos in ((False, 0), (True, Skv - Sq)):
+        O, L = oracle.attention_blocked(qd, kd, vd, scale, causal, pos)
+        out, lse = fa.fa_fwd(q, k, v, scale=scale, causal=causal, input_pos=pos)
+        torch.cuda.synchronize()
+        _check(out, lse, O, L, f"causal={causal}")
+
+
 def _window_case(Hq, Sq, Skv, W, seed):
     pos = Skv - Sq
     q = _randn((1, Hq, Sq, D), seed)
