@@ -76,11 +76,28 @@ def bench_of_run(path):
     return out
 
 
+def _kernel_rows(db):
+    """(name, duration ns) of every dispatch, in order of start time when the table has one."""
+    try:
+        return _rows(db, "select name, duration from kernels order by start")
+    except sqlite3.OperationalError:
+        return _rows(db, "select name, duration from kernels")
+
+
+def _bench_steps(path):
+    """`steps` of the bench.py line in the traced run's stdout, or None."""
+    with open(path, errors="replace") as f:
+        for raw in f:
+            raw = raw.strip()
+            if raw.startswith('{"metric"'):
+                return json.loads(raw).get("steps")
+    return None
+
+
 def trace(db, command, bench_out=None):
-    rows = _rows(db, "select name, duration from kernels")
     by = {}
-    for name, dur in rows:
-        by.setdefault(name, []).append(dur / 1e3)  # ns -> us
+    for name, dur in _kernel_rows(db):
+        by.setdefault(name, []).append(dur / 1e3)  # ns -> us, in dispatch order
     out = [f"# rocprofv3 kernel trace summary", f"# command: {command}",
            f"# source: {os.path.basename(db)}", "",
            f"{'kernel':<98} {'calls':>5} {'mean_us':>9} {'median_us':>9} {'min_us':>9} {'max_us':>9}"]
@@ -88,6 +105,17 @@ def trace(db, command, bench_out=None):
         out.append(f"{short(name):<98} {len(d):>5} {statistics.mean(d):>9.1f} "
                    f"{statistics.median(d):>9.1f} {min(d):>9.1f} {max(d):>9.1f}")
     if bench_out:
+        steps = _bench_steps(bench_out)
+        timed = [(n, d[-2 * steps:]) for n, d in by.items() if steps and len(d) >= 2 * steps]
+        if timed:
+            # bench.py times K launches back to back, then K more with an event pair around
+            # each: the last 2K dispatches of each kernel are the timed ones (the rest are the
+            # warm-up, at a ramping clock).
+            out += ["", f"# the {2 * steps} timed dispatches of each kernel (the last ones of the run):",
+                    f"{'kernel':<98} {'calls':>5} {'mean_us':>9} {'median_us':>9}"]
+            for name, d in sorted(timed, key=lambda kv: -sum(kv[1])):
+                out.append(f"{short(name):<98} {len(d):>5} {statistics.mean(d):>9.1f} "
+                           f"{statistics.median(d):>9.1f}")
         out += bench_of_run(bench_out)
     return "\n".join(out)
 

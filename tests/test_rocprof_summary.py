@@ -65,3 +65,25 @@ def test_bench_quote_missing_line(tmp_path):
     db = str(tmp_path / "r.db")
     _db(db, [("a", 1_000)])
     assert "bench.py line" not in rocprof_summary.trace(db, "CMD")
+
+
+def test_trace_timed_dispatches(tmp_path):
+    """With the traced run's `steps` = K, the last 2K dispatches of each kernel (in start
+    order when the table has a start column) are summarised apart from the warm-up."""
+    db = str(tmp_path / "t.db")
+    con = sqlite3.connect(db)
+    con.execute("create table kernels (name text, duration integer, start integer)")
+    # kernel a: warm-up 900, 800 us, then the timed 100, 200, 300, 400 us; inserted out of order
+    con.executemany("insert into kernels values (?, ?, ?)",
+                    [("a", 300_000, 5), ("a", 900_000, 1), ("a", 100_000, 3), ("a", 800_000, 2),
+                     ("a", 400_000, 6), ("a", 200_000, 4), ("b", 7_000, 7)])
+    con.commit()
+    con.close()
+    f = tmp_path / "bench.out"
+    f.write_text(json.dumps({"metric": "m", "value": 1.0, "unit": "TFLOP/s", "steps": 2,
+                             "config": {"workload": "w", "path": "fa_fwd", "kernel": "K"},
+                             "kernel_us": {}}) + "\n")
+    lines = rocprof_summary.trace(db, "CMD", str(f)).splitlines()
+    i = lines.index("# the 4 timed dispatches of each kernel (the last ones of the run):")
+    rows = [l.split() for l in lines[i + 2:] if l.startswith(("a ", "b "))]
+    assert rows == [["a", "4", "250.0", "250.0"]]   # b has fewer than 2K calls
