@@ -14,7 +14,7 @@ import math
 import os
 import threading
 
-__all__ = ["fa_fwd", "fa_fwd_into", "fa_bwd", "fa_bwd_into", "bwd_workspace_size", "fa_fwd_fp8",
+__all__ = ["fa_fwd", "fa_fwd_into", "fa_fwd_prepared", "fa_bwd", "fa_bwd_into", "bwd_workspace_size", "fa_fwd_fp8",
            "fa_fwd_fp8_into", "select_config_fp8", "fa_fwd_splitkv_fp8", "fa_fwd_splitkv_fp8_into",
            "splitkv_num_splits_fp8", "fa_fwd_splitkv", "fa_fwd_splitkv_into", "splitkv_num_splits",
            "fa_fwd_splitkv_noalloc", "fa_fwd_splitkv_noalloc_into", "NOALLOC_SCRATCH_BYTES",
@@ -191,6 +191,42 @@ def fa_fwd_into(q, k, v, out, lse, scale=None, causal=True, input_pos=0, config=
                                    stream, int(config))
     _check(rc)
     return out, lse
+
+
+def fa_fwd_prepared(q, k, v, out, lse, scale=None, causal=True, input_pos=0, config=-1, stream=None,
+                    window=0):
+    """``fa_fwd_into`` with its argument checks and marshalling done once: returns a callable
+    that, each time it is called, enqueues the same forward pass (same tensors, scale, masking,
+    configuration and stream) with one C call.  For launch loops whose per-call host time
+    matters (a short problem runs in a few microseconds on the GPU).  The callable holds
+    references to the tensors; their storage must not be resized or replaced while it is used.
+    A nonzero status raises FaError as in fa_fwd_into."""
+    import torch
+
+    lib = load_library()
+    B, Hq, Hkv, Sq, Skv, D = _check_tensors(q, k, v, out, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check_window(causal, window)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
+            Sq, Skv, D, float(scale))
+    if window > 0:
+        fn, args = lib.fa_fwd_window, ptrs + (int(input_pos), int(window), _dtype_code(q.dtype),
+                                              stream, int(config))
+    else:
+        fn, args = lib.fa_fwd_config, ptrs + (1 if causal else 0, int(input_pos),
+                                              _dtype_code(q.dtype), stream, int(config))
+    keep = (q, k, v, out, lse)
+
+    def call():
+        rc = fn(*args)
+        if rc != 0:
+            _check(rc)
+        return keep[3], keep[4]
+
+    return call
 
 
 def splitkv_num_splits(B, Hq, Hkv, Sq, Skv, D, causal, input_pos, dtype, config=-1, window=0) -> int:

@@ -197,6 +197,28 @@ def test_repeated_launches_bitwise_identical():
         assert torch.equal(o, ref[0]) and torch.equal(l, ref[1])
 
 
+def test_prepared_call_matches_fa_fwd_into():
+    """fa_fwd_prepared (arguments checked once, one C call per launch) gives bit-identical
+    results to fa_fwd_into, plain and with a window, re-launched after the inputs change;
+    an invalid argument raises when the call is prepared."""
+    dev = torch.device("cuda:0")
+    q, k, v = make_qkv(1, 8, 2, 300, 300, 128, "bf16", seed=15)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    for window in (0, 70):
+        out, lse = torch.empty_like(qd), torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+        call = fa.fa_fwd_prepared(qd, kd, vd, out, lse, causal=True, window=window)
+        for it in range(3):
+            qd.copy_(q.to(dev) * (1 + it))
+            call()
+            ref = fa.fa_fwd(qd, kd, vd, causal=True, window=window)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), (window, it)
+    with pytest.raises(fa.FaError):
+        fa.fa_fwd_prepared(qd, kd, vd, out, lse, scale=-1.0)()
+    with pytest.raises(ValueError):
+        fa.fa_fwd_prepared(qd, kd, vd, out, lse, causal=False, window=4)
+
+
 def test_empty_and_errors_on_gpu():
     dev = torch.device("cuda:0")
     q = torch.zeros(1, 4, 0, 128, dtype=torch.bfloat16, device=dev)
