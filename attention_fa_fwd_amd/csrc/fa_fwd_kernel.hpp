@@ -859,6 +859,57 @@ void fa_fwd_kernel(Params p) {
             acc[db][0] = acc[db][0] * a0 + *(const f32x16*)(xa + (db * 64 + lane) * 64) * a1;
     }
 
+    // Epilogue of a one-split, one-part call with 16-bit V: O leaves through LDS so that
+    // every global store writes whole 128-byte row segments.  A lane holds 16 consecutive d
+    // of one row per 32-wide block, so direct stores would put 16-byte pieces of each line
+    // into separate instructions; staged, eight lanes store one 128-byte segment.  The
+    // stores are non-temporal: nothing reads O back, and it need not displace K/V in L2.
+    // Each wave stages its 32 rows x 64 d (4 KiB) in its own part of the tile buffers,
+    // free once every wave is past its last P V; 16-byte chunks XOR-swizzled by row / 2.
+    if constexpr (!V8 && C::KS == 1 && QB == 1) {
+        if (p.num_splits == 1) {
+            static_assert(TILE >= 8192 && TILEK >= 4096 && C::NW <= 8, "eight 4 KiB stages");
+            const size_t head_row0 = (size_t)(b * p.Hq + hq) * p.Sq;
+            const float l = l_run[0];
+            const float inv = l > 0.0f ? __builtin_amdgcn_rcpf(l) : 0.0f;
+            if (h == 0 && qw0 + l32 < p.Sq)
+                p.lse[head_row0 + qw0 + l32] =
+                    l > 0.0f ? (m_run[0] + __builtin_amdgcn_logf(l)) * LN2 : -__builtin_inff();
+            // Two stages per 8 KiB buffer (fp8 keys: 4 KiB K buffers, one stage each).
+            unsigned char* sb;
+            if constexpr (TILEK >= 8192)
+                sb = (w >> 1 == 0 ? k_lds0 : w >> 1 == 1 ? k_lds1 : w >> 1 == 2 ? k_lds2 : v_lds0) + (w & 1) * 4096;
+            else
+                sb = w < 6 ? (w >> 1 == 0 ? v_lds0 : w >> 1 == 1 ? v_lds1 : v_lds2) + (w & 1) * 4096
+                           : (w == 6 ? k_lds0 : k_lds1);
+            __syncthreads();
+#pragma unroll
+            for (int ps = 0; ps < D / 64; ++ps) {
+                if (ps > 0) __syncthreads();   // this wave's reads of the previous pass are done
+#pragma unroll
+                for (int dh = 0; dh < 2; ++dh) {
+                    const f32x16 a = acc[2 * ps + dh][0] * inv;
+                    const u32x4 w0 = {pack2<BF16>(a[0], a[1]), pack2<BF16>(a[2], a[3]),
+                                      pack2<BF16>(a[4], a[5]), pack2<BF16>(a[6], a[7])};
+                    const u32x4 w1 = {pack2<BF16>(a[8], a[9]), pack2<BF16>(a[10], a[11]),
+                                      pack2<BF16>(a[12], a[13]), pack2<BF16>(a[14], a[15])};
+                    const int c = 4 * dh + 2 * h, sw = (l32 >> 1) & 7;
+                    *(u32x4*)(sb + l32 * 128 + ((c ^ sw) << 4)) = w0;
+                    *(u32x4*)(sb + l32 * 128 + (((c + 1) ^ sw) << 4)) = w1;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int r = 8 * k + (lane >> 3), c = lane & 7;
+                    const u32x4 x = *(const u32x4*)(sb + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+                    if (qw0 + r < p.Sq)
+                        __builtin_nontemporal_store(x, (u32x4*)((T*)p.o + (head_row0 + qw0 + r) * D + 64 * ps + 8 * c));
+                }
+            }
+            return;
+        }
+    }
+
     // Epilogue: O = acc / l (v_rcp_f32); LSE = ln2 (m + log2 l), -inf for a row with no
     // visible key (l = 0, O = 0).  One split: O rounded to the storage type.  Several
     // splits: the normalised partial O in fp32 and its LSE, for the merge kernel.
