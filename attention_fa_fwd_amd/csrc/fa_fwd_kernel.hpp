@@ -443,6 +443,9 @@ void fa_fwd_kernel(Params p) {
         k_lds2[TILEK * C::KS];
     __shared__ __attribute__((aligned(16))) unsigned char v_lds0[TILE * C::KS], v_lds1[TILE * C::KS],
         v_lds2[TILE * C::KS];
+    // fp8 V: the tile buffers (4 KiB each) are too small to stage O in the epilogue; it gets
+    // its own 4 KiB per wave.
+    __shared__ __attribute__((aligned(16))) unsigned char o_stage[V8 && C::KS == 1 ? C::NW * 4096 : 16];
     auto kl = [&](auto ph) -> unsigned char* {
         constexpr int P = decltype(ph)::value;
         return (P == 0 ? k_lds0 : P == 1 ? k_lds1 : k_lds2) + kpart * TILEK;
@@ -859,25 +862,29 @@ void fa_fwd_kernel(Params p) {
             acc[db][0] = acc[db][0] * a0 + *(const f32x16*)(xa + (db * 64 + lane) * 64) * a1;
     }
 
-    // Epilogue of a one-split, one-part call with 16-bit V: O leaves through LDS so that
-    // every global store writes whole 128-byte row segments.  A lane holds 16 consecutive d
-    // of one row per 32-wide block, so direct stores would put 16-byte pieces of each line
-    // into separate instructions; staged, eight lanes store one 128-byte segment.  The
-    // stores are non-temporal: nothing reads O back, and it need not displace K/V in L2.
-    // Each wave stages its 32 rows x 64 d (4 KiB) in its own part of the tile buffers,
-    // free once every wave is past its last P V; 16-byte chunks XOR-swizzled by row / 2.
-    if constexpr (!V8 && C::KS == 1 && QB == 1) {
+    // Epilogue of a one-split, one-part call: O leaves through LDS so that every global
+    // store writes whole 128-byte row segments.  A lane holds 16 consecutive d of one row
+    // per 32-wide block (fp8 V: four runs of four), so direct stores would put 16-byte (8-byte)
+    // pieces of each line into separate instructions; staged, eight lanes store one 128-byte
+    // segment.  The stores are non-temporal: nothing reads O back, and it need not displace
+    // K/V in L2.  Each wave stages its 32 rows x 64 d (4 KiB) in its own part of the tile
+    // buffers, free once every wave is past its last P V (fp8 V: in o_stage); 16-byte chunks
+    // XOR-swizzled by row / 2.
+    if constexpr (C::KS == 1 && QB == 1) {
         if (p.num_splits == 1) {
-            static_assert(TILE >= 8192 && TILEK >= 4096 && C::NW <= 8, "eight 4 KiB stages");
+            static_assert(V8 || (TILE >= 8192 && TILEK >= 4096 && C::NW <= 8), "eight 4 KiB stages");
             const size_t head_row0 = (size_t)(b * p.Hq + hq) * p.Sq;
             const float l = l_run[0];
-            const float inv = l > 0.0f ? __builtin_amdgcn_rcpf(l) : 0.0f;
+            float inv = l > 0.0f ? __builtin_amdgcn_rcpf(l) : 0.0f;
+            if constexpr (V8) inv *= p.o_scale;   // V's dequantisation factor
             if (h == 0 && qw0 + l32 < p.Sq)
                 p.lse[head_row0 + qw0 + l32] =
                     l > 0.0f ? (m_run[0] + __builtin_amdgcn_logf(l)) * LN2 : -__builtin_inff();
             // Two stages per 8 KiB buffer (fp8 keys: 4 KiB K buffers, one stage each).
             unsigned char* sb;
-            if constexpr (TILEK >= 8192)
+            if constexpr (V8)
+                sb = o_stage + w * 4096;
+            else if constexpr (TILEK >= 8192)
                 sb = (w >> 1 == 0 ? k_lds0 : w >> 1 == 1 ? k_lds1 : w >> 1 == 2 ? k_lds2 : v_lds0) + (w & 1) * 4096;
             else
                 sb = w < 6 ? (w >> 1 == 0 ? v_lds0 : w >> 1 == 1 ? v_lds1 : v_lds2) + (w & 1) * 4096
@@ -889,13 +896,22 @@ void fa_fwd_kernel(Params p) {
 #pragma unroll
                 for (int dh = 0; dh < 2; ++dh) {
                     const f32x16 a = acc[2 * ps + dh][0] * inv;
-                    const u32x4 w0 = {pack2<BF16>(a[0], a[1]), pack2<BF16>(a[2], a[3]),
-                                      pack2<BF16>(a[4], a[5]), pack2<BF16>(a[6], a[7])};
-                    const u32x4 w1 = {pack2<BF16>(a[8], a[9]), pack2<BF16>(a[10], a[11]),
-                                      pack2<BF16>(a[12], a[13]), pack2<BF16>(a[14], a[15])};
-                    const int c = 4 * dh + 2 * h, sw = (l32 >> 1) & 7;
-                    *(u32x4*)(sb + l32 * 128 + ((c ^ sw) << 4)) = w0;
-                    *(u32x4*)(sb + l32 * 128 + (((c + 1) ^ sw) << 4)) = w1;
+                    const int sw = (l32 >> 1) & 7;
+                    if constexpr (V8) {
+                        // d = 32 db + 8t + 4h + 0..3 in slots 4t .. 4t+3: half h of chunk 4 dh + t.
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            *(u32x2*)(sb + l32 * 128 + (((4 * dh + t) ^ sw) << 4) + 8 * h) =
+                                (u32x2){pack2<BF16>(a[4 * t], a[4 * t + 1]), pack2<BF16>(a[4 * t + 2], a[4 * t + 3])};
+                    } else {
+                        const u32x4 w0 = {pack2<BF16>(a[0], a[1]), pack2<BF16>(a[2], a[3]),
+                                          pack2<BF16>(a[4], a[5]), pack2<BF16>(a[6], a[7])};
+                        const u32x4 w1 = {pack2<BF16>(a[8], a[9]), pack2<BF16>(a[10], a[11]),
+                                          pack2<BF16>(a[12], a[13]), pack2<BF16>(a[14], a[15])};
+                        const int c = 4 * dh + 2 * h;
+                        *(u32x4*)(sb + l32 * 128 + ((c ^ sw) << 4)) = w0;
+                        *(u32x4*)(sb + l32 * 128 + (((c + 1) ^ sw) << 4)) = w1;
+                    }
                 }
                 __syncthreads();
 #pragma unroll
