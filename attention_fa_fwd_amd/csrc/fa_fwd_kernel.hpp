@@ -23,7 +23,9 @@
 //    V stays row-major in LDS; ds_read_b64_tr_b16 delivers V^T fragments: in each group
 //    of 16 lanes, lane i receives element (i mod 4) of the 8-byte rows addressed by lanes
 //    4j + i/4, j = 0..3.  The d-order of the fragments is chosen so that each lane ends
-//    with 16 consecutive d of its query (two 128-bit stores per 32-wide block).
+//    with 16 consecutive d of its query per 32-wide block.  In the plain call the
+//    epilogue stages O through LDS and writes whole 128-byte row segments with
+//    non-temporal stores; split partials are stored from the registers.
 //  * K and V tiles are triple-buffered in LDS and move there straight from HBM with
 //    gfx950's 128-bit buffer loads to LDS: no staging registers, no LDS write instructions
 //    (staging through registers measured 5% slower).  The buffer range ends at key Skv,
